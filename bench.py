@@ -1,0 +1,260 @@
+"""Throughput of the NVFP4 W4A4 linear layer on one MI355X.
+
+One step = the whole hot path on one batch: quantize the activations to NVFP4
+(per-tensor amax -> global scale -> E4M3 block scales -> E2M1 codes) and run the
+block-scaled GEMM against pre-quantized, pre-packed weights, FP32 out.  Inputs
+are resident in HBM before the timed region.  Steps are captured in a HIP graph
+(one replay covers a whole rotation of weight copies) so the host launch rate
+does not limit the measurement.
+
+Prints one JSON line (rank 0) with the headline metric (TFLOP/s of the step,
+activation quantization included), the roofline of the dominant kernel (the
+GEMM) measured with HIP events on the launch stream, and the CPU oracle timed on
+a bounded sample of the same workload.
+
+Default workload: the decode-skinny layer, X[16 x 5120] bf16 against W[5120 x 5120]
+NVFP4, with 40 rotated weight copies (590 MB > the 256 MB Infinity Cache) so the
+weight stream comes from HBM.  --config selects another workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "NVFP4 W4A4 GEMM TFLOPS incl. act-quantize; % of MFMA/HBM roofline at 1 GPU"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+F16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense FP16/BF16 matrix cores
+
+CONFIG_NAMES = {"tiny": "tiny", "decode": "decode-skinny", "gdn": "gdn-fused-input-projection",
+                "ngpt": "ngpt-d4096", "large": "large-prefill-d16384"}
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=None)
+    p.add_argument("--warmup", type=int, default=None)
+    p.add_argument("--config", default="decode", choices=sorted(CONFIG_NAMES))
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
+    return p.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (collectives are not part of it); "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import nvfp4_block_scaled_03_amd as nv
+    import workloads
+
+    name = args.config
+    small = name in ("tiny", "decode")
+    steps = args.steps if args.steps is not None else (2000 if small else 20)
+    warmup = args.warmup if args.warmup is not None else (200 if small else 5)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    t0 = time.time()
+    wl = workloads.make(name)
+    log(f"workload {name}: M={wl.M} K={wl.K} N={wl.N} modules={[w.shape[0] for w in wl.w]} "
+        f"generated in {time.time() - t0:.1f}s")
+    M, K, N = wl.M, wl.K, wl.N
+    xdt = torch.bfloat16 if wl.x_dtype == "bf16" else torch.float32
+    x = torch.from_numpy(wl.x).to(dev).to(xdt)
+    in_dtype = nv.NVFP4_IN_BF16 if xdt == torch.bfloat16 else nv.NVFP4_IN_F32
+
+    # weights: quantized per module (own global scale) and packed once, outside the timed region
+    w_dev = [torch.from_numpy(w).to(dev).to(torch.bfloat16 if wl.w_dtype == "bf16" else torch.float32)
+             for w in wl.w]
+    mods = [nv.quantize(w) for w in w_dev]
+    packed = nv.PackedWeight(mods, K)
+    copies = 40 if name == "decode" else 1
+    weights = [packed] + [packed.clone() for _ in range(copies - 1)]
+    if not wl.quantize_w_in_step:
+        del w_dev
+    torch.cuda.synchronize()
+
+    codes, scales, g = nv.empty_quantized(M, K, dev)
+    ws = torch.empty((max(nv.nvfp4_quantize_workspace_bytes(M, K), 256),), dtype=torch.uint8, device=dev)
+    y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    gws = nv.nvfp4_gemm_workspace_bytes(M, packed.desc)
+    gemm_ws = torch.empty((max(gws, 256),), dtype=torch.uint8, device=dev)
+    if wl.quantize_w_in_step:
+        wq_bufs = [nv.empty_quantized(w.shape[0], K, dev) for w in w_dev]
+        wq_ws = [torch.empty((max(nv.nvfp4_quantize_workspace_bytes(w.shape[0], K), 256),), dtype=torch.uint8,
+                             device=dev) for w in w_dev]
+
+    def step(i):
+        if wl.quantize_w_in_step:   # tiny case: both operands quantized inside the step
+            for w, (c, s, gg), wsb in zip(w_dev, wq_bufs, wq_ws):
+                nv.nvfp4_quantize(w, c, s, gg, nv.NVFP4_G_COMPUTE, wsb)
+        nv.nvfp4_quantize(x, codes, scales, g, nv.NVFP4_G_COMPUTE, ws, rows=M, K=K, ld_x=K, in_dtype=in_dtype)
+        nv.nvfp4_gemm(M, codes, scales, g, weights[i % copies].desc, y, N, gemm_ws, gws)
+
+    def gemm_only(i):
+        nv.nvfp4_gemm(M, codes, scales, g, weights[i % copies].desc, y, N, gemm_ws, gws)
+
+    def quant_only(i):
+        nv.nvfp4_quantize(x, codes, scales, g, nv.NVFP4_G_COMPUTE, ws, rows=M, K=K, ld_x=K, in_dtype=in_dtype)
+
+    stream = torch.cuda.Stream()
+    rot = copies
+
+    def make_runner(fn, count):
+        """Runs fn(0..count-1) once per call: as a replayed HIP graph, or eagerly."""
+        if args.no_graph:
+            def run():
+                for i in range(count):
+                    fn(i)
+            return run
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            for i in range(count):       # eager warm-up on the capture stream
+                fn(i)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=stream):
+            for i in range(count):
+                fn(i)
+        torch.cuda.synchronize()
+        return graph.replay
+
+    def timed(fn, n_steps, n_warm):
+        """Run n_warm untimed then exactly n_steps steps; returns seconds for the n_steps."""
+        per = rot if n_steps >= rot else n_steps
+        full = make_runner(fn, per)
+        rem = n_steps % per
+        rem_run = make_runner(fn, rem) if rem else None
+        for _ in range(max(1, n_warm // per)):
+            full()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        cur = torch.cuda.current_stream()
+        e0.record(cur)
+        for _ in range(n_steps // per):
+            full()
+        if rem_run:
+            rem_run()
+        e1.record(cur)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3
+
+    log(f"timing {steps} steps after {warmup} warm-up steps (graph={'no' if args.no_graph else 'yes'})")
+    t_step = timed(step, steps, warmup) / steps
+    # dominant kernel and the quantizer alone, same launch configuration, events on the launch stream
+    k_steps = max(steps, rot)
+    t_gemm = timed(gemm_only, k_steps, min(warmup, k_steps)) / k_steps
+    t_quant = timed(quant_only, k_steps, min(warmup, k_steps)) / k_steps
+
+    flops = 2.0 * M * N * K
+    tflops = flops / t_step / 1e12
+    w_bytes = N * K * 9 // 16
+    x_q_bytes = M * K * 9 // 16
+    gemm_bytes = w_bytes + x_q_bytes + M * N * 4
+    if name == "decode":
+        roof = {"bound": "hbm", "achieved": gemm_bytes / t_gemm / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": flops / t_gemm / 1e12, "peak": F16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = "gemm_skinny_kernel" if M <= 16 else "gemm_tile_kernel"
+    roof["kernel_us"] = t_gemm * 1e6
+    roof["algorithmic_bytes_per_launch"] = gemm_bytes
+
+    # parity of the last step (codes bit-exact, outputs within tolerance), on sampled rows for big M
+    torch.cuda.synchronize()
+    from oracle import nvfp4_ref as ref
+    rng = np.random.default_rng(0)
+    rows = np.arange(M) if M <= 64 else np.unique(np.concatenate([[0, M - 1], rng.choice(M, 16, replace=False)]))
+    gx = ref.global_scale(np.float32(np.abs(wl.x).max()))
+    xq = ref.quantize(wl.x[rows], g_mode="given", g=gx)
+    codes_ok = bool(np.array_equal(codes[torch.from_numpy(rows).to(dev)].cpu().numpy(), xq.codes) and
+                    np.array_equal(scales[torch.from_numpy(rows).to(dev)].cpu().numpy(), xq.scales) and
+                    np.float32(g.item()) == gx)
+    cols = np.arange(N) if N <= 8192 else np.unique(rng.choice(N, 512, replace=False))
+    parts, off = [], 0
+    for w in wl.w:
+        sel = cols[(cols >= off) & (cols < off + w.shape[0])] - off
+        if len(sel):
+            gw = ref.global_scale(np.float32(np.abs(w).max()))
+            parts.append(ref.dequantize(ref.quantize(w[sel], g_mode="given", g=gw)))
+        off += w.shape[0]
+    y_ref, a_ref = ref.gemm_dequantized(ref.dequantize(xq), np.concatenate(parts))
+    yd = y[torch.from_numpy(rows).to(dev)][:, torch.from_numpy(cols).to(dev)].cpu().numpy()
+    y_ok, worst = ref.gemm_within_tolerance(yd, y_ref, a_ref)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, ref)
+
+    out = {
+        "metric": METRIC,
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": t_step * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "nvfp4 w4a4 -> f16 mfma, f32 acc",
+        "data": "synthetic (seeded; distributions of the pages' workloads)",
+        "config": {"workload": CONFIG_NAMES[name], "M": M, "K": K, "N": N,
+                   "modules": [int(w.shape[0]) for w in wl.w], "x_dtype": wl.x_dtype,
+                   "weight_copies": copies, "graph": not args.no_graph},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "step_breakdown_us": {"quantize": t_quant * 1e6, "gemm": t_gemm * 1e6, "step": t_step * 1e6},
+        "step_gbs": (M * K * (2 if wl.x_dtype == "bf16" else 4) + w_bytes + M * N * 4) / t_step / 1e9,
+        "parity": {"codes_scales_bit_exact": codes_ok, "gemm_within_1e-5": bool(y_ok), "worst_ratio": worst,
+                   "rows_checked": int(len(rows)), "cols_checked": int(len(cols))},
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(wl, ref, budget_s=12.0):
+    """The oracle as it stands, on host cores: quantize X, dequantize, FP64 GEMM against the weights
+    dequantized once beforehand (they are static, like the packed blob).  Bounded sample: whole steps
+    for the small workloads, a block of rows for the large ones; reported in TFLOP/s of that sample."""
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        blas_threads = 1
+    M, K, N = wl.M, wl.K, wl.N
+    m_s = M if M <= 64 else 64
+    wh = np.concatenate([ref.dequantize(ref.quantize(w)) for w in wl.w])
+    gx = ref.global_scale(np.float32(np.abs(wl.x).max()))
+    xs = wl.x[:m_s]
+    n, t0 = 0, time.time()
+    while True:
+        xq = ref.quantize(xs, g_mode="given", g=gx)
+        ref.gemm_dequantized(ref.dequantize(xq), wh)
+        n += 1
+        if time.time() - t0 > budget_s or n >= 1000:
+            break
+    dt = (time.time() - t0) / n
+    return {"value": 2.0 * m_s * N * K / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads),
+            "kind": "oracle",
+            "sample": f"{n} oracle steps of X[{m_s} x {K}] (quantize, dequantize, FP64 GEMM with |terms|) "
+                      f"against W[{N} x {K}] dequantized once; {dt * 1e3:.1f} ms per step"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,212 @@
+/*
+ * nvfp4.h - C ABI of the MI355X (gfx950) NVFP4 W4A4 linear-layer library.
+ *
+ * The library computes one NVFP4 W4A4 linear layer: activations are quantized
+ * to NVFP4 on the fly and multiplied against pre-quantized, pre-swizzled NVFP4
+ * weights with FP32 accumulation.  This is the operation the pages apply to
+ * every linear layer of the hybrid Gated DeltaNet model ("Why Gated DeltaNet
+ * Survives 4-Bit Quantization: NVFP4 W4A4 for the Recurrent Half of a Hybrid
+ * 27B LLM", section "Performance and Efficiency Gains": weights and
+ * activations in NVFP4 on all 496 linear layers) and to nGPT's dot products
+ * ("Normalized Architectures are Natively 4-Bit", section "Approach").
+ *
+ * NVFP4 tensor (canonical layout, used for every input and output of this ABI
+ * except the packed weight blob):
+ *   - codes  : uint8 [rows][K/2]; byte j of a row holds element 2j in its low
+ *              nibble and element 2j+1 in its high nibble; each nibble is an
+ *              E2M1 code (bit 3 sign, bits 2..1 exponent with bias 1, bit 0
+ *              mantissa; magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6).
+ *   - scales : uint8 [rows][K/16]; one E4M3 ("FN": bias 7, max 448, no
+ *              infinities) scale per 16 consecutive elements along K
+ *              (blocks of 16: section "Why the 'Fragile' Recurrence is
+ *              Actually Robust" of the Gated DeltaNet page).
+ *   - g      : one FP32 per-tensor (per-module) global scale.
+ *   value(row, k) = e2m1(code) * e4m3(scale[row][k/16]) * g.
+ *
+ * Conventions for every entry point:
+ *   - All tensor arguments are device pointers to caller-owned memory.  The
+ *     library never allocates or frees device memory and keeps no state
+ *     between calls apart from a thread-local error message.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     All device work is enqueued asynchronously on it; nothing synchronizes.
+ *   - Arguments are validated on the host before any HIP call.  On error no
+ *     work is enqueued, a status other than NVFP4_OK is returned and
+ *     nvfp4_last_error() describes it.  No C++ exception crosses the ABI.
+ *   - Input values must be finite.  NaN or infinity in an input is outside
+ *     the contract (the outputs are then unspecified but no memory outside
+ *     the given buffers is touched).
+ *   - The functions are thread-safe; calls that share output buffers must be
+ *     ordered by the caller.
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NVFP4_ABI_VERSION 1
+
+typedef enum nvfp4_status {
+    NVFP4_OK = 0,
+    NVFP4_ERR_INVALID_ARG = 1, /* null pointer or unknown enum value */
+    NVFP4_ERR_SHAPE = 2,       /* negative size, K not a multiple of 16, leading dimension too small */
+    NVFP4_ERR_WORKSPACE = 3,   /* workspace missing or smaller than the *_workspace_bytes query */
+    NVFP4_ERR_UNSUPPORTED = 4, /* well-formed request outside what the kernels handle (documented per call) */
+    NVFP4_ERR_NO_DEVICE = 5,   /* no gfx950 GPU is visible */
+    NVFP4_ERR_HIP = 6,         /* a HIP runtime call failed; nvfp4_last_error() has its message */
+    NVFP4_ERR_DESCRIPTOR = 7   /* weight descriptor has a wrong magic/version or inconsistent fields */
+} nvfp4_status;
+
+/* Element type of an unquantized input tensor. */
+typedef enum nvfp4_in_dtype {
+    NVFP4_IN_F32 = 0,
+    NVFP4_IN_BF16 = 1
+} nvfp4_in_dtype;
+
+/* How the per-tensor global scale g is obtained. */
+typedef enum nvfp4_g_mode {
+    /* g = fl32(amax / 2688) from the tensor's largest magnitude (g = 1 for an
+     * all-zero tensor, floored at 2^-100), written to *g.  2688 = 6 * 448 puts
+     * the largest element of the tensor on code 6 of a block scaled by 448. */
+    NVFP4_G_COMPUTE = 0,
+    /* g is read from *g (finite, positive, normal FP32).  With g = 1 this is
+     * NVFP4 without per-tensor scaling ("Normalized Architectures are
+     * Natively 4-Bit", sections "Problem" and "Approach"); with a calibrated
+     * value it is the per-module calibrated scale of the Gated DeltaNet page
+     * ("Critical Lessons for Model Serving"). */
+    NVFP4_G_GIVEN = 1
+} nvfp4_g_mode;
+
+/* Library ABI version (NVFP4_ABI_VERSION of the build). */
+int nvfp4_abi_version(void);
+
+/* Message describing the last error returned on the calling thread ("" if none). */
+const char* nvfp4_last_error(void);
+
+/* NVFP4_OK if a gfx950 device is current, NVFP4_ERR_NO_DEVICE otherwise. */
+nvfp4_status nvfp4_device_check(void);
+
+/* ---------------------------------------------------------------------------
+ * Quantize: unquantized [rows][K] tensor -> canonical NVFP4 (codes, scales, g).
+ *
+ * Per tensor: amax = max |x|, g as in nvfp4_g_mode, s_enc = fl32(1/g).
+ * Per 16-element block along K: bamax = max |x|, S = E4M3 nearest to
+ * fl32(fl32(bamax * s_enc) / 6) (ties to even, saturating at 448).
+ * Per element: q = fl32(x * r) with r = fl32(s_enc / S) (r = 0 when S = 0),
+ * code = sign(q) | E2M1 magnitude nearest to |q| (ties to even, saturating
+ * at 6; the sign bit is kept when the magnitude rounds to 0).
+ * All of it in IEEE FP32 with one rounding per operation, so codes and scales
+ * are a deterministic function of the input.
+ *
+ * x        : device, rows x K elements of in_dtype, row r at x + r*ld_x elements
+ * rows     : >= 0 (rows == 0 is an empty tensor: g = 1 in COMPUTE mode)
+ * K        : > 0, multiple of 16
+ * ld_x     : >= K
+ * codes    : device, rows * K/2 bytes, written (dense, row stride K/2)
+ * scales   : device, rows * K/16 bytes, written (dense, row stride K/16)
+ * g        : device, one float; written in COMPUTE mode, read in GIVEN mode
+ * workspace: device, >= nvfp4_quantize_workspace_bytes(rows, K) bytes
+ *            (may be NULL when that is 0); contents need no initialisation
+ * ------------------------------------------------------------------------- */
+size_t nvfp4_quantize_workspace_bytes(int64_t rows, int64_t K);
+nvfp4_status nvfp4_quantize(const void* x, int in_dtype, int64_t rows, int64_t K, int64_t ld_x,
+                            uint8_t* codes, uint8_t* scales, float* g, int g_mode,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Packed weights.
+ *
+ * A projection is a stack of n_modules sub-modules (e.g. q,k,v,z,a,b of a
+ * Gated DeltaNet input projection) sharing one input.  Each sub-module was
+ * quantized on its own and keeps its own global scale g_w[s]: fused kernels
+ * must not apply one module's scale to another (section "Critical Lessons for
+ * Model Serving" of the Gated DeltaNet page).  Output column n of the fused
+ * GEMM belongs to the module whose row range holds n and is scaled by that
+ * module's g.
+ *
+ * The blob is opaque device memory holding a header, the codes and scales
+ * rearranged into tiles that load straight into MFMA operand registers, and
+ * one FP32 column scale per output row.  The descriptor is a host struct,
+ * filled by nvfp4_pack_weights and passed by pointer to the GEMM; it holds the
+ * device address of the blob, so the blob must outlive its use.
+ * ------------------------------------------------------------------------- */
+#define NVFP4_MAX_MODULES 16
+#define NVFP4_WEIGHT_MAGIC 0x34504656u /* "VFP4" */
+#define NVFP4_WEIGHT_VERSION 1u
+
+typedef struct nvfp4_weight_desc {
+    uint32_t magic;                  /* NVFP4_WEIGHT_MAGIC */
+    uint32_t version;                /* NVFP4_WEIGHT_VERSION */
+    int64_t n;                       /* total output features (sum of module rows) */
+    int64_t k;                       /* input features */
+    int64_t n_padded;                /* n rounded up to the packing tile (rows beyond n are zero) */
+    int32_t n_modules;
+    int32_t reserved;
+    int64_t module_rows[NVFP4_MAX_MODULES];
+    int64_t module_row_offset[NVFP4_MAX_MODULES];
+    const void* blob;                /* device address of the packed blob */
+    size_t blob_bytes;
+    size_t codes_offset;             /* byte offsets of the three regions inside the blob */
+    size_t scales_offset;
+    size_t colscale_offset;
+} nvfp4_weight_desc;
+
+/* Bytes of the blob for the given module row counts and K (0 if the shape is invalid). */
+size_t nvfp4_packed_weight_bytes(int n_modules, const int64_t* module_rows, int64_t K);
+
+/*
+ * Pack n_modules canonical NVFP4 tensors into one blob.
+ *
+ * n_modules   : 1..NVFP4_MAX_MODULES
+ * module_rows : host array, module_rows[s] >= 1
+ * K           : > 0, multiple of 128 (NVFP4_ERR_UNSUPPORTED otherwise)
+ * codes       : host array of n_modules device pointers, codes[s] is [module_rows[s]][K/2]
+ * scales      : host array of n_modules device pointers, scales[s] is [module_rows[s]][K/16]
+ * g_w         : host array of n_modules device pointers to each module's FP32 global scale
+ * blob        : device, blob_bytes >= nvfp4_packed_weight_bytes(...) (256-byte aligned)
+ * desc_out    : host, filled on success
+ */
+nvfp4_status nvfp4_pack_weights(int n_modules, const int64_t* module_rows, int64_t K,
+                                const uint8_t* const* codes, const uint8_t* const* scales,
+                                const float* const* g_w, void* blob, size_t blob_bytes,
+                                nvfp4_weight_desc* desc_out, void* stream);
+
+/*
+ * Inverse of the packing, for checking and for saving weights: writes the
+ * canonical codes [n][K/2], scales [n][K/16] and per-row column scale [n]
+ * (the owning module's g) of all modules stacked in order.
+ */
+nvfp4_status nvfp4_unpack_weights(const nvfp4_weight_desc* w, uint8_t* codes, uint8_t* scales,
+                                  float* colscale, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Block-scaled GEMM: Y[m][n] = sum_k xhat[m][k] * what[n][k], FP32 out.
+ *
+ * xhat = e2m1(a_code) * e4m3(a_scale) * g_x, what = e2m1(w_code) * e4m3(w_scale)
+ * * g_w[module(n)].  The products of decoded codes and block scales are exact in
+ * FP16 and are multiplied and summed on the matrix cores in FP32; the two
+ * global scales are applied once per output as fl32(acc * fl32(g_x * g_w)).
+ *
+ * M        : >= 0 (M == 0 enqueues nothing)
+ * a_codes  : device, canonical [M][K/2] codes of the activations (K = w->k)
+ * a_scales : device, canonical [M][K/16]
+ * g_x      : device, one float (the activations' global scale)
+ * w        : host descriptor from nvfp4_pack_weights
+ * y        : device, FP32, row m at y + m*ld_y; columns [0, w->n) are written
+ * ld_y     : >= w->n
+ * workspace: device, >= nvfp4_gemm_workspace_bytes(M, w) bytes (may be NULL when 0)
+ * ------------------------------------------------------------------------- */
+size_t nvfp4_gemm_workspace_bytes(int64_t M, const nvfp4_weight_desc* w);
+nvfp4_status nvfp4_gemm(int64_t M, const uint8_t* a_codes, const uint8_t* a_scales, const float* g_x,
+                        const nvfp4_weight_desc* w, float* y, int64_t ld_y,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_H */

@@ -1,0 +1,264 @@
+"""Python binding of libnvfp4 (include/nvfp4.h): argument marshalling only.
+
+Every computation runs in the HIP kernels of the shared library; this module
+turns torch tensors into device pointers and the current HIP stream, checks
+the returned status and raises ``NVFP4Error`` on failure.  It never computes
+anything itself and has no fallback: if the library is missing, importing
+this package raises.
+
+The functions mirror the C entry points (``nvfp4_quantize``,
+``nvfp4_pack_weights``, ``nvfp4_gemm`` ...) and take the output tensors as
+arguments.  ``quantize``, ``PackedWeight`` and ``gemm`` are conveniences that
+allocate outputs with torch before calling the same entry points.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnvfp4.so")
+
+NVFP4_OK = 0
+NVFP4_ERR_INVALID_ARG = 1
+NVFP4_ERR_SHAPE = 2
+NVFP4_ERR_WORKSPACE = 3
+NVFP4_ERR_UNSUPPORTED = 4
+NVFP4_ERR_NO_DEVICE = 5
+NVFP4_ERR_HIP = 6
+NVFP4_ERR_DESCRIPTOR = 7
+
+NVFP4_IN_F32 = 0
+NVFP4_IN_BF16 = 1
+NVFP4_G_COMPUTE = 0
+NVFP4_G_GIVEN = 1
+NVFP4_MAX_MODULES = 16
+NVFP4_WEIGHT_MAGIC = 0x34504656
+NVFP4_WEIGHT_VERSION = 1
+
+
+class NVFP4Error(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"nvfp4 status {status}: {message}")
+        self.status = status
+
+
+class WeightDesc(ctypes.Structure):
+    """Mirror of ``nvfp4_weight_desc``."""
+    _fields_ = [
+        ("magic", ctypes.c_uint32),
+        ("version", ctypes.c_uint32),
+        ("n", ctypes.c_int64),
+        ("k", ctypes.c_int64),
+        ("n_padded", ctypes.c_int64),
+        ("n_modules", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("module_rows", ctypes.c_int64 * NVFP4_MAX_MODULES),
+        ("module_row_offset", ctypes.c_int64 * NVFP4_MAX_MODULES),
+        ("blob", ctypes.c_void_p),
+        ("blob_bytes", ctypes.c_size_t),
+        ("codes_offset", ctypes.c_size_t),
+        ("scales_offset", ctypes.c_size_t),
+        ("colscale_offset", ctypes.c_size_t),
+    ]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'` "
+            "or `python nvfp4_block_scaled_03_amd/build.py`")
+    lib = ctypes.CDLL(LIB_PATH)
+    c_i64, c_sz, c_vp, c_int = ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int
+    sig = {
+        "nvfp4_abi_version": (c_int, []),
+        "nvfp4_last_error": (ctypes.c_char_p, []),
+        "nvfp4_device_check": (c_int, []),
+        "nvfp4_quantize_workspace_bytes": (c_sz, [c_i64, c_i64]),
+        "nvfp4_quantize": (c_int, [c_vp, c_int, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_int, c_vp, c_sz, c_vp]),
+        "nvfp4_packed_weight_bytes": (c_sz, [c_int, ctypes.POINTER(c_i64), c_i64]),
+        "nvfp4_pack_weights": (c_int, [c_int, ctypes.POINTER(c_i64), c_i64, ctypes.POINTER(c_vp),
+                                       ctypes.POINTER(c_vp), ctypes.POINTER(c_vp), c_vp, c_sz,
+                                       ctypes.POINTER(WeightDesc), c_vp]),
+        "nvfp4_unpack_weights": (c_int, [ctypes.POINTER(WeightDesc), c_vp, c_vp, c_vp, c_vp]),
+        "nvfp4_gemm_workspace_bytes": (c_sz, [c_i64, ctypes.POINTER(WeightDesc)]),
+        "nvfp4_gemm": (c_int, [c_i64, c_vp, c_vp, c_vp, ctypes.POINTER(WeightDesc), c_vp, c_i64, c_vp, c_sz, c_vp]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    if lib.nvfp4_abi_version() != 1:
+        raise ImportError("libnvfp4 ABI version mismatch")
+    return lib
+
+
+_lib = _load()
+lib = _lib
+
+
+def _check(status: int):
+    if status != NVFP4_OK:
+        raise NVFP4Error(status, _lib.nvfp4_last_error().decode(errors="replace"))
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else None
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def last_error() -> str:
+    return _lib.nvfp4_last_error().decode(errors="replace")
+
+
+def device_check() -> int:
+    return _lib.nvfp4_device_check()
+
+
+# ---------------------------------------------------------------------------
+# Direct entry points
+# ---------------------------------------------------------------------------
+
+
+def nvfp4_quantize_workspace_bytes(rows: int, K: int) -> int:
+    return _lib.nvfp4_quantize_workspace_bytes(rows, K)
+
+
+def nvfp4_quantize(x, codes, scales, g, g_mode=NVFP4_G_COMPUTE, workspace=None, stream=None, *,
+                   rows=None, K=None, ld_x=None, in_dtype=None):
+    """Quantize a 2-D device tensor x [rows, K] (float32 or bfloat16) into codes/scales/g."""
+    if rows is None:
+        rows, K = x.shape
+        ld_x = x.stride(0) if rows > 1 else K   # a single row's stride is arbitrary
+        if K > 1 and x.stride(-1) != 1:
+            raise ValueError("x must have unit stride along K")
+        in_dtype = NVFP4_IN_BF16 if x.dtype == torch.bfloat16 else NVFP4_IN_F32
+        if x.dtype not in (torch.bfloat16, torch.float32):
+            raise TypeError("x must be float32 or bfloat16")
+    ws_bytes = workspace.numel() * workspace.element_size() if isinstance(workspace, torch.Tensor) else 0
+    _check(_lib.nvfp4_quantize(_ptr(x), in_dtype, rows, K, ld_x, _ptr(codes), _ptr(scales), _ptr(g), g_mode,
+                               _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def nvfp4_packed_weight_bytes(module_rows: Sequence[int], K: int) -> int:
+    arr = (ctypes.c_int64 * len(module_rows))(*module_rows)
+    return _lib.nvfp4_packed_weight_bytes(len(module_rows), arr, K)
+
+
+def nvfp4_pack_weights(modules, K: int, blob, stream=None) -> WeightDesc:
+    """modules: sequence of (codes [rows, K/2] uint8, scales [rows, K/16] uint8, g [1] float32) device tensors."""
+    n = len(modules)
+    rows = (ctypes.c_int64 * n)(*[int(m[0].shape[0]) for m in modules])
+    cp = (ctypes.c_void_p * n)(*[_ptr(m[0]) for m in modules])
+    sp = (ctypes.c_void_p * n)(*[_ptr(m[1]) for m in modules])
+    gp = (ctypes.c_void_p * n)(*[_ptr(m[2]) for m in modules])
+    desc = WeightDesc()
+    nbytes = blob.numel() * blob.element_size()
+    _check(_lib.nvfp4_pack_weights(n, rows, K, cp, sp, gp, _ptr(blob), nbytes, ctypes.byref(desc),
+                                   _stream(stream)))
+    return desc
+
+
+def nvfp4_unpack_weights(desc: WeightDesc, codes, scales, colscale, stream=None):
+    _check(_lib.nvfp4_unpack_weights(ctypes.byref(desc), _ptr(codes), _ptr(scales), _ptr(colscale),
+                                     _stream(stream)))
+
+
+def nvfp4_gemm_workspace_bytes(M: int, desc: WeightDesc) -> int:
+    return _lib.nvfp4_gemm_workspace_bytes(M, ctypes.byref(desc))
+
+
+def nvfp4_gemm(M: int, a_codes, a_scales, g_x, desc: WeightDesc, y, ld_y=None, workspace=None, stream=None):
+    if ld_y is None:
+        ld_y = y.stride(0) if y.dim() == 2 and y.shape[0] > 1 else desc.n
+    ws_bytes = workspace.numel() * workspace.element_size() if isinstance(workspace, torch.Tensor) else 0
+    _check(_lib.nvfp4_gemm(M, _ptr(a_codes), _ptr(a_scales), _ptr(g_x), ctypes.byref(desc), _ptr(y), ld_y,
+                           _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# Conveniences (outputs allocated with torch, then the entry points above)
+# ---------------------------------------------------------------------------
+
+
+def empty_quantized(rows: int, K: int, device="cuda"):
+    codes = torch.empty((rows, K // 2), dtype=torch.uint8, device=device)
+    scales = torch.empty((rows, K // 16), dtype=torch.uint8, device=device)
+    g = torch.empty((1,), dtype=torch.float32, device=device)
+    return codes, scales, g
+
+
+def quantize(x: torch.Tensor, g=None, stream=None):
+    """NVFP4-quantize x [rows, K]; g=None computes the global scale, otherwise uses the given value."""
+    rows, K = x.shape
+    codes, scales, gt = empty_quantized(rows, K, x.device)
+    if g is None:
+        ws = torch.empty((max(nvfp4_quantize_workspace_bytes(rows, K), 1),), dtype=torch.uint8, device=x.device)
+        nvfp4_quantize(x, codes, scales, gt, NVFP4_G_COMPUTE, ws, stream)
+    else:
+        if isinstance(g, torch.Tensor):
+            gt.copy_(g.reshape(1))
+        else:
+            gt.fill_(float(g))
+        nvfp4_quantize(x, codes, scales, gt, NVFP4_G_GIVEN, None, stream)
+    return codes, scales, gt
+
+
+class PackedWeight:
+    """A packed (possibly fused multi-module) weight: the device blob plus its descriptor."""
+
+    def __init__(self, modules, K: int, stream=None):
+        rows = [int(m[0].shape[0]) for m in modules]
+        nbytes = nvfp4_packed_weight_bytes(rows, K)
+        if nbytes == 0:
+            raise NVFP4Error(NVFP4_ERR_SHAPE, f"invalid packed weight shape rows={rows} K={K}")
+        dev = modules[0][0].device
+        self.blob = torch.empty((nbytes,), dtype=torch.uint8, device=dev)
+        self.desc = nvfp4_pack_weights(modules, K, self.blob, stream)
+        self.module_rows = rows
+        self.K = K
+
+    @property
+    def n(self) -> int:
+        return int(self.desc.n)
+
+    def clone(self) -> "PackedWeight":
+        """A copy of the blob at another device address (the descriptor points at the copy)."""
+        other = PackedWeight.__new__(PackedWeight)
+        other.blob = self.blob.clone()
+        other.desc = WeightDesc.from_buffer_copy(self.desc)
+        other.desc.blob = other.blob.data_ptr()
+        other.module_rows, other.K = self.module_rows, self.K
+        return other
+
+    def unpack(self, stream=None):
+        n, K = self.n, self.K
+        codes = torch.empty((n, K // 2), dtype=torch.uint8, device=self.blob.device)
+        scales = torch.empty((n, K // 16), dtype=torch.uint8, device=self.blob.device)
+        colscale = torch.empty((n,), dtype=torch.float32, device=self.blob.device)
+        nvfp4_unpack_weights(self.desc, codes, scales, colscale, stream)
+        return codes, scales, colscale
+
+
+def gemm(a_codes, a_scales, g_x, w: PackedWeight, y=None, stream=None):
+    M = a_codes.shape[0]
+    if y is None:
+        y = torch.empty((M, w.n), dtype=torch.float32, device=a_codes.device)
+    ws_bytes = nvfp4_gemm_workspace_bytes(M, w.desc)
+    ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=a_codes.device) if ws_bytes else None
+    nvfp4_gemm(M, a_codes, a_scales, g_x, w.desc, y, None, ws, stream)
+    return y

@@ -1,0 +1,243 @@
+// Host side of the C ABI declared in include/nvfp4.h: argument validation (before
+// any HIP call), descriptor construction, device check and kernel dispatch.
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "common.h"
+
+namespace {
+
+thread_local std::string t_last_error;
+
+nvfp4_status fail(nvfp4_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+nvfp4_status fail(nvfp4_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    t_last_error = buf;
+    return st;
+}
+
+nvfp4_status ok() {
+    t_last_error.clear();
+    return NVFP4_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Per-device cache of "is this a gfx950": 0 unknown, 1 yes, 2 no.
+std::atomic<int> g_arch_ok[64];
+
+nvfp4_status check_device() {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0) {
+        (void)hipGetLastError();
+        return fail(NVFP4_ERR_NO_DEVICE, "no HIP device available (%s)", hipGetErrorString(e));
+    }
+    int state = dev < 64 ? g_arch_ok[dev].load(std::memory_order_relaxed) : 0;
+    if (state == 0) {
+        hipDeviceProp_t p;
+        e = hipGetDeviceProperties(&p, dev);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(NVFP4_ERR_NO_DEVICE, "hipGetDeviceProperties failed: %s", hipGetErrorString(e));
+        }
+        state = (strncmp(p.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+        if (dev < 64) g_arch_ok[dev].store(state, std::memory_order_relaxed);
+        if (state == 2) return fail(NVFP4_ERR_NO_DEVICE, "device %d is %s, this library is built for gfx950", dev, p.gcnArchName);
+    }
+    if (state == 2) return fail(NVFP4_ERR_NO_DEVICE, "device %d is not a gfx950", dev);
+    return NVFP4_OK;
+}
+
+nvfp4_status launched(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(NVFP4_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
+
+// Layout of a packed blob for the given shape (see pack.hip).
+bool blob_layout(int n_modules, const int64_t* rows, int64_t K, nvfp4_weight_desc* d) {
+    if (n_modules < 1 || n_modules > NVFP4_MAX_MODULES || rows == nullptr || K <= 0 || K % nvfp4::kPackK != 0)
+        return false;
+    std::memset(d, 0, sizeof(*d));
+    int64_t n = 0;
+    for (int s = 0; s < n_modules; ++s) {
+        if (rows[s] < 1 || rows[s] > (int64_t(1) << 40)) return false;
+        d->module_rows[s] = rows[s];
+        d->module_row_offset[s] = n;
+        n += rows[s];
+    }
+    if (K > (int64_t(1) << 30) || n > (int64_t(1) << 40)) return false;
+    d->magic = NVFP4_WEIGHT_MAGIC;
+    d->version = NVFP4_WEIGHT_VERSION;
+    d->n = n;
+    d->k = K;
+    d->n_padded = round_up(n, nvfp4::kPackNAlign);
+    d->n_modules = n_modules;
+    d->codes_offset = nvfp4::kBlobHeader;
+    d->scales_offset = d->codes_offset + (size_t)(d->n_padded * K / 2);
+    d->colscale_offset = (size_t)round_up((int64_t)(d->scales_offset + (size_t)(d->n_padded * K / 16)), 256);
+    d->blob_bytes = d->colscale_offset + (size_t)d->n_padded * sizeof(float);
+    return true;
+}
+
+nvfp4_status check_desc(const nvfp4_weight_desc* w) {
+    if (w == nullptr) return fail(NVFP4_ERR_INVALID_ARG, "weight descriptor is NULL");
+    if (w->magic != NVFP4_WEIGHT_MAGIC || w->version != NVFP4_WEIGHT_VERSION)
+        return fail(NVFP4_ERR_DESCRIPTOR, "weight descriptor magic/version mismatch (0x%08x v%u)", w->magic, w->version);
+    nvfp4_weight_desc ref;
+    if (!blob_layout(w->n_modules, w->module_rows, w->k, &ref))
+        return fail(NVFP4_ERR_DESCRIPTOR, "weight descriptor has an invalid shape");
+    if (ref.n != w->n || ref.n_padded != w->n_padded || ref.codes_offset != w->codes_offset ||
+        ref.scales_offset != w->scales_offset || ref.colscale_offset != w->colscale_offset ||
+        ref.blob_bytes != w->blob_bytes)
+        return fail(NVFP4_ERR_DESCRIPTOR, "weight descriptor fields are inconsistent");
+    for (int s = 0; s < w->n_modules; ++s)
+        if (ref.module_row_offset[s] != w->module_row_offset[s])
+            return fail(NVFP4_ERR_DESCRIPTOR, "weight descriptor module offsets are inconsistent");
+    if (w->blob == nullptr || !aligned(w->blob, 256)) return fail(NVFP4_ERR_DESCRIPTOR, "weight blob is NULL or not 256-byte aligned");
+    return NVFP4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int nvfp4_abi_version(void) { return NVFP4_ABI_VERSION; }
+
+const char* nvfp4_last_error(void) { return t_last_error.c_str(); }
+
+nvfp4_status nvfp4_device_check(void) {
+    nvfp4_status st = check_device();
+    return st == NVFP4_OK ? ok() : st;
+}
+
+size_t nvfp4_quantize_workspace_bytes(int64_t rows, int64_t K) {
+    if (rows < 0 || K <= 0) return 0;
+    return (size_t)round_up((int64_t)nvfp4::quantize_partials_count(rows, K) * (int64_t)sizeof(float), 256);
+}
+
+nvfp4_status nvfp4_quantize(const void* x, int in_dtype, int64_t rows, int64_t K, int64_t ld_x, uint8_t* codes,
+                            uint8_t* scales, float* g, int g_mode, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+    if (in_dtype != NVFP4_IN_F32 && in_dtype != NVFP4_IN_BF16)
+        return fail(NVFP4_ERR_INVALID_ARG, "unknown input dtype %d", in_dtype);
+    if (g_mode != NVFP4_G_COMPUTE && g_mode != NVFP4_G_GIVEN)
+        return fail(NVFP4_ERR_INVALID_ARG, "unknown g mode %d", g_mode);
+    if (g == nullptr) return fail(NVFP4_ERR_INVALID_ARG, "g is NULL");
+    if (rows < 0 || K <= 0 || K % 16 != 0)
+        return fail(NVFP4_ERR_SHAPE, "need rows >= 0 and K > 0 a multiple of 16 (rows=%lld K=%lld)",
+                    (long long)rows, (long long)K);
+    if (ld_x < K) return fail(NVFP4_ERR_SHAPE, "ld_x (%lld) < K (%lld)", (long long)ld_x, (long long)K);
+    if (rows > 0 && ld_x > INT64_MAX / rows) return fail(NVFP4_ERR_SHAPE, "tensor too large");
+    const int esize = in_dtype == NVFP4_IN_BF16 ? 2 : 4;
+    if (rows > 0) {
+        if (x == nullptr || codes == nullptr || scales == nullptr)
+            return fail(NVFP4_ERR_INVALID_ARG, "x, codes and scales must be non-NULL");
+        if (!aligned(x, 16) || (ld_x * esize) % 16 != 0)
+            return fail(NVFP4_ERR_UNSUPPORTED, "x must be 16-byte aligned with a 16-byte multiple row stride");
+        if (!aligned(codes, 8)) return fail(NVFP4_ERR_UNSUPPORTED, "codes must be 8-byte aligned");
+    }
+    const int n_partials = nvfp4::quantize_partials_count(rows, K);
+    if (g_mode == NVFP4_G_COMPUTE && rows > 0) {
+        const size_t need = nvfp4_quantize_workspace_bytes(rows, K);
+        if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 4))
+            return fail(NVFP4_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+    }
+    nvfp4_status st = check_device();
+    if (st != NVFP4_OK) return st;
+    return launched(nvfp4::launch_quantize(x, in_dtype, rows, K, ld_x, codes, scales, g, g_mode,
+                                           static_cast<float*>(workspace), n_partials,
+                                           static_cast<hipStream_t>(stream)),
+                    "quantize launch");
+}
+
+size_t nvfp4_packed_weight_bytes(int n_modules, const int64_t* module_rows, int64_t K) {
+    nvfp4_weight_desc d;
+    if (!blob_layout(n_modules, module_rows, K, &d)) return 0;
+    return d.blob_bytes;
+}
+
+nvfp4_status nvfp4_pack_weights(int n_modules, const int64_t* module_rows, int64_t K, const uint8_t* const* codes,
+                                const uint8_t* const* scales, const float* const* g_w, void* blob, size_t blob_bytes,
+                                nvfp4_weight_desc* desc_out, void* stream) {
+    if (n_modules > NVFP4_MAX_MODULES)
+        return fail(NVFP4_ERR_UNSUPPORTED, "at most %d modules per packed weight (got %d)", NVFP4_MAX_MODULES, n_modules);
+    if (n_modules < 1) return fail(NVFP4_ERR_INVALID_ARG, "n_modules must be >= 1");
+    if (module_rows == nullptr || codes == nullptr || scales == nullptr || g_w == nullptr || desc_out == nullptr)
+        return fail(NVFP4_ERR_INVALID_ARG, "NULL array argument");
+    for (int s = 0; s < n_modules; ++s)
+        if (module_rows[s] < 1) return fail(NVFP4_ERR_SHAPE, "module %d has %lld rows", s, (long long)module_rows[s]);
+    if (K <= 0 || K % 16 != 0) return fail(NVFP4_ERR_SHAPE, "K must be a positive multiple of 16 (got %lld)", (long long)K);
+    if (K % nvfp4::kPackK != 0)
+        return fail(NVFP4_ERR_UNSUPPORTED, "packed weights need K a multiple of %d (got %lld)", nvfp4::kPackK, (long long)K);
+    nvfp4_weight_desc d;
+    if (!blob_layout(n_modules, module_rows, K, &d)) return fail(NVFP4_ERR_SHAPE, "weight shape too large");
+    for (int s = 0; s < n_modules; ++s) {
+        if (codes[s] == nullptr || scales[s] == nullptr || g_w[s] == nullptr)
+            return fail(NVFP4_ERR_INVALID_ARG, "module %d has a NULL codes/scales/g pointer", s);
+        if (!aligned(codes[s], 16) || !aligned(scales[s], 8) || !aligned(g_w[s], 4))
+            return fail(NVFP4_ERR_UNSUPPORTED, "module %d: codes must be 16-byte and scales 8-byte aligned", s);
+    }
+    if (blob == nullptr || !aligned(blob, 256)) return fail(NVFP4_ERR_INVALID_ARG, "blob must be non-NULL and 256-byte aligned");
+    if (blob_bytes < d.blob_bytes)
+        return fail(NVFP4_ERR_WORKSPACE, "blob needs %zu bytes (got %zu)", d.blob_bytes, blob_bytes);
+    nvfp4_status st = check_device();
+    if (st != NVFP4_OK) return st;
+    d.blob = blob;
+    hipError_t e = nvfp4::launch_pack(d, codes, scales, g_w, static_cast<uint8_t*>(blob), static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(NVFP4_ERR_HIP, "pack launch: %s", hipGetErrorString(e));
+    *desc_out = d;
+    return ok();
+}
+
+nvfp4_status nvfp4_unpack_weights(const nvfp4_weight_desc* w, uint8_t* codes, uint8_t* scales, float* colscale,
+                                  void* stream) {
+    nvfp4_status st = check_desc(w);
+    if (st != NVFP4_OK) return st;
+    if (codes == nullptr || scales == nullptr || colscale == nullptr)
+        return fail(NVFP4_ERR_INVALID_ARG, "unpack outputs must be non-NULL");
+    if (!aligned(codes, 16) || !aligned(scales, 8) || !aligned(colscale, 4))
+        return fail(NVFP4_ERR_UNSUPPORTED, "unpack: codes must be 16-byte and scales 8-byte aligned");
+    st = check_device();
+    if (st != NVFP4_OK) return st;
+    return launched(nvfp4::launch_unpack(*w, codes, scales, colscale, static_cast<hipStream_t>(stream)), "unpack launch");
+}
+
+size_t nvfp4_gemm_workspace_bytes(int64_t M, const nvfp4_weight_desc* w) {
+    if (w == nullptr || M < 0) return 0;
+    return nvfp4::gemm_workspace_bytes(M, *w);
+}
+
+nvfp4_status nvfp4_gemm(int64_t M, const uint8_t* a_codes, const uint8_t* a_scales, const float* g_x,
+                        const nvfp4_weight_desc* w, float* y, int64_t ld_y, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+    nvfp4_status st = check_desc(w);
+    if (st != NVFP4_OK) return st;
+    if (M < 0) return fail(NVFP4_ERR_SHAPE, "M must be >= 0 (got %lld)", (long long)M);
+    if (M == 0) return ok();
+    if (a_codes == nullptr || a_scales == nullptr || g_x == nullptr || y == nullptr)
+        return fail(NVFP4_ERR_INVALID_ARG, "a_codes, a_scales, g_x and y must be non-NULL");
+    if (ld_y < w->n) return fail(NVFP4_ERR_SHAPE, "ld_y (%lld) < n (%lld)", (long long)ld_y, (long long)w->n);
+    if (M > (int64_t(1) << 31) || ld_y > INT64_MAX / M) return fail(NVFP4_ERR_SHAPE, "M too large");
+    if (!aligned(a_codes, 16) || !aligned(a_scales, 4) || !aligned(y, 4))
+        return fail(NVFP4_ERR_UNSUPPORTED, "a_codes must be 16-byte and a_scales 4-byte aligned");
+    const size_t need = nvfp4::gemm_workspace_bytes(M, *w);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+        return fail(NVFP4_ERR_WORKSPACE, "gemm workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+    st = check_device();
+    if (st != NVFP4_OK) return st;
+    return launched(nvfp4::launch_gemm(M, a_codes, a_scales, g_x, *w, y, ld_y, workspace, workspace_bytes,
+                                       static_cast<hipStream_t>(stream)),
+                    "gemm launch");
+}
+
+}  // extern "C"

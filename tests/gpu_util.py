@@ -1,0 +1,54 @@
+"""Helpers for the GPU parity tests: host <-> device marshalling and oracle comparisons."""
+import sys
+
+import numpy as np
+import torch
+
+from oracle import nvfp4_ref as ref
+
+DEV = torch.device("cuda:0")
+
+
+def say(msg):
+    """Print and flush what names the case before a GPU step."""
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(a: np.ndarray, dtype: str) -> torch.Tensor:
+    """FP32 host values (bf16-exact when dtype == 'bf16') -> device tensor of that dtype."""
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    if dtype == "bf16":
+        t = t.to(torch.bfloat16)
+        assert torch.equal(t.float(), torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))), \
+            "input is not bf16-representable"
+    return t.to(DEV)
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().numpy()
+
+
+def assert_quant_equal(codes, scales, g, oq, rows=None, what=""):
+    """Bit-exact comparison of device codes/scales/g with an oracle Quantized (optionally on a row subset)."""
+    c = host(codes) if rows is None else host(codes[rows])
+    s = host(scales) if rows is None else host(scales[rows])
+    gv = np.float32(host(g)[0])
+    assert gv.tobytes() == np.float32(oq.g).tobytes(), f"{what}: g {gv!r} != oracle {oq.g!r}"
+    if not np.array_equal(s, oq.scales):
+        bad = np.argwhere(s != oq.scales)
+        r, b = bad[0]
+        raise AssertionError(f"{what}: {len(bad)} scale bytes differ, first at row {r} block {b}: "
+                             f"gpu 0x{s[r, b]:02x} oracle 0x{oq.scales[r, b]:02x}")
+    if not np.array_equal(c, oq.codes):
+        bad = np.argwhere(c != oq.codes)
+        r, j = bad[0]
+        raise AssertionError(f"{what}: {len(bad)} code bytes differ, first at row {r} byte {j}: "
+                             f"gpu 0x{c[r, j]:02x} oracle 0x{oq.codes[r, j]:02x}")
+
+
+def oracle_quantize_rows(x: np.ndarray, rows, g_mode="compute", g=None):
+    """Oracle quantization of a row subset with the global scale of the whole tensor."""
+    if g_mode == "compute":
+        g = ref.global_scale(np.float32(np.max(np.abs(x))) if x.size else np.float32(0))
+    return ref.quantize(x[rows], g_mode="given", g=g)

@@ -1,0 +1,213 @@
+"""The C-ABI library on the host: it loads, exports every function include/nvfp4.h
+declares, and validates arguments before touching a device.  No GPU needed:
+pointers here are fake but never dereferenced, because every call either fails
+validation or (with no GPU present) stops at the device check."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4.h")
+LIB = os.path.join(ROOT, "nvfp4_block_scaled_03_amd", "libnvfp4.so")
+
+
+def _ensure_built():
+    if not os.path.exists(LIB):
+        from nvfp4_block_scaled_03_amd import build as b
+        b.build()
+
+
+_ensure_built()
+import nvfp4_block_scaled_03_amd as nv  # noqa: E402
+
+FAKE = 1 << 20  # 256-byte aligned fake device address (never dereferenced)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    text = "\n".join(l for l in text.splitlines() if not l.lstrip().startswith("#"))
+    names = set(re.findall(r"\b(nvfp4_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ["nvfp4_quantize", "nvfp4_pack_weights", "nvfp4_gemm", "nvfp4_last_error",
+                     "nvfp4_quantize_workspace_bytes", "nvfp4_packed_weight_bytes", "nvfp4_unpack_weights",
+                     "nvfp4_gemm_workspace_bytes", "nvfp4_abi_version", "nvfp4_device_check"]:
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if l.strip()}
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, missing
+    lib = ctypes.CDLL(LIB)
+    for n in declared_functions():
+        getattr(lib, n)
+
+
+def test_abi_version():
+    assert nv.lib.nvfp4_abi_version() == 1
+
+
+def _no_gpu():
+    return nv.device_check() == nv.NVFP4_ERR_NO_DEVICE
+
+
+def q(**kw):
+    args = dict(x=FAKE, in_dtype=nv.NVFP4_IN_BF16, rows=4, K=64, ld_x=64, codes=FAKE, scales=FAKE, g=FAKE,
+                g_mode=nv.NVFP4_G_COMPUTE, ws=FAKE, ws_bytes=1 << 16)
+    args.update(kw)
+    return nv.lib.nvfp4_quantize(args["x"], args["in_dtype"], args["rows"], args["K"], args["ld_x"], args["codes"],
+                                 args["scales"], args["g"], args["g_mode"], args["ws"], args["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(in_dtype=7), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(g_mode=3), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(g=None), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(x=None), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(codes=None), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(K=0), nv.NVFP4_ERR_SHAPE),
+    (dict(K=24, ld_x=24), nv.NVFP4_ERR_SHAPE),
+    (dict(rows=-1), nv.NVFP4_ERR_SHAPE),
+    (dict(ld_x=32), nv.NVFP4_ERR_SHAPE),
+    (dict(x=FAKE + 2), nv.NVFP4_ERR_UNSUPPORTED),
+    (dict(ld_x=68), nv.NVFP4_ERR_UNSUPPORTED),            # bf16 row stride not a multiple of 16 bytes
+    (dict(codes=FAKE + 4), nv.NVFP4_ERR_UNSUPPORTED),
+    (dict(ws=None), nv.NVFP4_ERR_WORKSPACE),
+    (dict(ws_bytes=0), nv.NVFP4_ERR_WORKSPACE),
+])
+def test_quantize_validation(kw, status):
+    assert q(**kw) == status
+    assert nv.last_error() != ""
+
+
+def test_quantize_given_mode_needs_no_workspace():
+    if not _no_gpu():
+        pytest.skip("a GPU is visible; this host-only check would launch on fake pointers")
+    assert q(ws=None, ws_bytes=0, g_mode=nv.NVFP4_G_GIVEN) == nv.NVFP4_ERR_NO_DEVICE
+
+
+def test_valid_calls_stop_at_device_check_without_gpu():
+    if not _no_gpu():
+        pytest.skip("a GPU is visible; this host-only check would launch on fake pointers")
+    assert q() == nv.NVFP4_ERR_NO_DEVICE
+    assert "device" in nv.last_error()
+
+
+def test_workspace_query():
+    assert nv.nvfp4_quantize_workspace_bytes(16, 5120) >= 4
+    assert nv.nvfp4_quantize_workspace_bytes(32768, 16384) % 256 == 0
+    assert nv.nvfp4_quantize_workspace_bytes(32768, 16384) <= 1024 * 4
+    assert nv.nvfp4_quantize_workspace_bytes(-1, 16) == 0
+
+
+def expected_blob_bytes(rows, K):
+    n = sum(rows)
+    n_pad = (n + 255) // 256 * 256
+    scales_off = 256 + n_pad * K // 2
+    colscale_off = (scales_off + n_pad * K // 16 + 255) // 256 * 256
+    return colscale_off + n_pad * 4
+
+
+@pytest.mark.parametrize("rows,K", [([5120], 5120), ([4096, 4096, 4096, 4096, 48, 48], 5120), ([256], 512),
+                                    ([16384], 16384), ([1], 128), ([100, 37, 48], 640)])
+def test_packed_weight_bytes(rows, K):
+    got = nv.nvfp4_packed_weight_bytes(rows, K)
+    assert got == expected_blob_bytes(rows, K)
+    # 4.5 bits per weight element, plus the header, padding rows and one FP32 per row
+    n_pad = (sum(rows) + 255) // 256 * 256
+    assert got >= n_pad * K * 9 // 16
+
+
+@pytest.mark.parametrize("rows,K", [([], 512), ([0], 512), ([16], 100), ([16], 144), ([1] * 17, 128)])
+def test_packed_weight_bytes_invalid(rows, K):
+    assert nv.nvfp4_packed_weight_bytes(rows, K) == 0
+
+
+def _pack(n_modules=1, rows=(64,), K=256, blob=FAKE, blob_bytes=1 << 30, codes=FAKE, scales=FAKE, g=FAKE):
+    n = len(rows)
+    r = (ctypes.c_int64 * max(n, 1))(*rows)
+    cp = (ctypes.c_void_p * max(n, 1))(*([codes] * max(n, 1)))
+    sp = (ctypes.c_void_p * max(n, 1))(*([scales] * max(n, 1)))
+    gp = (ctypes.c_void_p * max(n, 1))(*([g] * max(n, 1)))
+    d = nv.WeightDesc()
+    return nv.lib.nvfp4_pack_weights(n_modules, r, K, cp, sp, gp, blob, blob_bytes, ctypes.byref(d), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n_modules=0, rows=()), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(n_modules=17, rows=(1,) * 17), nv.NVFP4_ERR_UNSUPPORTED),
+    (dict(rows=(0,)), nv.NVFP4_ERR_SHAPE),
+    (dict(K=100), nv.NVFP4_ERR_SHAPE),
+    (dict(K=144), nv.NVFP4_ERR_UNSUPPORTED),
+    (dict(codes=None), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(codes=FAKE + 8), nv.NVFP4_ERR_UNSUPPORTED),
+    (dict(blob=None), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(blob=FAKE + 16), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(blob_bytes=1000), nv.NVFP4_ERR_WORKSPACE),
+])
+def test_pack_validation(kw, status):
+    assert _pack(**kw) == status
+
+
+def make_desc(rows=(100, 37, 48), K=640, blob=FAKE):
+    d = nv.WeightDesc()
+    n = sum(rows)
+    d.magic, d.version = nv.NVFP4_WEIGHT_MAGIC, nv.NVFP4_WEIGHT_VERSION
+    d.n, d.k, d.n_padded, d.n_modules = n, K, (n + 255) // 256 * 256, len(rows)
+    off = 0
+    for i, r in enumerate(rows):
+        d.module_rows[i], d.module_row_offset[i] = r, off
+        off += r
+    d.blob = blob
+    d.codes_offset = 256
+    d.scales_offset = 256 + d.n_padded * K // 2
+    d.colscale_offset = (d.scales_offset + d.n_padded * K // 16 + 255) // 256 * 256
+    d.blob_bytes = d.colscale_offset + d.n_padded * 4
+    return d
+
+
+def g_(M=32, d=None, a=FAKE, s=FAKE, gx=FAKE, y=FAKE, ld_y=None, ws=None, ws_bytes=0):
+    d = make_desc() if d is None else d
+    return nv.lib.nvfp4_gemm(M, a, s, gx, ctypes.byref(d) if d is not False else None, y,
+                             d.n if ld_y is None else ld_y, ws, ws_bytes, None)
+
+
+def test_gemm_validation():
+    assert g_(M=-1) == nv.NVFP4_ERR_SHAPE
+    assert g_(M=0) == nv.NVFP4_OK                     # empty: nothing to do
+    assert g_(y=None) == nv.NVFP4_ERR_INVALID_ARG
+    assert g_(a=None) == nv.NVFP4_ERR_INVALID_ARG
+    assert g_(ld_y=100) == nv.NVFP4_ERR_SHAPE
+    assert g_(a=FAKE + 4) == nv.NVFP4_ERR_UNSUPPORTED
+    assert nv.lib.nvfp4_gemm(4, FAKE, FAKE, FAKE, None, FAKE, 1000, None, 0, None) == nv.NVFP4_ERR_INVALID_ARG
+    d = make_desc()
+    d.magic = 0
+    assert g_(d=d) == nv.NVFP4_ERR_DESCRIPTOR
+    d = make_desc()
+    d.version = 9
+    assert g_(d=d) == nv.NVFP4_ERR_DESCRIPTOR
+    d = make_desc()
+    d.n = 999
+    assert g_(d=d) == nv.NVFP4_ERR_DESCRIPTOR
+    d = make_desc()
+    d.module_row_offset[1] = 5
+    assert g_(d=d) == nv.NVFP4_ERR_DESCRIPTOR
+    d = make_desc(blob=FAKE + 64)
+    assert g_(d=d) == nv.NVFP4_ERR_DESCRIPTOR
+    assert nv.lib.nvfp4_unpack_weights(None, FAKE, FAKE, FAKE, None) == nv.NVFP4_ERR_INVALID_ARG
+
+
+def test_gemm_valid_stops_at_device_check_without_gpu():
+    if not _no_gpu():
+        pytest.skip("a GPU is visible; this host-only check would launch on fake pointers")
+    assert g_() == nv.NVFP4_ERR_NO_DEVICE

@@ -1,0 +1,182 @@
+"""Block-scaled GEMM parity on the GPU against the FP64 oracle.
+
+Each output must satisfy |y_gpu - y_ref| <= 1e-5 * sum_k |x^[m,k] w^[n,k]| (the FP32
+accumulation-order error scale), where the oracle quantizes both operands itself
+(its codes are checked bit-for-bit against the GPU's in the same test).  Small
+shapes are compared element by element; the full-size workloads on sampled
+row x column blocks that include every module boundary and the ragged tail."""
+import numpy as np
+import pytest
+import torch
+
+import nvfp4_block_scaled_03_amd as nv
+import workloads
+from gpu_util import DEV, assert_quant_equal, host, oracle_quantize_rows, say, to_dev
+from oracle import nvfp4_ref as ref
+
+pytestmark = pytest.mark.gpu
+F32 = np.float32
+
+
+def gpu_linear(x, x_dtype, ws, w_dtype, g_x=None, g_w=None):
+    xd = to_dev(x, x_dtype)
+    xc, xs, gx = nv.quantize(xd, g=g_x)
+    mods = [nv.quantize(to_dev(w, w_dtype), g=g_w) for w in ws]
+    pw = nv.PackedWeight(mods, x.shape[1])
+    y = nv.gemm(xc, xs, gx, pw)
+    torch.cuda.synchronize()
+    return y, (xc, xs, gx), mods, pw
+
+
+def check_dense(x, x_dtype, ws, w_dtype, what, g_x=None, g_w=None):
+    say(f"gemm parity (dense): {what} M={x.shape[0]} K={x.shape[1]} modules={[w.shape[0] for w in ws]}")
+    y, (xc, xs, gx), mods, _ = gpu_linear(x, x_dtype, ws, w_dtype, g_x, g_w)
+    mode = "compute" if g_x is None else "given"
+    xq = ref.quantize(x, mode, g_x)
+    wq = [ref.quantize(w, "compute" if g_w is None else "given", g_w) for w in ws]
+    assert_quant_equal(xc, xs, gx, xq, what=f"{what} X")
+    for i, (m, q) in enumerate(zip(mods, wq)):
+        assert_quant_equal(*m, q, what=f"{what} W[{i}]")
+    y_ref, a_ref = ref.gemm(xq, wq)
+    ok, worst = ref.gemm_within_tolerance(host(y), y_ref, a_ref)
+    assert ok, f"{what}: worst |dy|/sum|terms| = {worst:.3e}"
+    return y
+
+
+def test_tiny_workload():
+    wl = workloads.make_tiny()
+    check_dense(wl.x, "f32", wl.w, "f32", "tiny")
+
+
+def test_decode_workload():
+    wl = workloads.make_decode()
+    check_dense(wl.x, "bf16", wl.w, "bf16", "decode")
+
+
+@pytest.mark.parametrize("M", [1, 2, 5, 15, 16])
+def test_skinny_shapes(M):
+    x = workloads.random_matrix(100 + M, M, 384, dtype="bf16")
+    ws = [workloads.random_matrix(200 + M, 300, 384, 0.05, dtype="bf16")]
+    check_dense(x, "bf16", ws, "bf16", f"skinny M={M}")
+
+
+@pytest.mark.parametrize("M", [17, 33, 128, 300])
+def test_tiled_ragged_fused(M):
+    x = workloads.random_matrix(300 + M, M, 640, dtype="bf16")
+    ws = [workloads.random_matrix(400 + i, r, 640, s, dtype="bf16")
+          for i, (r, s) in enumerate([(100, 0.02), (37, 0.2), (48, 0.002)])]
+    check_dense(x, "bf16", ws, "bf16", f"tiled fused M={M}")
+
+
+def test_fused_module_mix_skinny():
+    x = workloads.random_matrix(501, 7, 512, dtype="bf16")
+    ws = [workloads.random_matrix(502 + i, r, 512, s, dtype="bf16")
+          for i, (r, s) in enumerate([(64, 0.02), (48, 0.2), (48, 0.002), (16, 3.0)])]
+    check_dense(x, "bf16", ws, "bf16", "skinny fused")
+
+
+def test_gdn_small_m_dense():
+    wl = workloads.make_gdn(M=160)
+    check_dense(wl.x, "bf16", wl.w, "bf16", "gdn M=160")
+
+
+def test_ngpt_without_per_tensor_scaling():
+    wl = workloads.make_ngpt(M=256)
+    check_dense(wl.x, "bf16", [wl.w[0][:512]], "bf16", "ngpt g=1", g_x=1.0, g_w=1.0)
+
+
+def _boundary_cols(wl):
+    cols = [0, wl.N - 1]
+    off = 0
+    for w in wl.w:
+        cols += [off, off + 1, off + w.shape[0] - 2, off + w.shape[0] - 1]
+        off += w.shape[0]
+    return np.array(sorted(set(c for c in cols if 0 <= c < wl.N)))
+
+
+@pytest.mark.parametrize("name", ["gdn", "ngpt", "large"])
+def test_workload_sampled(name):
+    """Full-size workload in the bench launch configuration; sampled rows x columns against the oracle."""
+    wl = workloads.make(name)
+    say(f"gemm parity (sampled): {name} M={wl.M} K={wl.K} N={wl.N}")
+    y, (xc, xs, gx), mods, _ = gpu_linear(wl.x, wl.x_dtype, wl.w, wl.w_dtype)
+    rng = np.random.default_rng(7)
+    rows = np.unique(np.concatenate([[0, wl.M - 1], rng.choice(wl.M, 40, replace=False)]))
+    cols = np.unique(np.concatenate([_boundary_cols(wl), rng.choice(wl.N, 200, replace=False)]))
+    xq = oracle_quantize_rows(wl.x, rows)
+    assert_quant_equal(xc, xs, gx, xq, rows=torch.from_numpy(rows).to(DEV), what=f"{name} X rows")
+    # oracle weight rows for the sampled columns, each with its own module's global scale
+    off, parts = 0, []
+    for w in wl.w:
+        r0, r1 = off, off + w.shape[0]
+        sel = cols[(cols >= r0) & (cols < r1)] - r0
+        if len(sel):
+            parts.append(ref.dequantize(oracle_quantize_rows(w, sel)))
+        off = r1
+    wh = np.concatenate(parts, axis=0)
+    xh = ref.dequantize(xq)
+    y_ref, a_ref = ref.gemm_dequantized(xh, wh)
+    yd = host(y[torch.from_numpy(rows).to(DEV)][:, torch.from_numpy(cols).to(DEV)])
+    ok, worst = ref.gemm_within_tolerance(yd, y_ref, a_ref)
+    assert ok, f"{name}: worst |dy|/sum|terms| = {worst:.3e}"
+    say(f"{name}: worst |dy|/sum|terms| = {worst:.3e} over {yd.size} sampled outputs")
+
+
+def test_fused_equals_per_module():
+    """One fused GEMM over stacked sub-modules = the per-module GEMMs side by side, bit for bit."""
+    wl = workloads.make_gdn(M=96)
+    say("gemm fused == per-module concat")
+    y, (xc, xs, gx), mods, _ = gpu_linear(wl.x, "bf16", wl.w, "bf16")
+    parts = [nv.gemm(xc, xs, gx, nv.PackedWeight([m], wl.K)) for m in mods]
+    torch.cuda.synchronize()
+    assert torch.equal(y, torch.cat(parts, dim=1))
+
+
+def test_shared_scale_pitfall_is_detected():
+    """Negative control: packing module a's codes with module q's global scale (one scale for a
+    fused kernel) corrupts exactly the a columns, and the parity check catches it."""
+    wl = workloads.make_gdn(M=64)
+    say("gemm pitfall negative control")
+    xd = to_dev(wl.x, "bf16")
+    xc, xs, gx = nv.quantize(xd)
+    q = nv.quantize(to_dev(wl.w[0][:256], "bf16"))
+    a = nv.quantize(to_dev(wl.w[4], "bf16"))
+    y_bad = nv.gemm(xc, xs, gx, nv.PackedWeight([q, (a[0], a[1], q[2])], wl.K))
+    torch.cuda.synchronize()
+    xq = ref.quantize(wl.x)
+    y_ref, a_ref = ref.gemm(xq, [ref.quantize(wl.w[0][:256]), ref.quantize(wl.w[4])])
+    ok_q, _ = ref.gemm_within_tolerance(host(y_bad)[:, :256], y_ref[:, :256], a_ref[:, :256])
+    ok_a, worst_a = ref.gemm_within_tolerance(host(y_bad)[:, 256:], y_ref[:, 256:], a_ref[:, 256:])
+    assert ok_q and not ok_a and worst_a > 1e-2
+
+
+def test_unpack_round_trip():
+    wl = workloads.make_gdn(M=16)
+    say("pack/unpack round trip")
+    mods = [nv.quantize(to_dev(w[:200], "bf16")) for w in wl.w]
+    pw = nv.PackedWeight(mods, wl.K)
+    c, s, cs = pw.unpack()
+    torch.cuda.synchronize()
+    assert torch.equal(c, torch.cat([m[0] for m in mods]))
+    assert torch.equal(s, torch.cat([m[1] for m in mods]))
+    want = torch.cat([m[2].expand(m[0].shape[0]) for m in mods])
+    assert torch.equal(cs, want)
+
+
+def test_clone_and_determinism():
+    wl = workloads.make_decode()
+    say("gemm clone + determinism")
+    y, (xc, xs, gx), mods, pw = gpu_linear(wl.x, "bf16", wl.w, "bf16")
+    pw2 = pw.clone()
+    ys = [nv.gemm(xc, xs, gx, p) for p in (pw, pw2, pw)]
+    torch.cuda.synchronize()
+    for t in ys:
+        assert torch.equal(t, y)
+
+
+def test_empty_m():
+    wl = workloads.make_tiny()
+    _, (xc, xs, gx), _, pw = gpu_linear(wl.x, "f32", wl.w, "f32")
+    y = torch.full((0, pw.n), 7.0, device=DEV)
+    nv.nvfp4_gemm(0, xc, xs, gx, pw.desc, y, pw.n)
+    torch.cuda.synchronize()
