@@ -93,8 +93,8 @@ def main():
     codes, scales, g = nv.empty_quantized(M, K, dev)
     ws = torch.empty((max(nv.nvfp4_quantize_workspace_bytes(M, K), 256),), dtype=torch.uint8, device=dev)
     y = torch.empty((M, N), dtype=torch.float32, device=dev)
-    gws = nv.nvfp4_gemm_workspace_bytes(M, packed.desc)
-    gemm_ws = torch.empty((max(gws, 256),), dtype=torch.uint8, device=dev)
+    gemm_ws = torch.empty((max(nv.nvfp4_gemm_workspace_bytes(M, packed.desc), 256),), dtype=torch.uint8,
+                          device=dev)
     if wl.quantize_w_in_step:
         wq_bufs = [nv.empty_quantized(w.shape[0], K, dev) for w in w_dev]
         wq_ws = [torch.empty((max(nv.nvfp4_quantize_workspace_bytes(w.shape[0], K), 256),), dtype=torch.uint8,
@@ -105,10 +105,10 @@ def main():
             for w, (c, s, gg), wsb in zip(w_dev, wq_bufs, wq_ws):
                 nv.nvfp4_quantize(w, c, s, gg, nv.NVFP4_G_COMPUTE, wsb)
         nv.nvfp4_quantize(x, codes, scales, g, nv.NVFP4_G_COMPUTE, ws, rows=M, K=K, ld_x=K, in_dtype=in_dtype)
-        nv.nvfp4_gemm(M, codes, scales, g, weights[i % copies].desc, y, N, gemm_ws, gws)
+        nv.nvfp4_gemm(M, codes, scales, g, weights[i % copies].desc, y, N, gemm_ws)
 
     def gemm_only(i):
-        nv.nvfp4_gemm(M, codes, scales, g, weights[i % copies].desc, y, N, gemm_ws, gws)
+        nv.nvfp4_gemm(M, codes, scales, g, weights[i % copies].desc, y, N, gemm_ws)
 
     def quant_only(i):
         nv.nvfp4_quantize(x, codes, scales, g, nv.NVFP4_G_COMPUTE, ws, rows=M, K=K, ld_x=K, in_dtype=in_dtype)

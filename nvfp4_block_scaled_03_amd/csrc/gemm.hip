@@ -14,9 +14,29 @@
 // runs of the k-step (matching one 16-byte load), and each 8-element chunk a
 // lane feeds to one instruction lies inside one 16-element block, so a lane
 // applies exactly one block scale per chunk.
+//
+// All operand loads are buffer loads: a scalar resource per tensor, one 32-bit
+// per-lane offset, and the per-k-step / per-tile advance in a scalar offset.
+// Reads past the end of a tensor return zero, which is how rows beyond M (a
+// ragged last tile) contribute nothing without any clamping.
 #include "common.h"
 
 namespace nvfp4 {
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)(uint32_t)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 bload16(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+__device__ __forceinline__ uint32_t bload4(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
+}
+__device__ __forceinline__ uint32_t bload2(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, (int)soff, 0);
+}
 
 __device__ __forceinline__ _Float16 scale_byte(uint32_t packed, int i) {
     return e4m3_to_f16((packed >> (8 * i)) & 0xFFu);
@@ -27,45 +47,95 @@ __device__ __forceinline__ uint32_t word_of(const uint4& v, int i) {
 }
 
 // ---------------------------------------------------------------------------
-// Skinny GEMM (M <= 16): one workgroup per 16 weight rows, 4 wavefronts split
-// the k-steps and reduce through LDS.  16x16x32 FP16 instructions with the
-// weight rows as the A operand and the (at most 16) tokens as B.
+// Skinny GEMM (M <= 16), bound by the weight stream from HBM.  One workgroup per
+// 16 weight rows; its 4 wavefronts split the k-steps (wave w takes k-steps
+// w, w+4, ...) and reduce through LDS.  Each wavefront issues every load of a
+// pass (16 B of codes and 2 B of scales per lane for the weights and for the
+// activations) before it decodes anything, so the whole weight stream of the
+// grid is in flight at once.  16x16x32 FP16 instructions with the weight rows
+// as the A operand and the tokens as B.
 // ---------------------------------------------------------------------------
 constexpr int kSkinnyM = 16;
+constexpr int kSkWaves = 4;
+constexpr int kSkMaxKs = 12;
 
+// One k-step of the skinny product: decode the weight and activation chunks
+// (one E4M3 scale per 16-element block) and accumulate four 16x16x32 products.
+__device__ __forceinline__ void skinny_step(float4v& acc, const uint4& wv, uint32_t ws, const uint4& xv,
+                                            uint32_t xs) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const half8 a = decode8(word_of(wv, c), scale_byte(ws, c >> 1));
+        const half8 b = decode8(word_of(xv, c), scale_byte(xs, c >> 1));
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
+    }
+}
+
+// NKS > 0: every wavefront owns exactly NKS k-steps (K = 4*NKS*128); all loads
+// are issued up front and each k-step is consumed as soon as its own loads have
+// landed.  NKS == 0: any K, in passes of up to kSkMaxKs k-steps per wavefront.
+template <int NKS>
 __global__ __launch_bounds__(256) void gemm_skinny_kernel(int M, const uint8_t* __restrict__ a_codes,
                                                           const uint8_t* __restrict__ a_scales,
                                                           const float* __restrict__ g_x,
                                                           const uint8_t* __restrict__ w_codes,
                                                           const uint8_t* __restrict__ w_scales,
-                                                          const float* __restrict__ colscale, int64_t N, int64_t K,
-                                                          float* __restrict__ y, int64_t ld_y) {
+                                                          const float* __restrict__ colscale, int64_t N,
+                                                          int64_t n_pad, int64_t K, float* __restrict__ y,
+                                                          int64_t ld_y) {
     const int rb = blockIdx.x;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int64_t KS = K / kPackK;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int KS = (int)(K / kPackK);
     const int r16 = lane & 15, kg = lane >> 4;
-    const int tok = r16 < M ? r16 : M - 1;
 
-    const uint8_t* wc = w_codes + (size_t)rb * KS * 1024 + kg * 256 + r16 * 16;
-    const uint8_t* wsc = w_scales + (size_t)rb * KS * 128 + r16 * 8 + kg * 2;
-    const uint8_t* xc = a_codes + (size_t)tok * (K / 2) + kg * 16;
-    const uint8_t* xsc = a_scales + (size_t)tok * (K / 16) + kg * 2;
+    const rsrc_t rwc = make_rsrc(w_codes, (uint64_t)n_pad * K / 2);
+    const rsrc_t rws = make_rsrc(w_scales, (uint64_t)n_pad * K / 16);
+    const rsrc_t rxc = make_rsrc(a_codes, (uint64_t)M * K / 2);     // tokens >= M read as zero
+    const rsrc_t rxs = make_rsrc(a_scales, (uint64_t)M * K / 16);
+    const uint32_t wc_off = (uint32_t)rb * KS * 1024 + kg * 256 + r16 * 16;
+    const uint32_t ws_off = (uint32_t)rb * KS * 128 + r16 * 8 + kg * 2;
+    const uint32_t xc_off = (uint32_t)(r16 * (K / 2)) + kg * 16;
+    const uint32_t xs_off = (uint32_t)(r16 * (K / 16)) + kg * 2;
 
     float4v acc = {0.f, 0.f, 0.f, 0.f};
-    for (int64_t ks = wave; ks < KS; ks += 4) {
-        const uint4 wv = *reinterpret_cast<const uint4*>(wc + ks * 1024);
-        const uint32_t ws = *reinterpret_cast<const uint16_t*>(wsc + ks * 128);
-        const uint4 xv = *reinterpret_cast<const uint4*>(xc + ks * 64);
-        const uint32_t xs = *reinterpret_cast<const uint16_t*>(xsc + ks * 8);
+    if constexpr (NKS > 0) {
+        uint4 wv[NKS], xv[NKS];
+        uint32_t ws[NKS], xs[NKS];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const half8 a = decode8(word_of(wv, c), scale_byte(ws, c >> 1));
-            const half8 b = decode8(word_of(xv, c), scale_byte(xs, c >> 1));
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
+        for (int j = 0; j < NKS; ++j) {   // loads land in issue order: interleave so k-step j is usable early
+            const uint32_t ks = wave + kSkWaves * j;
+            wv[j] = bload16(rwc, wc_off, ks * 1024);
+            ws[j] = bload2(rws, ws_off, ks * 128);
+            xv[j] = bload16(rxc, xc_off, ks * 64);
+            xs[j] = bload2(rxs, xs_off, ks * 8);
+        }
+        // keep every load ahead of the math: the scheduler would otherwise sink
+        // loads next to their uses and leave only a few in flight
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < NKS; ++j) skinny_step(acc, wv[j], ws[j], xv[j], xs[j]);
+    } else {
+        for (int base = wave; base < KS; base += kSkWaves * kSkMaxKs) {
+            uint4 wv[kSkMaxKs], xv[kSkMaxKs];
+            uint32_t ws[kSkMaxKs], xs[kSkMaxKs];
+#pragma unroll
+            for (int j = 0; j < kSkMaxKs; ++j) {
+                const int ks = base + kSkWaves * j;
+                if (ks < KS) {
+                    wv[j] = bload16(rwc, wc_off, (uint32_t)ks * 1024);
+                    ws[j] = bload2(rws, ws_off, (uint32_t)ks * 128);
+                    xv[j] = bload16(rxc, xc_off, (uint32_t)ks * 64);
+                    xs[j] = bload2(rxs, xs_off, (uint32_t)ks * 8);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < kSkMaxKs; ++j)
+                if (base + kSkWaves * j < KS) skinny_step(acc, wv[j], ws[j], xv[j], xs[j]);
         }
     }
 
-    __shared__ float red[3][64][4];
+    __shared__ float red[kSkWaves - 1][64][4];
     if (wave > 0) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) red[wave - 1][lane][r] = acc[r];
@@ -83,89 +153,219 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(int M, const uint8_t* 
 }
 
 // ---------------------------------------------------------------------------
-// Tiled GEMM: 128x128 output tile per workgroup, 2x2 wavefronts of 64x64, each
-// a 2x2 grid of 32x32x16 FP16 instructions.  Operands load straight from
-// global memory into registers (activations row-major, weights pre-swizzled).
+// Tiled GEMM: a workgroup of 2x2 wavefronts computes a (2*TM*32) x (2*TN*32)
+// output tile; each wavefront a TM x TN grid of 32x32x16 FP16 instructions.
+//
+// Operands move global -> registers -> LDS in a two-stage ring: while the
+// wavefronts decode and multiply k-step ks out of one LDS stage, the packed
+// codes and scales of k-step ks+1 are already in registers (16-byte buffer
+// loads issued a whole compute phase earlier) and are written to the other
+// stage after a barrier.  Each operand byte is fetched once per workgroup.
+//
+// LDS stage layout (bytes), "lane" = l32 + 32*h of the consuming wavefront:
+//   A codes  [row block 8][half p 2][lane 64][16]  rows rb*32+l32, bytes h*32+p*16 of the k-step
+//   B codes  [col block 8][half p 2][lane 64][16]  packed unit kg = 2h+p of column cb*32+l32
+//   A scales [row block 8][lane 64][4]             block scales 4h..4h+3 of the row
+//   B scales [col block 8][lane 64][4]
+// so every fragment read is one ds_read_b128 (or b32) of a contiguous,
+// bank-conflict-free 1 KB (256 B) span.
+//
+// Workgroups are numbered so that the ones sharing an XCD (consecutive
+// hardware ids go round-robin over the 8 XCDs) work on a compact group of
+// tiles and reuse operands from that XCD's L2.
 // ---------------------------------------------------------------------------
-constexpr int kTileM = 128, kTileN = 128;
+constexpr int kXcds = 8;
+constexpr int kGroupM = 8;   // tile rows per group of the grouped tile order
 
+template <int TM, int TN>
+struct TileGeom {
+    static constexpr int BM = 2 * TM * 32, BN = 2 * TN * 32;
+    static constexpr int RB = BM / 32, CB = BN / 32;               // 32-row / 32-column blocks
+    static constexpr int A_CODES = RB * 2 * 1024;
+    static constexpr int B_CODES = CB * 2 * 1024;
+    static constexpr int A_SC = RB * 256, B_SC = CB * 256;
+    static constexpr int STAGE = A_CODES + B_CODES + A_SC + B_SC;
+    static constexpr int A_CHUNKS = A_CODES / 16 / 256, B_CHUNKS = B_CODES / 16 / 256;   // per thread
+    static constexpr int AS_WORDS = A_SC / 4 / 256, BS_WORDS = B_SC / 4 / 256;
+};
+
+template <int TM, int TN>
+struct Staging {
+    uint4 a[TileGeom<TM, TN>::A_CHUNKS], b[TileGeom<TM, TN>::B_CHUNKS];
+    uint32_t as[TileGeom<TM, TN>::AS_WORDS], bs[TileGeom<TM, TN>::BS_WORDS];
+};
+
+struct TileSrc {
+    rsrc_t ac, as, bc, bs;
+    uint32_t a_lane, as_lane, b_lane, bs_lane;   // per-lane offsets inside a 32-row / 32-column block
+    uint32_t a_tile, as_tile, b_tile, bs_tile;   // offsets of the workgroup tile's first block
+    uint32_t a_blk, as_blk, b_blk, bs_blk;       // advance per 32-row / 32-column block
+};
+
+// Global -> registers for k-step ks.  Thread t of wavefront w stages slabs w, w+4, ...
+template <int TM, int TN>
+__device__ __forceinline__ void stage_load(Staging<TM, TN>& st, const TileSrc& s, uint32_t ks, int wave) {
+    using G = TileGeom<TM, TN>;
+#pragma unroll
+    for (int u = 0; u < G::A_CHUNKS; ++u) {
+        const int slab = wave + 4 * u, rb = slab >> 1, p = slab & 1;
+        st.a[u] = bload16(s.ac, s.a_lane, s.a_tile + rb * s.a_blk + ks * 64 + p * 16);
+    }
+#pragma unroll
+    for (int u = 0; u < G::B_CHUNKS; ++u) {
+        const int slab = wave + 4 * u, cb = slab >> 1, p = slab & 1;
+        st.b[u] = bload16(s.bc, s.b_lane, s.b_tile + cb * s.b_blk + ks * 1024 + p * 256);
+    }
+#pragma unroll
+    for (int u = 0; u < G::AS_WORDS; ++u)
+        st.as[u] = bload4(s.as, s.as_lane, s.as_tile + (wave + 4 * u) * s.as_blk + ks * 8);
+#pragma unroll
+    for (int u = 0; u < G::BS_WORDS; ++u)
+        st.bs[u] = bload4(s.bs, s.bs_lane, s.bs_tile + (wave + 4 * u) * s.bs_blk + ks * 128);
+}
+
+template <int TM, int TN>
+__device__ __forceinline__ void stage_store(uint8_t* stage, const Staging<TM, TN>& st, int wave, int lane) {
+    using G = TileGeom<TM, TN>;
+#pragma unroll
+    for (int u = 0; u < G::A_CHUNKS; ++u)
+        *reinterpret_cast<uint4*>(stage + (wave + 4 * u) * 1024 + lane * 16) = st.a[u];
+#pragma unroll
+    for (int u = 0; u < G::B_CHUNKS; ++u)
+        *reinterpret_cast<uint4*>(stage + G::A_CODES + (wave + 4 * u) * 1024 + lane * 16) = st.b[u];
+#pragma unroll
+    for (int u = 0; u < G::AS_WORDS; ++u)
+        *reinterpret_cast<uint32_t*>(stage + G::A_CODES + G::B_CODES + (wave + 4 * u) * 256 + lane * 4) = st.as[u];
+#pragma unroll
+    for (int u = 0; u < G::BS_WORDS; ++u)
+        *reinterpret_cast<uint32_t*>(stage + G::A_CODES + G::B_CODES + G::A_SC + (wave + 4 * u) * 256 + lane * 4) =
+            st.bs[u];
+}
+
+// Decode and multiply one k-step held in an LDS stage.
+template <int TM, int TN>
+__device__ __forceinline__ void stage_compute(float16v (&acc)[TM][TN], const uint8_t* stage, int wm, int wn,
+                                              int lane) {
+    using G = TileGeom<TM, TN>;
+    uint32_t asc[TM], bsc[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+        asc[i] = *reinterpret_cast<const uint32_t*>(stage + G::A_CODES + G::B_CODES + (wm * TM + i) * 256 + lane * 4);
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+        bsc[j] = *reinterpret_cast<const uint32_t*>(stage + G::A_CODES + G::B_CODES + G::A_SC +
+                                                    (wn * TN + j) * 256 + lane * 4);
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        uint4 av[TM], bv[TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+            av[i] = *reinterpret_cast<const uint4*>(stage + ((wm * TM + i) * 2 + p) * 1024 + lane * 16);
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+            bv[j] = *reinterpret_cast<const uint4*>(stage + G::A_CODES + ((wn * TN + j) * 2 + p) * 1024 + lane * 16);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            half8 a[TM], b[TN];
+#pragma unroll
+            for (int i = 0; i < TM; ++i) a[i] = decode8(word_of(av[i], c), scale_byte(asc[i], 2 * p + (c >> 1)));
+#pragma unroll
+            for (int j = 0; j < TN; ++j) b[j] = decode8(word_of(bv[j], c), scale_byte(bsc[j], 2 * p + (c >> 1)));
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+        }
+    }
+}
+
+template <int TM, int TN>
 __global__ __launch_bounds__(256) void gemm_tile_kernel(int64_t M, const uint8_t* __restrict__ a_codes,
                                                         const uint8_t* __restrict__ a_scales,
                                                         const float* __restrict__ g_x,
                                                         const uint8_t* __restrict__ w_codes,
                                                         const uint8_t* __restrict__ w_scales,
-                                                        const float* __restrict__ colscale, int64_t N, int64_t K,
-                                                        float* __restrict__ y, int64_t ld_y) {
-    const int64_t tn = blockIdx.x, tm = blockIdx.y;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+                                                        const float* __restrict__ colscale, int64_t N,
+                                                        int64_t n_pad, int64_t K, float* __restrict__ y,
+                                                        int64_t ld_y, int tiles_m, int tiles_n) {
+    using G = TileGeom<TM, TN>;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * G::STAGE];
+
+    // hardware id -> logical id: the workgroups of one XCD get consecutive logical ids
+    const int nwg = tiles_m * tiles_n;
+    const int hw = blockIdx.x;
+    const int per_xcd = (nwg + kXcds - 1) / kXcds;
+    const int full = nwg - (per_xcd - 1) * kXcds;   // XCDs that get per_xcd workgroups
+    const int xcd = hw % kXcds, slot = hw / kXcds;
+    const int lid = (xcd < full ? xcd * per_xcd : full * per_xcd + (xcd - full) * (per_xcd - 1)) + slot;
+    // grouped order: kGroupM tile rows at a time, column-major inside the group
+    const int group = lid / (kGroupM * tiles_n);
+    const int first_m = group * kGroupM;
+    const int gm = min(tiles_m - first_m, kGroupM);
+    const int in_group = lid - group * kGroupM * tiles_n;
+    const int tm = first_m + in_group % gm;
+    const int tn = in_group / gm;
+
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int wm = wave >> 1, wn = wave & 1;
     const int l32 = lane & 31, h = lane >> 5;
-    const int64_t KS = K / kPackK;
+    const uint32_t KS = (uint32_t)(K / kPackK);
 
-    const uint8_t* ac[2];
-    const uint8_t* as[2];
-    const uint8_t* bc[2];
-    const uint8_t* bs[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        int64_t m = tm * kTileM + wm * 64 + i * 32 + l32;
-        if (m >= M) m = M - 1;
-        ac[i] = a_codes + m * (K / 2) + h * 32;
-        as[i] = a_scales + m * (K / 16) + h * 4;
-        const int64_t n = tn * kTileN + wn * 64 + i * 32 + l32;
-        bc[i] = w_codes + (size_t)(n >> 4) * KS * 1024 + (2 * h) * 256 + (n & 15) * 16;
-        bs[i] = w_scales + (size_t)(n >> 4) * KS * 128 + (n & 15) * 8 + h * 4;
-    }
+    TileSrc s;
+    s.ac = make_rsrc(a_codes, (uint64_t)M * K / 2);        // rows >= M read as zero
+    s.as = make_rsrc(a_scales, (uint64_t)M * K / 16);
+    s.bc = make_rsrc(w_codes, (uint64_t)n_pad * K / 2);
+    s.bs = make_rsrc(w_scales, (uint64_t)n_pad * K / 16);
+    s.a_lane = (uint32_t)l32 * (uint32_t)(K / 2) + h * 32;
+    s.as_lane = (uint32_t)l32 * (uint32_t)(K / 16) + h * 4;
+    s.b_lane = (uint32_t)(l32 >> 4) * KS * 1024 + (2 * h) * 256 + (l32 & 15) * 16;
+    s.bs_lane = (uint32_t)(l32 >> 4) * KS * 128 + (l32 & 15) * 8 + h * 4;
+    s.a_blk = 32 * (uint32_t)(K / 2);
+    s.as_blk = 32 * (uint32_t)(K / 16);
+    s.b_blk = 2 * KS * 1024;     // 32 columns = two 16-row packed blocks
+    s.bs_blk = 2 * KS * 128;
+    s.a_tile = (uint32_t)tm * G::RB * s.a_blk;
+    s.as_tile = (uint32_t)tm * G::RB * s.as_blk;
+    s.b_tile = (uint32_t)tn * G::CB * s.b_blk;
+    s.bs_tile = (uint32_t)tn * G::CB * s.bs_blk;
 
-    float16v acc[2][2];
+    float16v acc[TM][TN];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < TN; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    for (int64_t ks = 0; ks < KS; ++ks) {
-        uint4 alo[2], ahi[2], blo[2], bhi[2];
-        uint32_t asc[2], bsc[2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            alo[i] = *reinterpret_cast<const uint4*>(ac[i] + ks * 64);
-            ahi[i] = *reinterpret_cast<const uint4*>(ac[i] + ks * 64 + 16);
-            asc[i] = *reinterpret_cast<const uint32_t*>(as[i] + ks * 8);
-            blo[i] = *reinterpret_cast<const uint4*>(bc[i] + ks * 1024);
-            bhi[i] = *reinterpret_cast<const uint4*>(bc[i] + ks * 1024 + 256);
-            bsc[i] = *reinterpret_cast<const uint32_t*>(bs[i] + ks * 128);
-        }
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            half8 a[2], b[2];
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const uint32_t aw = c < 4 ? word_of(alo[i], c) : word_of(ahi[i], c - 4);
-                const uint32_t bw = c < 4 ? word_of(blo[i], c) : word_of(bhi[i], c - 4);
-                a[i] = decode8(aw, scale_byte(asc[i], c >> 1));
-                b[i] = decode8(bw, scale_byte(bsc[i], c >> 1));
-            }
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+    Staging<TM, TN> st;
+    stage_load<TM, TN>(st, s, 0, wave);
+    stage_store<TM, TN>(lds, st, wave, lane);
+    if (KS > 1) stage_load<TM, TN>(st, s, 1, wave);
+    __syncthreads();
+    for (uint32_t ks = 0; ks < KS; ++ks) {
+        uint8_t* cur = lds + (ks & 1) * G::STAGE;
+        stage_compute<TM, TN>(acc, cur, wm, wn, lane);
+        if (ks + 1 < KS) {
+            __syncthreads();                                  // everyone is done with the other stage
+            stage_store<TM, TN>(lds + ((ks + 1) & 1) * G::STAGE, st, wave, lane);
+            if (ks + 2 < KS) stage_load<TM, TN>(st, s, ks + 2, wave);
+            __syncthreads();                                  // stage ks+1 is complete
         }
     }
 
     const float gx = g_x[0];
+    const int64_t n0 = (int64_t)tn * G::BN + wn * (TN * 32) + l32;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int64_t n = tn * kTileN + wn * 64 + j * 32 + l32;
+    for (int j = 0; j < TN; ++j) {
+        const int64_t n = n0 + j * 32;
         if (n >= N) continue;
         const float cs = gx * colscale[n];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < TM; ++i) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int64_t m = tm * kTileM + wm * 64 + i * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
+                const int64_t m = (int64_t)tm * G::BM + wm * (TM * 32) + i * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
                 if (m < M) y[m * ld_y + n] = acc[i][j][r] * cs;
             }
         }
@@ -181,12 +381,30 @@ hipError_t launch_gemm(int64_t M, const uint8_t* a_codes, const uint8_t* a_scale
     const uint8_t* wsc = blob + d.scales_offset;
     const float* cs = reinterpret_cast<const float*>(blob + d.colscale_offset);
     if (M <= kSkinnyM) {
-        hipLaunchKernelGGL(gemm_skinny_kernel, dim3((unsigned)(d.n_padded / 16)), dim3(256), 0, stream,
-                           (int)M, a_codes, a_scales, g_x, wc, wsc, cs, d.n, d.k, y, ld_y);
+        const int64_t KS = d.k / kPackK;
+        const dim3 grid((unsigned)(d.n_padded / 16)), block(256);
+        const int args_M = (int)M;
+#define NVFP4_SKINNY(NKS) hipLaunchKernelGGL((gemm_skinny_kernel<NKS>), grid, block, 0, stream, args_M, a_codes, \
+                                             a_scales, g_x, wc, wsc, cs, d.n, d.n_padded, d.k, y, ld_y)
+        switch (KS % kSkWaves == 0 ? KS / kSkWaves : 0) {
+            case 1: NVFP4_SKINNY(1); break;
+            case 2: NVFP4_SKINNY(2); break;
+            case 4: NVFP4_SKINNY(4); break;
+            case 8: NVFP4_SKINNY(8); break;
+            case 10: NVFP4_SKINNY(10); break;
+            case 12: NVFP4_SKINNY(12); break;
+            case 16: NVFP4_SKINNY(16); break;
+            default: NVFP4_SKINNY(0); break;
+        }
+#undef NVFP4_SKINNY
+    } else if (M <= 128) {
+        const int tiles_m = (int)((M + 127) / 128), tiles_n = (int)(d.n_padded / 128);
+        hipLaunchKernelGGL((gemm_tile_kernel<2, 2>), dim3(tiles_m * tiles_n), dim3(256), 0, stream, M, a_codes,
+                           a_scales, g_x, wc, wsc, cs, d.n, d.n_padded, d.k, y, ld_y, tiles_m, tiles_n);
     } else {
-        dim3 grid((unsigned)(d.n_padded / kTileN), (unsigned)((M + kTileM - 1) / kTileM));
-        hipLaunchKernelGGL(gemm_tile_kernel, grid, dim3(256), 0, stream, M, a_codes, a_scales, g_x, wc, wsc, cs,
-                           d.n, d.k, y, ld_y);
+        const int tiles_m = (int)((M + 255) / 256), tiles_n = (int)(d.n_padded / 256);
+        hipLaunchKernelGGL((gemm_tile_kernel<4, 4>), dim3(tiles_m * tiles_n), dim3(256), 0, stream, M, a_codes,
+                           a_scales, g_x, wc, wsc, cs, d.n, d.n_padded, d.k, y, ld_y, tiles_m, tiles_n);
     }
     return hipGetLastError();
 }

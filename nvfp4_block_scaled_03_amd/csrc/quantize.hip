@@ -45,15 +45,16 @@ __device__ __forceinline__ float wave_max(float m) {
     return m;
 }
 
+template <int kThreads>
 __device__ __forceinline__ float block_max(float m) {
-    __shared__ float red[kQThreads / 64];
+    __shared__ float red[kThreads / 64];
     m = wave_max(m);
     const int wid = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0) red[wid] = m;
     __syncthreads();
     float r = red[0];
 #pragma unroll
-    for (int i = 1; i < kQThreads / 64; ++i) r = fmaxf(r, red[i]);
+    for (int i = 1; i < kThreads / 64; ++i) r = fmaxf(r, red[i]);
     __syncthreads();
     return r;
 }
@@ -85,7 +86,7 @@ __global__ __launch_bounds__(kQThreads) void amax_partials_kernel(const T* __res
             }
         }
     }
-    m = block_max(m);
+    m = block_max<kQThreads>(m);
     if (threadIdx.x == 0) partials[blockIdx.x] = m;
 }
 
@@ -132,7 +133,7 @@ __global__ __launch_bounds__(kQThreads) void encode_kernel(const T* __restrict__
     } else {
         float m = 0.0f;
         for (int i = threadIdx.x; i < n_partials; i += kQThreads) m = fmaxf(m, partials[i]);
-        m = block_max(m);
+        m = block_max<kQThreads>(m);
         if (threadIdx.x == 0) {
             const float g = global_scale_from_amax(m);
             s_senc = 1.0f / g;

@@ -180,3 +180,42 @@ def test_empty_m():
     y = torch.full((0, pw.n), 7.0, device=DEV)
     nv.nvfp4_gemm(0, xc, xs, gx, pw.desc, y, pw.n)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("name,M", [("decode", None), ("gdn", 96)])
+def test_graph_replays_match_eager(name, M):
+    """Quantize + GEMM captured in a HIP graph: every replay (with eager work in between) equals the eager result."""
+    wl = workloads.make(name) if M is None else workloads.make(name, M=M)
+    say(f"graph replay vs eager: {name}")
+    xd = to_dev(wl.x, "bf16")
+    mods = [nv.quantize(to_dev(w, "bf16")) for w in wl.w]
+    pw = nv.PackedWeight(mods, wl.K)
+    codes, scales, g = nv.empty_quantized(wl.M, wl.K)
+    ws = torch.empty((max(nv.nvfp4_quantize_workspace_bytes(wl.M, wl.K), 256),), dtype=torch.uint8, device=DEV)
+    y = torch.empty((wl.M, wl.N), dtype=torch.float32, device=DEV)
+
+    def step():
+        nv.nvfp4_quantize(xd, codes, scales, g, nv.NVFP4_G_COMPUTE, ws)
+        nv.nvfp4_gemm(wl.M, codes, scales, g, pw.desc, y, wl.N)
+
+    step()
+    torch.cuda.synchronize()
+    want = (y.clone(), codes.clone(), scales.clone(), g.clone())
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        step()
+    torch.cuda.synchronize()
+    for i in range(4):
+        y.zero_()
+        codes.zero_()
+        g.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, want[0]) and torch.equal(codes, want[1]) and torch.equal(scales, want[2]) \
+            and torch.equal(g, want[3]), f"replay {i} differs from eager"
+        _ = (xd.float() * 2).sum().item()      # unrelated eager work between replays
