@@ -92,9 +92,11 @@ def main():
 
     codes, scales, g = nv.empty_quantized(M, K, dev)
     ws = torch.empty((max(nv.nvfp4_quantize_workspace_bytes(M, K), 256),), dtype=torch.uint8, device=dev)
+    lin_ws = nv.linear_workspace(M, xdt, packed, dev)       # zero-filled once, reused by every step
+    skinny = M <= 16     # few-token path: amax kernel + one fused quantize-and-product kernel
     y = torch.empty((M, N), dtype=torch.float32, device=dev)
-    gemm_ws = torch.empty((max(nv.nvfp4_gemm_workspace_bytes(M, packed.desc), 256),), dtype=torch.uint8,
-                          device=dev)
+    gemm_ws = torch.zeros((max(nv.nvfp4_gemm_workspace_bytes(M, packed.desc), 256),), dtype=torch.uint8,
+                          device=dev)       # split-K counters start at zero; every call leaves them so
     if wl.quantize_w_in_step:
         wq_bufs = [nv.empty_quantized(w.shape[0], K, dev) for w in w_dev]
         wq_ws = [torch.empty((max(nv.nvfp4_quantize_workspace_bytes(w.shape[0], K), 256),), dtype=torch.uint8,
@@ -104,8 +106,12 @@ def main():
         if wl.quantize_w_in_step:   # tiny case: both operands quantized inside the step
             for w, (c, s, gg), wsb in zip(w_dev, wq_bufs, wq_ws):
                 nv.nvfp4_quantize(w, c, s, gg, nv.NVFP4_G_COMPUTE, wsb)
-        nv.nvfp4_quantize(x, codes, scales, g, nv.NVFP4_G_COMPUTE, ws, rows=M, K=K, ld_x=K, in_dtype=in_dtype)
-        nv.nvfp4_gemm(M, codes, scales, g, weights[i % copies].desc, y, N, gemm_ws)
+        nv.nvfp4_linear(x, codes, scales, g, weights[i % copies].desc, y, lin_ws, M=M, ld_x=K, in_dtype=in_dtype,
+                        ld_y=N)
+
+    def fused_only(i):   # the fused kernel alone: the global scale handed in (that of the last step)
+        nv.nvfp4_linear(x, codes, scales, g, weights[i % copies].desc, y, lin_ws, g_mode=nv.NVFP4_G_GIVEN, M=M,
+                        ld_x=K, in_dtype=in_dtype, ld_y=N)
 
     def gemm_only(i):
         nv.nvfp4_gemm(M, codes, scales, g, weights[i % copies].desc, y, N, gemm_ws)
@@ -159,22 +165,31 @@ def main():
     # dominant kernel and the quantizer alone, same launch configuration, events on the launch stream
     k_steps = max(steps, rot)
     t_gemm = timed(gemm_only, k_steps, min(warmup, k_steps)) / k_steps
+    t_fused = timed(fused_only, k_steps, min(warmup, k_steps)) / k_steps if skinny else None
     t_quant = timed(quant_only, k_steps, min(warmup, k_steps)) / k_steps
 
     flops = 2.0 * M * N * K
     tflops = flops / t_step / 1e12
     w_bytes = N * K * 9 // 16
     x_q_bytes = M * K * 9 // 16
-    gemm_bytes = w_bytes + x_q_bytes + M * N * 4
-    if name == "decode":
-        roof = {"bound": "hbm", "achieved": gemm_bytes / t_gemm / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    x_in_bytes = M * K * (2 if wl.x_dtype == "bf16" else 4)
+    if skinny:
+        # the fused kernel quantizes the activations and takes the product: its bytes are the
+        # weights (codes + scales), the activations in, their codes and scales out, and Y
+        kern, t_kern = "skinny_kernel (quantize + product)", t_fused
+        kern_bytes = w_bytes + x_in_bytes + x_q_bytes + M * N * 4
     else:
-        roof = {"bound": "mfma", "achieved": flops / t_gemm / 1e12, "peak": F16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s"}
+        kern, t_kern = "gemm_tile_kernel", t_gemm
+        kern_bytes = w_bytes + x_q_bytes + M * N * 4
+    if M <= 16:
+        roof = {"bound": "hbm", "achieved": kern_bytes / t_kern / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": flops / t_kern / 1e12, "peak": F16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = None
-    roof["kernel"] = "gemm_skinny_kernel" if M <= 16 else "gemm_tile_kernel"
-    roof["kernel_us"] = t_gemm * 1e6
-    roof["algorithmic_bytes_per_launch"] = gemm_bytes
+    roof["kernel"] = kern
+    roof["kernel_us"] = t_kern * 1e6
+    roof["algorithmic_bytes_per_launch"] = kern_bytes
 
     # parity of the last step (codes bit-exact, outputs within tolerance), on sampled rows for big M
     torch.cuda.synchronize()
@@ -220,8 +235,10 @@ def main():
                    "weight_copies": copies, "graph": not args.no_graph},
         "roofline": roof,
         "cpu_baseline": cpu,
-        "step_breakdown_us": {"quantize": t_quant * 1e6, "gemm": t_gemm * 1e6, "step": t_step * 1e6},
-        "step_gbs": (M * K * (2 if wl.x_dtype == "bf16" else 4) + w_bytes + M * N * 4) / t_step / 1e9,
+        "step_breakdown_us": {"step (nvfp4_linear)": t_step * 1e6,
+                              "fused quantize+product, scale given": t_fused * 1e6 if skinny else None,
+                              "quantize alone": t_quant * 1e6, "gemm alone": t_gemm * 1e6},
+        "step_gbs": (x_in_bytes + w_bytes + x_q_bytes + M * N * 4) / t_step / 1e9,
         "parity": {"codes_scales_bit_exact": codes_ok, "gemm_within_1e-5": bool(y_ok), "worst_ratio": worst,
                    "rows_checked": int(len(rows)), "cols_checked": int(len(cols))},
     }

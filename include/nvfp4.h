@@ -155,7 +155,9 @@ typedef struct nvfp4_weight_desc {
     size_t colscale_offset;
 } nvfp4_weight_desc;
 
-/* Bytes of the blob for the given module row counts and K (0 if the shape is invalid). */
+/* Bytes of the blob for the given module row counts and K (0 if the shape is
+ * invalid: K not a multiple of 128, or the padded codes n_padded*K/2 above
+ * 2 GiB, since the GEMM kernels address each operand with 32-bit offsets). */
 size_t nvfp4_packed_weight_bytes(int n_modules, const int64_t* module_rows, int64_t K);
 
 /*
@@ -191,19 +193,51 @@ nvfp4_status nvfp4_unpack_weights(const nvfp4_weight_desc* w, uint8_t* codes, ui
  * FP16 and are multiplied and summed on the matrix cores in FP32; the two
  * global scales are applied once per output as fl32(acc * fl32(g_x * g_w)).
  *
- * M        : >= 0 (M == 0 enqueues nothing)
+ * M        : >= 0 (M == 0 enqueues nothing); M*K/2 <= 2 GiB, else
+ *            NVFP4_ERR_UNSUPPORTED (32-bit operand offsets)
  * a_codes  : device, canonical [M][K/2] codes of the activations (K = w->k)
  * a_scales : device, canonical [M][K/16]
  * g_x      : device, one float (the activations' global scale)
  * w        : host descriptor from nvfp4_pack_weights
  * y        : device, FP32, row m at y + m*ld_y; columns [0, w->n) are written
  * ld_y     : >= w->n
- * workspace: device, >= nvfp4_gemm_workspace_bytes(M, w) bytes (may be NULL when 0)
+ * workspace: device, >= nvfp4_gemm_workspace_bytes(M, w) bytes, 256-byte aligned
+ *            (may be NULL when that is 0).  For few tokens (1 <= M <= 16) the
+ *            product is split along K over workgroups; the workspace holds one
+ *            counter per 64 weight rows, which must be ZERO before its first use
+ *            and which every call leaves zero, and the partial tiles, which the
+ *            last workgroup of each group adds in a fixed order (so results do
+ *            not depend on scheduling).  Calls that run concurrently must not
+ *            share a workspace.
  * ------------------------------------------------------------------------- */
 size_t nvfp4_gemm_workspace_bytes(int64_t M, const nvfp4_weight_desc* w);
 nvfp4_status nvfp4_gemm(int64_t M, const uint8_t* a_codes, const uint8_t* a_scales, const float* g_x,
                         const nvfp4_weight_desc* w, float* y, int64_t ld_y,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Linear layer: quantize the activations and multiply them by a packed weight
+ * in one call (the W4A4 linear layer of the Gated DeltaNet page, section
+ * "Performance and Efficiency Gains").  Same codes, scales, g and Y bits as
+ * nvfp4_quantize followed by nvfp4_gemm on the same stream.
+ *
+ * For few tokens (1 <= M <= 16) the activations are not written out and read
+ * back between two kernels: after a small kernel that reduces max|x|, one
+ * kernel quantizes each K-slice of the activations next to the weight stream
+ * that consumes it (see nvfp4_gemm) and also stores the codes and scales.
+ *
+ * x, in_dtype, ld_x     : as for nvfp4_quantize, rows = M, K = w->k (M*K/2 <= 2 GiB)
+ * x_codes, x_scales, g_x: the activations' NVFP4 encoding (outputs; g_x is an
+ *                         input in NVFP4_G_GIVEN mode), as for nvfp4_quantize
+ * w, y, ld_y            : as for nvfp4_gemm
+ * workspace             : device, >= nvfp4_linear_workspace_bytes(M, in_dtype, w)
+ *                         bytes, 256-byte aligned, zero-filled before its first
+ *                         use (as the few-token workspace of nvfp4_gemm).
+ * ------------------------------------------------------------------------- */
+size_t nvfp4_linear_workspace_bytes(int64_t M, int in_dtype, const nvfp4_weight_desc* w);
+nvfp4_status nvfp4_linear(const void* x, int in_dtype, int64_t M, int64_t ld_x, uint8_t* x_codes,
+                          uint8_t* x_scales, float* g_x, int g_mode, const nvfp4_weight_desc* w, float* y,
+                          int64_t ld_y, void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -86,6 +86,9 @@ def _load():
         "nvfp4_unpack_weights": (c_int, [ctypes.POINTER(WeightDesc), c_vp, c_vp, c_vp, c_vp]),
         "nvfp4_gemm_workspace_bytes": (c_sz, [c_i64, ctypes.POINTER(WeightDesc)]),
         "nvfp4_gemm": (c_int, [c_i64, c_vp, c_vp, c_vp, ctypes.POINTER(WeightDesc), c_vp, c_i64, c_vp, c_sz, c_vp]),
+        "nvfp4_linear_workspace_bytes": (c_sz, [c_i64, c_int, ctypes.POINTER(WeightDesc)]),
+        "nvfp4_linear": (c_int, [c_vp, c_int, c_i64, c_i64, c_vp, c_vp, c_vp, c_int, ctypes.POINTER(WeightDesc), c_vp,
+                                 c_i64, c_vp, c_sz, c_vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -190,6 +193,24 @@ def nvfp4_gemm(M: int, a_codes, a_scales, g_x, desc: WeightDesc, y, ld_y=None, w
                            _ptr(workspace), ws_bytes, _stream(stream)))
 
 
+def nvfp4_linear_workspace_bytes(M: int, in_dtype: int, desc: WeightDesc) -> int:
+    return _lib.nvfp4_linear_workspace_bytes(M, in_dtype, ctypes.byref(desc))
+
+
+def nvfp4_linear(x, x_codes, x_scales, g_x, desc: WeightDesc, y, workspace, g_mode=NVFP4_G_COMPUTE, stream=None, *,
+                 M=None, ld_x=None, in_dtype=None, ld_y=None):
+    """Quantize x [M, K] and multiply by a packed weight in one call (workspace zero-filled before first use)."""
+    if M is None:
+        M = x.shape[0]
+        ld_x = x.stride(0) if M > 1 else x.shape[1]
+        in_dtype = NVFP4_IN_BF16 if x.dtype == torch.bfloat16 else NVFP4_IN_F32
+    if ld_y is None:
+        ld_y = y.stride(0) if y.dim() == 2 and y.shape[0] > 1 else desc.n
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(_lib.nvfp4_linear(_ptr(x), in_dtype, M, ld_x, _ptr(x_codes), _ptr(x_scales), _ptr(g_x), g_mode,
+                             ctypes.byref(desc), _ptr(y), ld_y, _ptr(workspace), ws_bytes, _stream(stream)))
+
+
 # ---------------------------------------------------------------------------
 # Conveniences (outputs allocated with torch, then the entry points above)
 # ---------------------------------------------------------------------------
@@ -254,11 +275,31 @@ class PackedWeight:
         return codes, scales, colscale
 
 
+def linear_workspace(M: int, x_dtype, w: "PackedWeight", device="cuda") -> torch.Tensor:
+    """A zero-filled workspace for nvfp4_linear (reusable by later calls on the same stream)."""
+    in_dtype = NVFP4_IN_BF16 if x_dtype == torch.bfloat16 else NVFP4_IN_F32
+    return torch.zeros((nvfp4_linear_workspace_bytes(M, in_dtype, w.desc),), dtype=torch.uint8, device=device)
+
+
+def linear(x: torch.Tensor, w: "PackedWeight", workspace=None, g=None, stream=None):
+    """Y = NVFP4(x) . W^T in one call; returns (y, codes, scales, g)."""
+    M, K = x.shape
+    codes, scales, gt = empty_quantized(M, K, x.device)
+    if g is not None:
+        gt.fill_(float(g))
+    if workspace is None:
+        workspace = linear_workspace(M, x.dtype, w, x.device)
+    y = torch.empty((M, w.n), dtype=torch.float32, device=x.device)
+    nvfp4_linear(x, codes, scales, gt, w.desc, y, workspace, NVFP4_G_GIVEN if g is not None else NVFP4_G_COMPUTE,
+                 stream)
+    return y, codes, scales, gt
+
+
 def gemm(a_codes, a_scales, g_x, w: PackedWeight, y=None, stream=None):
     M = a_codes.shape[0]
     if y is None:
         y = torch.empty((M, w.n), dtype=torch.float32, device=a_codes.device)
     ws_bytes = nvfp4_gemm_workspace_bytes(M, w.desc)
-    ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=a_codes.device) if ws_bytes else None
+    ws = torch.zeros((ws_bytes,), dtype=torch.uint8, device=a_codes.device) if ws_bytes else None
     nvfp4_gemm(M, a_codes, a_scales, g_x, w.desc, y, None, ws, stream)
     return y

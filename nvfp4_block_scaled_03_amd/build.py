@@ -19,7 +19,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libnvfp4.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.hip", "quantize.hip", "pack.hip", "gemm.hip"]
+SOURCES = ["api.hip", "quantize.hip", "pack.hip", "gemm.hip", "skinny.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950",
@@ -28,8 +28,10 @@ FLAGS = [
     "-fPIC",
     "-I", os.path.join(ROOT, "include"),
     "-I", SRC,
-    # IEEE FP32 division (the quantizer's scale decisions depend on it)
+    # IEEE FP32 division and no fused multiply-adds: the quantizer's code and
+    # scale decisions depend on one rounding per operation
     "-fhip-fp32-correctly-rounded-divide-sqrt",
+    "-ffp-contract=off",
     # no packed FP32 instructions anywhere
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall",

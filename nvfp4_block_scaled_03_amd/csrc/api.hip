@@ -81,6 +81,7 @@ bool blob_layout(int n_modules, const int64_t* rows, int64_t K, nvfp4_weight_des
     d->n = n;
     d->k = K;
     d->n_padded = round_up(n, nvfp4::kPackNAlign);
+    if (d->n_padded * K / 2 > nvfp4::kMaxCodeBytes) return false;   // kernels address codes with 32-bit offsets
     d->n_modules = n_modules;
     d->codes_offset = nvfp4::kBlobHeader;
     d->scales_offset = d->codes_offset + (size_t)(d->n_padded * K / 2);
@@ -228,16 +229,81 @@ nvfp4_status nvfp4_gemm(int64_t M, const uint8_t* a_codes, const uint8_t* a_scal
         return fail(NVFP4_ERR_INVALID_ARG, "a_codes, a_scales, g_x and y must be non-NULL");
     if (ld_y < w->n) return fail(NVFP4_ERR_SHAPE, "ld_y (%lld) < n (%lld)", (long long)ld_y, (long long)w->n);
     if (M > (int64_t(1) << 31) || ld_y > INT64_MAX / M) return fail(NVFP4_ERR_SHAPE, "M too large");
+    if (M * w->k / 2 > nvfp4::kMaxCodeBytes)
+        return fail(NVFP4_ERR_UNSUPPORTED, "activation codes above 2 GiB (M*K/2 = %lld)", (long long)(M * w->k / 2));
     if (!aligned(a_codes, 16) || !aligned(a_scales, 4) || !aligned(y, 4))
         return fail(NVFP4_ERR_UNSUPPORTED, "a_codes must be 16-byte and a_scales 4-byte aligned");
     const size_t need = nvfp4::gemm_workspace_bytes(M, *w);
-    if (need > 0 && (workspace == nullptr || workspace_bytes < need))
-        return fail(NVFP4_ERR_WORKSPACE, "gemm workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256)))
+        return fail(NVFP4_ERR_WORKSPACE, "gemm workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
+                    workspace_bytes);
     st = check_device();
     if (st != NVFP4_OK) return st;
     return launched(nvfp4::launch_gemm(M, a_codes, a_scales, g_x, *w, y, ld_y, workspace, workspace_bytes,
                                        static_cast<hipStream_t>(stream)),
                     "gemm launch");
+}
+
+size_t nvfp4_linear_workspace_bytes(int64_t M, int in_dtype, const nvfp4_weight_desc* w) {
+    if (w == nullptr || M < 0 || w->k <= 0 || w->n_padded <= 0) return 0;
+    (void)in_dtype;
+    const size_t skinny = nvfp4::skinny_applies(M, *w) ? nvfp4::skinny_workspace_bytes(*w) : 0;
+    return skinny + nvfp4_quantize_workspace_bytes(M, w->k);
+}
+
+nvfp4_status nvfp4_linear(const void* x, int in_dtype, int64_t M, int64_t ld_x, uint8_t* x_codes, uint8_t* x_scales,
+                          float* g_x, int g_mode, const nvfp4_weight_desc* w, float* y, int64_t ld_y,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+    nvfp4_status st = check_desc(w);
+    if (st != NVFP4_OK) return st;
+    const int64_t K = w->k;
+    if (in_dtype != NVFP4_IN_F32 && in_dtype != NVFP4_IN_BF16)
+        return fail(NVFP4_ERR_INVALID_ARG, "unknown input dtype %d", in_dtype);
+    if (g_mode != NVFP4_G_COMPUTE && g_mode != NVFP4_G_GIVEN)
+        return fail(NVFP4_ERR_INVALID_ARG, "unknown g mode %d", g_mode);
+    if (M < 0) return fail(NVFP4_ERR_SHAPE, "M must be >= 0 (got %lld)", (long long)M);
+    if (g_x == nullptr) return fail(NVFP4_ERR_INVALID_ARG, "g_x is NULL");
+    if (ld_x < K) return fail(NVFP4_ERR_SHAPE, "ld_x (%lld) < K (%lld)", (long long)ld_x, (long long)K);
+    if (M > 0) {
+        if (x == nullptr || x_codes == nullptr || x_scales == nullptr || y == nullptr)
+            return fail(NVFP4_ERR_INVALID_ARG, "x, x_codes, x_scales and y must be non-NULL");
+        if (ld_y < w->n) return fail(NVFP4_ERR_SHAPE, "ld_y (%lld) < n (%lld)", (long long)ld_y, (long long)w->n);
+        if (M > (int64_t(1) << 31) || ld_x > INT64_MAX / M || ld_y > INT64_MAX / M)
+            return fail(NVFP4_ERR_SHAPE, "M too large");
+        if (M * K / 2 > nvfp4::kMaxCodeBytes)
+            return fail(NVFP4_ERR_UNSUPPORTED, "activation codes above 2 GiB (M*K/2 = %lld)", (long long)(M * K / 2));
+        const int esize = in_dtype == NVFP4_IN_BF16 ? 2 : 4;
+        if (!aligned(x, 16) || (ld_x * esize) % 16 != 0)
+            return fail(NVFP4_ERR_UNSUPPORTED, "x must be 16-byte aligned with a 16-byte multiple row stride");
+        if (!aligned(x_codes, 16) || !aligned(x_scales, 4) || !aligned(y, 4))
+            return fail(NVFP4_ERR_UNSUPPORTED, "x_codes must be 16-byte and x_scales 4-byte aligned");
+    }
+    const size_t need = nvfp4_linear_workspace_bytes(M, in_dtype, w);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256)))
+        return fail(NVFP4_ERR_WORKSPACE, "linear workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
+                    workspace_bytes);
+    st = check_device();
+    if (st != NVFP4_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint8_t* wsb = static_cast<uint8_t*>(workspace);
+    const bool skinny = nvfp4::skinny_applies(M, *w);
+    float* partials = reinterpret_cast<float*>(wsb + (skinny ? nvfp4::skinny_workspace_bytes(*w) : 0));
+    const int n_partials = nvfp4::quantize_partials_count(M, K);
+    if (M == 0 || !skinny) {
+        hipError_t e = nvfp4::launch_quantize(x, in_dtype, M, K, ld_x, x_codes, x_scales, g_x, g_mode, partials,
+                                              n_partials, s);
+        if (e != hipSuccess) return fail(NVFP4_ERR_HIP, "linear quantize launch: %s", hipGetErrorString(e));
+        if (M == 0) return ok();
+        return launched(nvfp4::launch_gemm(M, x_codes, x_scales, g_x, *w, y, ld_y, nullptr, 0, s),
+                        "linear gemm launch");
+    }
+    if (g_mode == NVFP4_G_COMPUTE) {
+        hipError_t e = nvfp4::launch_amax(x, in_dtype, M, K, ld_x, partials, n_partials, s);
+        if (e != hipSuccess) return fail(NVFP4_ERR_HIP, "linear amax launch: %s", hipGetErrorString(e));
+    }
+    return launched(nvfp4::launch_skinny(M, x, in_dtype, ld_x, partials, n_partials, g_x, g_mode, x_codes, x_scales,
+                                         true, *w, y, ld_y, workspace, s),
+                    "linear launch");
 }
 
 }  // extern "C"

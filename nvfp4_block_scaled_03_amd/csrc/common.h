@@ -15,6 +15,7 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float float16v __attribute__((ext_vector_type(16)));
 typedef float float4v __attribute__((ext_vector_type(4)));
+typedef int v4i __attribute__((ext_vector_type(4)));
 
 // Largest E2M1 magnitude and largest finite E4M3 value; their product maps a
 // tensor's amax onto code 6 of a block scaled by 448.
@@ -27,7 +28,13 @@ constexpr float kGFloor = 7.8886090522101181e-31f;   // 2^-100
 constexpr int kPackRows = 16;      // rows per packed row-block
 constexpr int kPackK = 128;        // K elements per packed k-step (64 code bytes per row)
 constexpr int kPackNAlign = 256;   // n is padded to a multiple of this
+constexpr int64_t kMaxCodeBytes = int64_t(1) << 31;   // per operand: the GEMMs use 32-bit byte offsets
 constexpr size_t kBlobHeader = 256;
+
+// Skinny (few-token) products: at most 16 tokens, 4 wavefronts per workgroup
+// splitting the k-steps of one 16-row weight block.
+constexpr int kSkinnyM = 16;
+constexpr int kSkWaves = 4;
 
 // ---------------------------------------------------------------------------
 // Encodings (IEEE FP32 decisions, no fused operations).
@@ -80,10 +87,125 @@ __device__ __forceinline__ half8 decode8(uint32_t w, _Float16 s) {
 }
 
 // ---------------------------------------------------------------------------
+// Quantizer building blocks (IEEE FP32, one rounding per operation; every
+// translation unit that encodes is compiled with FP contraction off).
+// ---------------------------------------------------------------------------
+
+// 8 consecutive elements -> FP32 (bf16 widens exactly).
+__device__ __forceinline__ void load8(const uint16_t* p, float v[8]) {
+    uint4 u = *reinterpret_cast<const uint4*>(p);
+    uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(w[i] << 16);
+        v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+}
+__device__ __forceinline__ void load8(const float* p, float v[8]) {
+    float4 a = *reinterpret_cast<const float4*>(p);
+    float4 b = *reinterpret_cast<const float4*>(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+__device__ __forceinline__ float wave_max(float m) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    return m;
+}
+
+template <int kThreads>
+__device__ __forceinline__ float block_max(float m) {
+    __shared__ float red[kThreads / 64];
+    m = wave_max(m);
+    const int wid = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) red[wid] = m;
+    __syncthreads();
+    float r = red[0];
+#pragma unroll
+    for (int i = 1; i < kThreads / 64; ++i) r = fmaxf(r, red[i]);
+    __syncthreads();
+    return r;
+}
+
+// g from the tensor amax: fl32(amax/2688); 1 for an all-zero tensor; floored at 2^-100.
+__device__ __forceinline__ float global_scale_from_amax(float amax) {
+    if (amax == 0.0f) return 1.0f;
+    float g = amax / kGlobalRange;
+    return g < kGFloor ? kGFloor : g;
+}
+
+// Encode one 16-element block held in v[16].
+__device__ __forceinline__ void encode_block(const float v[16], float s_enc, uint32_t& lo, uint32_t& hi,
+                                             uint32_t& scale) {
+    float bamax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) bamax = fmaxf(bamax, __builtin_fabsf(v[i]));
+    const float t = bamax * s_enc;
+    const float u = t / kE2M1Max;
+    const uint32_t S = e4m3_rne_sat(u);
+    const float r = (S == 0u) ? 0.0f : s_enc / e4m3_to_f32(S);
+    float q[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) q[i] = v[i] * r;
+    uint32_t a = 0, b = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        a |= e2m1_pair(q[2 * i], q[2 * i + 1]) << (8 * i);
+        b |= e2m1_pair(q[8 + 2 * i], q[8 + 2 * i + 1]) << (8 * i);
+    }
+    lo = a;
+    hi = b;
+    scale = S;
+}
+
+// ---------------------------------------------------------------------------
+// Operand loads and decode for the GEMMs.
+// ---------------------------------------------------------------------------
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)(uint32_t)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 bload16(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+__device__ __forceinline__ uint32_t bload4(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
+}
+__device__ __forceinline__ uint32_t bload2(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, (int)soff, 0);
+}
+
+__device__ __forceinline__ _Float16 scale_byte(uint32_t packed, int i) {
+    return e4m3_to_f16((packed >> (8 * i)) & 0xFFu);
+}
+
+__device__ __forceinline__ uint32_t word_of(const uint4& v, int i) {
+    return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+// One k-step of the skinny product: decode the weight and activation chunks
+// (one E4M3 scale per 16-element block) and accumulate four 16x16x32 products.
+__device__ __forceinline__ void skinny_step(float4v& acc, const uint4& wv, uint32_t ws, const uint4& xv,
+                                            uint32_t xs) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const half8 a = decode8(word_of(wv, c), scale_byte(ws, c >> 1));
+        const half8 b = decode8(word_of(xv, c), scale_byte(xs, c >> 1));
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Host launchers (each returns hipSuccess or the launch error).
 // ---------------------------------------------------------------------------
 
 int quantize_partials_count(int64_t rows, int64_t K);
+// Per-workgroup partial maxima of |x| (n_partials workgroups), as the first kernel of the quantizer.
+hipError_t launch_amax(const void* x, int in_dtype, int64_t rows, int64_t K, int64_t ld_x, float* partials,
+                       int n_partials, hipStream_t stream);
 hipError_t launch_quantize(const void* x, int in_dtype, int64_t rows, int64_t K, int64_t ld_x,
                            uint8_t* codes, uint8_t* scales, float* g, int g_mode,
                            float* partials, int n_partials, hipStream_t stream);
@@ -98,5 +220,14 @@ size_t gemm_workspace_bytes(int64_t M, const nvfp4_weight_desc& d);
 hipError_t launch_gemm(int64_t M, const uint8_t* a_codes, const uint8_t* a_scales, const float* g_x,
                        const nvfp4_weight_desc& d, float* y, int64_t ld_y, void* ws, size_t ws_bytes,
                        hipStream_t stream);
+
+// Few-token products (skinny.hip).  The workspace starts with one 32-bit counter
+// per 64-row weight group, which must be zero before first use (each call
+// leaves it zero), followed by the split-K partial tiles.
+bool skinny_applies(int64_t M, const nvfp4_weight_desc& d);
+size_t skinny_workspace_bytes(const nvfp4_weight_desc& d);
+hipError_t launch_skinny(int64_t M, const void* x, int in_dtype, int64_t ld_x, const float* amax_partials,
+                         int n_partials, float* g_x, int g_mode, uint8_t* x_codes, uint8_t* x_scales, bool quantize,
+                         const nvfp4_weight_desc& d, float* y, int64_t ld_y, void* ws, hipStream_t stream);
 
 }  // namespace nvfp4

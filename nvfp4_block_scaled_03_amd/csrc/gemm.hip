@@ -23,135 +23,6 @@
 
 namespace nvfp4 {
 
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-
-__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint64_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)(uint32_t)bytes, 0x00020000);
-}
-__device__ __forceinline__ uint4 bload16(rsrc_t r, uint32_t voff, uint32_t soff) {
-    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
-}
-__device__ __forceinline__ uint32_t bload4(rsrc_t r, uint32_t voff, uint32_t soff) {
-    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
-}
-__device__ __forceinline__ uint32_t bload2(rsrc_t r, uint32_t voff, uint32_t soff) {
-    return (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, (int)soff, 0);
-}
-
-__device__ __forceinline__ _Float16 scale_byte(uint32_t packed, int i) {
-    return e4m3_to_f16((packed >> (8 * i)) & 0xFFu);
-}
-
-__device__ __forceinline__ uint32_t word_of(const uint4& v, int i) {
-    return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
-}
-
-// ---------------------------------------------------------------------------
-// Skinny GEMM (M <= 16), bound by the weight stream from HBM.  One workgroup per
-// 16 weight rows; its 4 wavefronts split the k-steps (wave w takes k-steps
-// w, w+4, ...) and reduce through LDS.  Each wavefront issues every load of a
-// pass (16 B of codes and 2 B of scales per lane for the weights and for the
-// activations) before it decodes anything, so the whole weight stream of the
-// grid is in flight at once.  16x16x32 FP16 instructions with the weight rows
-// as the A operand and the tokens as B.
-// ---------------------------------------------------------------------------
-constexpr int kSkinnyM = 16;
-constexpr int kSkWaves = 4;
-constexpr int kSkMaxKs = 12;
-
-// One k-step of the skinny product: decode the weight and activation chunks
-// (one E4M3 scale per 16-element block) and accumulate four 16x16x32 products.
-__device__ __forceinline__ void skinny_step(float4v& acc, const uint4& wv, uint32_t ws, const uint4& xv,
-                                            uint32_t xs) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const half8 a = decode8(word_of(wv, c), scale_byte(ws, c >> 1));
-        const half8 b = decode8(word_of(xv, c), scale_byte(xs, c >> 1));
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
-    }
-}
-
-// NKS > 0: every wavefront owns exactly NKS k-steps (K = 4*NKS*128); all loads
-// are issued up front and each k-step is consumed as soon as its own loads have
-// landed.  NKS == 0: any K, in passes of up to kSkMaxKs k-steps per wavefront.
-template <int NKS>
-__global__ __launch_bounds__(256) void gemm_skinny_kernel(int M, const uint8_t* __restrict__ a_codes,
-                                                          const uint8_t* __restrict__ a_scales,
-                                                          const float* __restrict__ g_x,
-                                                          const uint8_t* __restrict__ w_codes,
-                                                          const uint8_t* __restrict__ w_scales,
-                                                          const float* __restrict__ colscale, int64_t N,
-                                                          int64_t n_pad, int64_t K, float* __restrict__ y,
-                                                          int64_t ld_y) {
-    const int rb = blockIdx.x;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int KS = (int)(K / kPackK);
-    const int r16 = lane & 15, kg = lane >> 4;
-
-    const rsrc_t rwc = make_rsrc(w_codes, (uint64_t)n_pad * K / 2);
-    const rsrc_t rws = make_rsrc(w_scales, (uint64_t)n_pad * K / 16);
-    const rsrc_t rxc = make_rsrc(a_codes, (uint64_t)M * K / 2);     // tokens >= M read as zero
-    const rsrc_t rxs = make_rsrc(a_scales, (uint64_t)M * K / 16);
-    const uint32_t wc_off = (uint32_t)rb * KS * 1024 + kg * 256 + r16 * 16;
-    const uint32_t ws_off = (uint32_t)rb * KS * 128 + r16 * 8 + kg * 2;
-    const uint32_t xc_off = (uint32_t)(r16 * (K / 2)) + kg * 16;
-    const uint32_t xs_off = (uint32_t)(r16 * (K / 16)) + kg * 2;
-
-    float4v acc = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (NKS > 0) {
-        uint4 wv[NKS], xv[NKS];
-        uint32_t ws[NKS], xs[NKS];
-#pragma unroll
-        for (int j = 0; j < NKS; ++j) {   // loads land in issue order: interleave so k-step j is usable early
-            const uint32_t ks = wave + kSkWaves * j;
-            wv[j] = bload16(rwc, wc_off, ks * 1024);
-            ws[j] = bload2(rws, ws_off, ks * 128);
-            xv[j] = bload16(rxc, xc_off, ks * 64);
-            xs[j] = bload2(rxs, xs_off, ks * 8);
-        }
-        // keep every load ahead of the math: the scheduler would otherwise sink
-        // loads next to their uses and leave only a few in flight
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int j = 0; j < NKS; ++j) skinny_step(acc, wv[j], ws[j], xv[j], xs[j]);
-    } else {
-        for (int base = wave; base < KS; base += kSkWaves * kSkMaxKs) {
-            uint4 wv[kSkMaxKs], xv[kSkMaxKs];
-            uint32_t ws[kSkMaxKs], xs[kSkMaxKs];
-#pragma unroll
-            for (int j = 0; j < kSkMaxKs; ++j) {
-                const int ks = base + kSkWaves * j;
-                if (ks < KS) {
-                    wv[j] = bload16(rwc, wc_off, (uint32_t)ks * 1024);
-                    ws[j] = bload2(rws, ws_off, (uint32_t)ks * 128);
-                    xv[j] = bload16(rxc, xc_off, (uint32_t)ks * 64);
-                    xs[j] = bload2(rxs, xs_off, (uint32_t)ks * 8);
-                }
-            }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int j = 0; j < kSkMaxKs; ++j)
-                if (base + kSkWaves * j < KS) skinny_step(acc, wv[j], ws[j], xv[j], xs[j]);
-        }
-    }
-
-    __shared__ float red[kSkWaves - 1][64][4];
-    if (wave > 0) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) red[wave - 1][lane][r] = acc[r];
-    }
-    __syncthreads();
-    if (wave == 0) {
-        const float gx = g_x[0];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float s = ((acc[r] + red[0][lane][r]) + red[1][lane][r]) + red[2][lane][r];
-            const int64_t n = (int64_t)rb * 16 + (lane >> 4) * 4 + r;   // A row -> weight row
-            if (r16 < M && n < N) y[(int64_t)r16 * ld_y + n] = s * (gx * colscale[n]);
-        }
-    }
-}
-
 // ---------------------------------------------------------------------------
 // Tiled GEMM: a workgroup of 2x2 wavefronts computes a (2*TM*32) x (2*TN*32)
 // output tile; each wavefront a TM x TN grid of 32x32x16 FP16 instructions.
@@ -372,31 +243,20 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(int64_t M, const uint8_t
     }
 }
 
-size_t gemm_workspace_bytes(int64_t, const nvfp4_weight_desc&) { return 0; }
+size_t gemm_workspace_bytes(int64_t M, const nvfp4_weight_desc& d) {
+    return skinny_applies(M, d) ? skinny_workspace_bytes(d) : 0;
+}
 
 hipError_t launch_gemm(int64_t M, const uint8_t* a_codes, const uint8_t* a_scales, const float* g_x,
-                       const nvfp4_weight_desc& d, float* y, int64_t ld_y, void*, size_t, hipStream_t stream) {
+                       const nvfp4_weight_desc& d, float* y, int64_t ld_y, void* ws, size_t, hipStream_t stream) {
     const uint8_t* blob = static_cast<const uint8_t*>(d.blob);
     const uint8_t* wc = blob + d.codes_offset;
     const uint8_t* wsc = blob + d.scales_offset;
     const float* cs = reinterpret_cast<const float*>(blob + d.colscale_offset);
-    if (M <= kSkinnyM) {
-        const int64_t KS = d.k / kPackK;
-        const dim3 grid((unsigned)(d.n_padded / 16)), block(256);
-        const int args_M = (int)M;
-#define NVFP4_SKINNY(NKS) hipLaunchKernelGGL((gemm_skinny_kernel<NKS>), grid, block, 0, stream, args_M, a_codes, \
-                                             a_scales, g_x, wc, wsc, cs, d.n, d.n_padded, d.k, y, ld_y)
-        switch (KS % kSkWaves == 0 ? KS / kSkWaves : 0) {
-            case 1: NVFP4_SKINNY(1); break;
-            case 2: NVFP4_SKINNY(2); break;
-            case 4: NVFP4_SKINNY(4); break;
-            case 8: NVFP4_SKINNY(8); break;
-            case 10: NVFP4_SKINNY(10); break;
-            case 12: NVFP4_SKINNY(12); break;
-            case 16: NVFP4_SKINNY(16); break;
-            default: NVFP4_SKINNY(0); break;
-        }
-#undef NVFP4_SKINNY
+    if (skinny_applies(M, d)) {
+        return launch_skinny(M, nullptr, NVFP4_IN_BF16, 0, nullptr, 0, const_cast<float*>(g_x), NVFP4_G_GIVEN,
+                             const_cast<uint8_t*>(a_codes), const_cast<uint8_t*>(a_scales), false, d, y, ld_y, ws,
+                             stream);
     } else if (M <= 128) {
         const int tiles_m = (int)((M + 127) / 128), tiles_n = (int)(d.n_padded / 128);
         hipLaunchKernelGGL((gemm_tile_kernel<2, 2>), dim3(tiles_m * tiles_n), dim3(256), 0, stream, M, a_codes,

@@ -22,43 +22,6 @@ namespace nvfp4 {
 constexpr int kQThreads = 256;
 constexpr int kMaxPartials = 1024;
 
-// 8 consecutive elements -> FP32 (bf16 widens exactly).
-__device__ __forceinline__ void load8(const uint16_t* p, float v[8]) {
-    uint4 u = *reinterpret_cast<const uint4*>(p);
-    uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        v[2 * i] = __uint_as_float(w[i] << 16);
-        v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-    }
-}
-__device__ __forceinline__ void load8(const float* p, float v[8]) {
-    float4 a = *reinterpret_cast<const float4*>(p);
-    float4 b = *reinterpret_cast<const float4*>(p + 4);
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-}
-
-__device__ __forceinline__ float wave_max(float m) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-    return m;
-}
-
-template <int kThreads>
-__device__ __forceinline__ float block_max(float m) {
-    __shared__ float red[kThreads / 64];
-    m = wave_max(m);
-    const int wid = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) red[wid] = m;
-    __syncthreads();
-    float r = red[0];
-#pragma unroll
-    for (int i = 1; i < kThreads / 64; ++i) r = fmaxf(r, red[i]);
-    __syncthreads();
-    return r;
-}
-
 // Segments of a row: each thread reads kSegVec vectors of 8 elements.
 constexpr int kSegVec = 4;
 constexpr int64_t kSegElems = (int64_t)kQThreads * 8 * kSegVec;
@@ -88,37 +51,6 @@ __global__ __launch_bounds__(kQThreads) void amax_partials_kernel(const T* __res
     }
     m = block_max<kQThreads>(m);
     if (threadIdx.x == 0) partials[blockIdx.x] = m;
-}
-
-// g from the tensor amax: fl32(amax/2688); 1 for an all-zero tensor; floored at 2^-100.
-__device__ __forceinline__ float global_scale_from_amax(float amax) {
-    if (amax == 0.0f) return 1.0f;
-    float g = amax / kGlobalRange;
-    return g < kGFloor ? kGFloor : g;
-}
-
-// Encode one 16-element block held in v[16].
-__device__ __forceinline__ void encode_block(const float v[16], float s_enc, uint32_t& lo, uint32_t& hi,
-                                             uint32_t& scale) {
-    float bamax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) bamax = fmaxf(bamax, __builtin_fabsf(v[i]));
-    const float t = bamax * s_enc;
-    const float u = t / kE2M1Max;
-    const uint32_t S = e4m3_rne_sat(u);
-    const float r = (S == 0u) ? 0.0f : s_enc / e4m3_to_f32(S);
-    float q[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) q[i] = v[i] * r;
-    uint32_t a = 0, b = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        a |= e2m1_pair(q[2 * i], q[2 * i + 1]) << (8 * i);
-        b |= e2m1_pair(q[8 + 2 * i], q[8 + 2 * i + 1]) << (8 * i);
-    }
-    lo = a;
-    hi = b;
-    scale = S;
 }
 
 template <typename T>
@@ -178,6 +110,17 @@ static int encode_grid(int64_t rows, int64_t K) {
     const int64_t cap = 256 * 16;  // ~16 workgroups per CU, the rest by grid stride
     if (wg > cap) wg = cap;
     return (int)(wg < 1 ? 1 : wg);
+}
+
+hipError_t launch_amax(const void* x, int in_dtype, int64_t rows, int64_t K, int64_t ld_x, float* partials,
+                       int n_partials, hipStream_t stream) {
+    if (in_dtype == NVFP4_IN_BF16)
+        hipLaunchKernelGGL(amax_partials_kernel<uint16_t>, dim3(n_partials), dim3(kQThreads), 0, stream,
+                           static_cast<const uint16_t*>(x), rows, K, ld_x, partials);
+    else
+        hipLaunchKernelGGL(amax_partials_kernel<float>, dim3(n_partials), dim3(kQThreads), 0, stream,
+                           static_cast<const float*>(x), rows, K, ld_x, partials);
+    return hipGetLastError();
 }
 
 hipError_t launch_quantize(const void* x, int in_dtype, int64_t rows, int64_t K, int64_t ld_x,

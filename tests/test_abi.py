@@ -211,3 +211,29 @@ def test_gemm_valid_stops_at_device_check_without_gpu():
     if not _no_gpu():
         pytest.skip("a GPU is visible; this host-only check would launch on fake pointers")
     assert g_() == nv.NVFP4_ERR_NO_DEVICE
+
+
+def test_linear_validation():
+    d = make_desc(rows=(5120,), K=5120)
+    need = nv.lib.nvfp4_linear_workspace_bytes(16, nv.NVFP4_IN_BF16, ctypes.byref(d))
+    assert need >= 4 * (d.n_padded // 64) + (d.n_padded // 64) * 256 * 16    # counters + one partial tile per group
+
+    def call(**kw):
+        a = dict(x=FAKE, dt=nv.NVFP4_IN_BF16, M=16, ld_x=5120, c=FAKE, s=FAKE, g=FAKE, mode=0, d=d, y=FAKE,
+                 ld_y=5120, ws=FAKE, wsb=need)
+        a.update(kw)
+        return nv.lib.nvfp4_linear(a["x"], a["dt"], a["M"], a["ld_x"], a["c"], a["s"], a["g"], a["mode"],
+                                   ctypes.byref(a["d"]) if a["d"] is not None else None, a["y"], a["ld_y"],
+                                   a["ws"], a["wsb"], None)
+    assert call(dt=5) == nv.NVFP4_ERR_INVALID_ARG
+    assert call(mode=9) == nv.NVFP4_ERR_INVALID_ARG
+    assert call(M=-1) == nv.NVFP4_ERR_SHAPE
+    assert call(ld_x=100) == nv.NVFP4_ERR_SHAPE
+    assert call(ld_y=100) == nv.NVFP4_ERR_SHAPE
+    assert call(y=None) == nv.NVFP4_ERR_INVALID_ARG
+    assert call(x=FAKE + 8) == nv.NVFP4_ERR_UNSUPPORTED
+    assert call(ws=None) == nv.NVFP4_ERR_WORKSPACE
+    assert call(wsb=need - 1) == nv.NVFP4_ERR_WORKSPACE
+    assert call(d=None) == nv.NVFP4_ERR_INVALID_ARG
+    if _no_gpu():
+        assert call() == nv.NVFP4_ERR_NO_DEVICE

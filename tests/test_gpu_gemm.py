@@ -192,11 +192,12 @@ def test_graph_replays_match_eager(name, M):
     pw = nv.PackedWeight(mods, wl.K)
     codes, scales, g = nv.empty_quantized(wl.M, wl.K)
     ws = torch.empty((max(nv.nvfp4_quantize_workspace_bytes(wl.M, wl.K), 256),), dtype=torch.uint8, device=DEV)
+    gws = torch.zeros((max(nv.nvfp4_gemm_workspace_bytes(wl.M, pw.desc), 256),), dtype=torch.uint8, device=DEV)
     y = torch.empty((wl.M, wl.N), dtype=torch.float32, device=DEV)
 
     def step():
         nv.nvfp4_quantize(xd, codes, scales, g, nv.NVFP4_G_COMPUTE, ws)
-        nv.nvfp4_gemm(wl.M, codes, scales, g, pw.desc, y, wl.N)
+        nv.nvfp4_gemm(wl.M, codes, scales, g, pw.desc, y, wl.N, gws)
 
     step()
     torch.cuda.synchronize()
