@@ -45,7 +45,37 @@ def parse():
     p.add_argument("--config", default="decode", choices=sorted(CONFIG_NAMES))
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
+    p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                   help="only run a plain device-to-device copy of MIB MiB 20 times (calibrates HBM byte counters)")
     return p.parse_args()
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the dominant kernel, from the committed counter runs (profiles/traffic.json),
+    or None when there are none for this workload or the kernel's sources have changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(workload)
+    if rec is None:
+        return None
+    h = hashlib.sha256()
+    for f in rec["sources"]:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return rec["traffic_bytes"] if h.hexdigest() == rec["sources_sha256"] else None
+
+
+def copy_probe(mib):
+    """A copy of known size: the HBM byte counters of its kernel scale those of the product kernels."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(20):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "launches": 20}), flush=True)
 
 
 def log(msg):
@@ -58,6 +88,10 @@ def main():
         print("bench.py measures one GPU: this build has no multi-GPU path (collectives are not part of it); "
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
 
     import torch
     import nvfp4_block_scaled_03_amd as nv
@@ -186,7 +220,7 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": flops / t_kern / 1e12, "peak": F16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(CONFIG_NAMES[name])
     roof["kernel"] = kern
     roof["kernel_us"] = t_kern * 1e6
     roof["algorithmic_bytes_per_launch"] = kern_bytes
