@@ -286,23 +286,23 @@ nvfp4_status nvfp4_linear(const void* x, int in_dtype, int64_t M, int64_t ld_x, 
     if (st != NVFP4_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     uint8_t* wsb = static_cast<uint8_t*>(workspace);
+    // the fused few-token kernel addresses the activations with 32-bit offsets
+    const int64_t esize = in_dtype == NVFP4_IN_BF16 ? 2 : 4;
     const bool skinny = nvfp4::skinny_applies(M, *w);
+    const bool fused = skinny && M * ld_x * esize <= INT32_MAX;
     float* partials = reinterpret_cast<float*>(wsb + (skinny ? nvfp4::skinny_workspace_bytes(*w) : 0));
     const int n_partials = nvfp4::quantize_partials_count(M, K);
-    if (M == 0 || !skinny) {
+    if (M == 0 || !fused) {
         hipError_t e = nvfp4::launch_quantize(x, in_dtype, M, K, ld_x, x_codes, x_scales, g_x, g_mode, partials,
                                               n_partials, s);
         if (e != hipSuccess) return fail(NVFP4_ERR_HIP, "linear quantize launch: %s", hipGetErrorString(e));
         if (M == 0) return ok();
-        return launched(nvfp4::launch_gemm(M, x_codes, x_scales, g_x, *w, y, ld_y, nullptr, 0, s),
+        return launched(nvfp4::launch_gemm(M, x_codes, x_scales, g_x, *w, y, ld_y, skinny ? workspace : nullptr,
+                                           skinny ? nvfp4::skinny_workspace_bytes(*w) : 0, s),
                         "linear gemm launch");
     }
-    if (g_mode == NVFP4_G_COMPUTE) {
-        hipError_t e = nvfp4::launch_amax(x, in_dtype, M, K, ld_x, partials, n_partials, s);
-        if (e != hipSuccess) return fail(NVFP4_ERR_HIP, "linear amax launch: %s", hipGetErrorString(e));
-    }
-    return launched(nvfp4::launch_skinny(M, x, in_dtype, ld_x, partials, n_partials, g_x, g_mode, x_codes, x_scales,
-                                         true, *w, y, ld_y, workspace, s),
+    return launched(nvfp4::launch_skinny(M, x, in_dtype, ld_x, g_x, g_mode, x_codes, x_scales, true, *w, y, ld_y,
+                                         workspace, s),
                     "linear launch");
 }
 

@@ -31,10 +31,9 @@ constexpr int kPackNAlign = 256;   // n is padded to a multiple of this
 constexpr int64_t kMaxCodeBytes = int64_t(1) << 31;   // per operand: the GEMMs use 32-bit byte offsets
 constexpr size_t kBlobHeader = 256;
 
-// Skinny (few-token) products: at most 16 tokens, 4 wavefronts per workgroup
-// splitting the k-steps of one 16-row weight block.
+// Few-token products: at most 16 tokens (one 16-column matrix-instruction tile).
 constexpr int kSkinnyM = 16;
-constexpr int kSkWaves = 4;
+constexpr int kMaxAmaxPartials = 1024;   // upper bound of quantize_partials_count
 
 // ---------------------------------------------------------------------------
 // Encodings (IEEE FP32 decisions, no fused operations).
@@ -108,6 +107,20 @@ __device__ __forceinline__ void load8(const float* p, float v[8]) {
     v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
+// One 16-element block of raw input, as loaded (two or four 16-byte vectors).
+template <typename T> struct RawBlock;
+template <> struct RawBlock<uint16_t> { uint4 v[2]; };
+template <> struct RawBlock<float> { uint4 v[4]; };
+
+__device__ __forceinline__ void widen(const RawBlock<uint16_t>& r, float v[16]) {
+    load8(reinterpret_cast<const uint16_t*>(&r.v[0]), v);
+    load8(reinterpret_cast<const uint16_t*>(&r.v[1]), v + 8);
+}
+__device__ __forceinline__ void widen(const RawBlock<float>& r, float v[16]) {
+    load8(reinterpret_cast<const float*>(&r.v[0]), v);
+    load8(reinterpret_cast<const float*>(&r.v[2]), v + 8);
+}
+
 __device__ __forceinline__ float wave_max(float m) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
@@ -165,6 +178,10 @@ __device__ __forceinline__ void encode_block(const float v[16], float s_enc, uin
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
+// A buffer offset past every record count used here (they are all <= INT32_MAX):
+// a load from it returns zero, with no branch around the load.
+constexpr uint32_t kOutOfBounds = 0xFFFFFF00u;
+
 __device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint64_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)(uint32_t)bytes, 0x00020000);
 }
@@ -173,6 +190,12 @@ __device__ __forceinline__ uint4 bload16(rsrc_t r, uint32_t voff, uint32_t soff)
 }
 __device__ __forceinline__ uint32_t bload4(rsrc_t r, uint32_t voff, uint32_t soff) {
     return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
+}
+__device__ __forceinline__ uint2 bload8(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0));
+}
+__device__ __forceinline__ uint32_t bload1(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return (uint32_t)(uint8_t)__builtin_amdgcn_raw_buffer_load_b8(r, (int)voff, (int)soff, 0);
 }
 __device__ __forceinline__ uint32_t bload2(rsrc_t r, uint32_t voff, uint32_t soff) {
     return (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, (int)soff, 0);
@@ -226,8 +249,8 @@ hipError_t launch_gemm(int64_t M, const uint8_t* a_codes, const uint8_t* a_scale
 // leaves it zero), followed by the split-K partial tiles.
 bool skinny_applies(int64_t M, const nvfp4_weight_desc& d);
 size_t skinny_workspace_bytes(const nvfp4_weight_desc& d);
-hipError_t launch_skinny(int64_t M, const void* x, int in_dtype, int64_t ld_x, const float* amax_partials,
-                         int n_partials, float* g_x, int g_mode, uint8_t* x_codes, uint8_t* x_scales, bool quantize,
-                         const nvfp4_weight_desc& d, float* y, int64_t ld_y, void* ws, hipStream_t stream);
+hipError_t launch_skinny(int64_t M, const void* x, int in_dtype, int64_t ld_x, float* g_x, int g_mode,
+                         uint8_t* x_codes, uint8_t* x_scales, bool quantize, const nvfp4_weight_desc& d, float* y,
+                         int64_t ld_y, void* ws, hipStream_t stream);
 
 }  // namespace nvfp4

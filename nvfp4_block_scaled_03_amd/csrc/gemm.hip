@@ -254,7 +254,7 @@ hipError_t launch_gemm(int64_t M, const uint8_t* a_codes, const uint8_t* a_scale
     const uint8_t* wsc = blob + d.scales_offset;
     const float* cs = reinterpret_cast<const float*>(blob + d.colscale_offset);
     if (skinny_applies(M, d)) {
-        return launch_skinny(M, nullptr, NVFP4_IN_BF16, 0, nullptr, 0, const_cast<float*>(g_x), NVFP4_G_GIVEN,
+        return launch_skinny(M, nullptr, NVFP4_IN_BF16, 0, const_cast<float*>(g_x), NVFP4_G_GIVEN,
                              const_cast<uint8_t*>(a_codes), const_cast<uint8_t*>(a_scales), false, d, y, ld_y, ws,
                              stream);
     } else if (M <= 128) {

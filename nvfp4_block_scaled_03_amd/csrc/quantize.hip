@@ -20,7 +20,7 @@
 namespace nvfp4 {
 
 constexpr int kQThreads = 256;
-constexpr int kMaxPartials = 1024;
+constexpr int kMaxPartials = kMaxAmaxPartials;
 
 // Segments of a row: each thread reads kSegVec vectors of 8 elements.
 constexpr int kSegVec = 4;
@@ -97,6 +97,93 @@ __global__ __launch_bounds__(kQThreads) void encode_kernel(const T* __restrict__
 
 __global__ void write_unit_g_kernel(float* g) { g[0] = 1.0f; }
 
+// Small tensors (at most kSmallThreads * P blocks) in one launch: every one of
+// the P workgroups loads the whole tensor (thread t holds blocks t, t + 1024,
+// ...), reduces max|x| itself, so no workgroup depends on another, and then
+// encodes its own share: workgroup w encodes the w-th block of every thread.
+constexpr int kSmallThreads = 1024;
+
+template <typename T, int P>
+__global__ __launch_bounds__(kSmallThreads) void quantize_small_kernel(const T* __restrict__ x, int64_t rows,
+                                                                       int64_t K, int64_t ld,
+                                                                       uint8_t* __restrict__ codes,
+                                                                       uint8_t* __restrict__ scales,
+                                                                       float* __restrict__ g_io, int g_given) {
+    const int bpr = (int)(K / 16);
+    const int nblk = (int)rows * bpr;
+    const rsrc_t rx = make_rsrc(x, (uint64_t)rows * ld * sizeof(T));
+    RawBlock<T> raw[P];
+#pragma unroll
+    for (int i = 0; i < P; ++i) {   // branch-free: blocks past the tensor read as zero
+        const int b = threadIdx.x + i * kSmallThreads;
+        const int r = b / bpr, kb = b - r * bpr;
+        const uint32_t off = b < nblk ? (uint32_t)(((int64_t)r * ld + (int64_t)kb * 16) * (int64_t)sizeof(T))
+                                      : kOutOfBounds;
+#pragma unroll
+        for (int q = 0; q < (int)(sizeof(RawBlock<T>) / 16); ++q) raw[i].v[q] = bload16(rx, off, (uint32_t)q * 16);
+    }
+    float g;
+    if (g_given) {
+        g = g_io[0];
+    } else {
+        float m = 0.0f;
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+            float v[16];
+            widen(raw[i], v);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) m = fmaxf(m, __builtin_fabsf(v[e]));
+        }
+        g = global_scale_from_amax(block_max<kSmallThreads>(m));
+        if (blockIdx.x == 0 && threadIdx.x == 0) g_io[0] = g;
+    }
+    RawBlock<T> mine = raw[0];
+#pragma unroll
+    for (int i = 1; i < P; ++i)
+        if ((int)blockIdx.x == i) mine = raw[i];
+    const int b = threadIdx.x + (int)blockIdx.x * kSmallThreads;
+    if (b < nblk) {
+        float v[16];
+        widen(mine, v);
+        uint32_t lo, hi, S;
+        encode_block(v, 1.0f / g, lo, hi, S);
+        *reinterpret_cast<uint2*>(codes + (int64_t)b * 8) = make_uint2(lo, hi);
+        scales[b] = (uint8_t)S;
+    }
+}
+
+// Blocks per thread of the one-launch path for this tensor, or 0 when it does not apply.
+static int small_blocks_per_thread(int64_t rows, int64_t K, int64_t ld, int in_dtype) {
+    const int esize = in_dtype == NVFP4_IN_BF16 ? 2 : 4;
+    const int64_t nblk = rows * (K / 16);
+    const int max_p = in_dtype == NVFP4_IN_BF16 ? 8 : 4;   // raw registers: 8 or 16 per block
+    if (rows < 1 || nblk > (int64_t)kSmallThreads * max_p || rows * ld * esize > INT32_MAX) return 0;
+    return (int)((nblk + kSmallThreads - 1) / kSmallThreads);
+}
+
+template <typename T>
+static hipError_t launch_small(int p, const T* x, int64_t rows, int64_t K, int64_t ld, uint8_t* codes,
+                               uint8_t* scales, float* g, int given, hipStream_t stream) {
+#define NVFP4_QS(P)                                                                                             \
+    case P:                                                                                                     \
+        hipLaunchKernelGGL((quantize_small_kernel<T, P>), dim3(P), dim3(kSmallThreads), 0, stream, x, rows, K, \
+                           ld, codes, scales, g, given);                                                        \
+        break;
+    switch (p) {
+        NVFP4_QS(1)
+        NVFP4_QS(2)
+        NVFP4_QS(3)
+        NVFP4_QS(4)
+        NVFP4_QS(5)
+        NVFP4_QS(6)
+        NVFP4_QS(7)
+        NVFP4_QS(8)
+        default: return hipErrorInvalidValue;
+    }
+#undef NVFP4_QS
+    return hipGetLastError();
+}
+
 int quantize_partials_count(int64_t rows, int64_t K) {
     const int64_t elems = rows * K;
     int64_t segs = (elems + kSegElems - 1) / kSegElems;
@@ -130,6 +217,15 @@ hipError_t launch_quantize(const void* x, int in_dtype, int64_t rows, int64_t K,
     if (rows == 0) {
         if (!given) hipLaunchKernelGGL(write_unit_g_kernel, dim3(1), dim3(1), 0, stream, g);
         return hipGetLastError();
+    }
+    const int p = small_blocks_per_thread(rows, K, ld_x, in_dtype);
+    if (p > 0) {
+        if (in_dtype == NVFP4_IN_BF16)
+            return launch_small<uint16_t>(p, static_cast<const uint16_t*>(x), rows, K, ld_x, codes, scales, g, given,
+                                          stream);
+        if (p <= 4)
+            return launch_small<float>(p, static_cast<const float*>(x), rows, K, ld_x, codes, scales, g, given,
+                                       stream);
     }
     const int grid = encode_grid(rows, K);
     if (in_dtype == NVFP4_IN_BF16) {
