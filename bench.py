@@ -127,7 +127,7 @@ def main():
     codes, scales, g = nv.empty_quantized(M, K, dev)
     ws = torch.empty((max(nv.nvfp4_quantize_workspace_bytes(M, K), 256),), dtype=torch.uint8, device=dev)
     lin_ws = nv.linear_workspace(M, xdt, packed, dev)       # zero-filled once, reused by every step
-    skinny = M <= 16     # few-token path: amax kernel + one fused quantize-and-product kernel
+    skinny = M <= 16     # few-token path: one kernel (amax, quantize and product)
     y = torch.empty((M, N), dtype=torch.float32, device=dev)
     gemm_ws = torch.zeros((max(nv.nvfp4_gemm_workspace_bytes(M, packed.desc), 256),), dtype=torch.uint8,
                           device=dev)       # split-K counters start at zero; every call leaves them so
@@ -142,10 +142,6 @@ def main():
                 nv.nvfp4_quantize(w, c, s, gg, nv.NVFP4_G_COMPUTE, wsb)
         nv.nvfp4_linear(x, codes, scales, g, weights[i % copies].desc, y, lin_ws, M=M, ld_x=K, in_dtype=in_dtype,
                         ld_y=N)
-
-    def fused_only(i):   # the fused kernel alone: the global scale handed in (that of the last step)
-        nv.nvfp4_linear(x, codes, scales, g, weights[i % copies].desc, y, lin_ws, g_mode=nv.NVFP4_G_GIVEN, M=M,
-                        ld_x=K, in_dtype=in_dtype, ld_y=N)
 
     def gemm_only(i):
         nv.nvfp4_gemm(M, codes, scales, g, weights[i % copies].desc, y, N, gemm_ws)
@@ -199,7 +195,6 @@ def main():
     # dominant kernel and the quantizer alone, same launch configuration, events on the launch stream
     k_steps = max(steps, rot)
     t_gemm = timed(gemm_only, k_steps, min(warmup, k_steps)) / k_steps
-    t_fused = timed(fused_only, k_steps, min(warmup, k_steps)) / k_steps if skinny else None
     t_quant = timed(quant_only, k_steps, min(warmup, k_steps)) / k_steps
 
     flops = 2.0 * M * N * K
@@ -208,9 +203,9 @@ def main():
     x_q_bytes = M * K * 9 // 16
     x_in_bytes = M * K * (2 if wl.x_dtype == "bf16" else 4)
     if skinny:
-        # the fused kernel quantizes the activations and takes the product: its bytes are the
-        # weights (codes + scales), the activations in, their codes and scales out, and Y
-        kern, t_kern = "skinny_kernel (quantize + product)", t_fused
+        # the step is one launch of the few-token kernel (amax, quantize and product): its bytes
+        # are the weights (codes + scales), the activations in, their codes and scales out, and Y
+        kern, t_kern = "skinny_kernel (amax + quantize + product, one launch)", t_step
         kern_bytes = w_bytes + x_in_bytes + x_q_bytes + M * N * 4
     else:
         kern, t_kern = "gemm_tile_kernel", t_gemm
@@ -269,8 +264,7 @@ def main():
                    "weight_copies": copies, "graph": not args.no_graph},
         "roofline": roof,
         "cpu_baseline": cpu,
-        "step_breakdown_us": {"step (nvfp4_linear)": t_step * 1e6,
-                              "fused quantize+product, scale given": t_fused * 1e6 if skinny else None,
+        "step_breakdown_us": {"step (nvfp4_linear)": t_step * 1e6, "launches_per_step": 1 if skinny else 3,
                               "quantize alone": t_quant * 1e6, "gemm alone": t_gemm * 1e6},
         "step_gbs": (x_in_bytes + w_bytes + x_q_bytes + M * N * 4) / t_step / 1e9,
         "parity": {"codes_scales_bit_exact": codes_ok, "gemm_within_1e-5": bool(y_ok), "worst_ratio": worst,

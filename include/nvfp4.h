@@ -203,11 +203,12 @@ nvfp4_status nvfp4_unpack_weights(const nvfp4_weight_desc* w, uint8_t* codes, ui
  * ld_y     : >= w->n
  * workspace: device, >= nvfp4_gemm_workspace_bytes(M, w) bytes, 256-byte aligned
  *            (may be NULL when that is 0).  For few tokens (1 <= M <= 16) the
- *            product is split along K over workgroups; the workspace holds one
- *            counter per 64 weight rows, which must be ZERO before its first use
- *            and which every call leaves zero, and the partial tiles, which the
- *            last workgroup of each group adds in a fixed order (so results do
- *            not depend on scheduling).  Calls that run concurrently must not
+ *            product is split along K over workgroups: the workspace holds a
+ *            ticket counter and a few exchange words per group of weight rows
+ *            and one partial tile per workgroup.  It must be ZERO before its
+ *            first use, and every call leaves it zero; the last workgroup of a
+ *            group to start adds the partials in a fixed order (results do not
+ *            depend on scheduling).  Calls that may run concurrently must not
  *            share a workspace.
  * ------------------------------------------------------------------------- */
 size_t nvfp4_gemm_workspace_bytes(int64_t M, const nvfp4_weight_desc* w);
@@ -221,10 +222,14 @@ nvfp4_status nvfp4_gemm(int64_t M, const uint8_t* a_codes, const uint8_t* a_scal
  * "Performance and Efficiency Gains").  Same codes, scales, g and Y bits as
  * nvfp4_quantize followed by nvfp4_gemm on the same stream.
  *
- * For few tokens (1 <= M <= 16) the activations are not written out and read
- * back between two kernels: after a small kernel that reduces max|x|, one
- * kernel quantizes each K-slice of the activations next to the weight stream
- * that consumes it (see nvfp4_gemm) and also stores the codes and scales.
+ * For few tokens (1 <= M <= 16) the whole call is one kernel: the workgroups
+ * that share a K-slice of the weight stream quantize that slice of the
+ * activations next to it, after exchanging per-slice max|x| with the other
+ * workgroups of their row group (no second pass over the activations and no
+ * extra launch).  The exchange waits a bounded number of polls for each peer
+ * and otherwise reduces the missing slices itself, so it never depends on
+ * another workgroup being resident; the environment variable
+ * NVFP4_AMAX_POLLS overrides the bound (0 forces the local path, for tests).
  *
  * x, in_dtype, ld_x     : as for nvfp4_quantize, rows = M, K = w->k (M*K/2 <= 2 GiB)
  * x_codes, x_scales, g_x: the activations' NVFP4 encoding (outputs; g_x is an

@@ -199,17 +199,6 @@ static int encode_grid(int64_t rows, int64_t K) {
     return (int)(wg < 1 ? 1 : wg);
 }
 
-hipError_t launch_amax(const void* x, int in_dtype, int64_t rows, int64_t K, int64_t ld_x, float* partials,
-                       int n_partials, hipStream_t stream) {
-    if (in_dtype == NVFP4_IN_BF16)
-        hipLaunchKernelGGL(amax_partials_kernel<uint16_t>, dim3(n_partials), dim3(kQThreads), 0, stream,
-                           static_cast<const uint16_t*>(x), rows, K, ld_x, partials);
-    else
-        hipLaunchKernelGGL(amax_partials_kernel<float>, dim3(n_partials), dim3(kQThreads), 0, stream,
-                           static_cast<const float*>(x), rows, K, ld_x, partials);
-    return hipGetLastError();
-}
-
 hipError_t launch_quantize(const void* x, int in_dtype, int64_t rows, int64_t K, int64_t ld_x,
                            uint8_t* codes, uint8_t* scales, float* g, int g_mode,
                            float* partials, int n_partials, hipStream_t stream) {

@@ -29,6 +29,8 @@
 // partials in slice order 0..S-1 (its own from registers), so the result does
 // not depend on timing, writes Y = sum * g_x * g_w, zeroes the partials it
 // read and resets the counter: the workspace is zero again for the next call.
+#include <cstdlib>
+
 #include "common.h"
 
 namespace nvfp4 {
@@ -37,7 +39,8 @@ constexpr int kWriteThrough = 1 | 16;   // sc0|sc1: store past the non-coherent 
 constexpr int kDepth = 4;               // weight k-steps in flight per wavefront ahead of the math
 constexpr int kMaxSlices = 8;           // K-slices per group (the reducer polls at most 7 partials)
 constexpr int kSpinLimit = 1 << 20;     // polls before the reducer gives up (a misuse, never a hang)
-constexpr int kMaxPre = 10;             // longest slice whose weights are decoded ahead (16 VGPRs per k-step)
+constexpr int kMaxPre = 10;             // longest slice (bf16 input; 4 for fp32) whose weights are decoded
+                                        // ahead of the activations (16 VGPRs per k-step)
 
 constexpr int kAmaxSpin = 1 << 12;      // polls for a peer's slice max before reducing that slice here
 
@@ -77,7 +80,7 @@ __global__ __launch_bounds__(R * 64) void skinny_kernel(
     uint8_t* __restrict__ x_codes, uint8_t* __restrict__ x_scales, const uint8_t* __restrict__ w_codes,
     const uint8_t* __restrict__ w_scales, const float* __restrict__ colscale, int64_t N, int64_t n_pad,
     float* __restrict__ y, int64_t ld_y, uint32_t* __restrict__ counters, uint32_t* __restrict__ slots,
-    float* __restrict__ partials, int S) {
+    float* __restrict__ partials, int S, int amax_polls) {
     constexpr int kThreads = R * 64;
     constexpr int kXhatBytes = NKSL * 4 * 64 * 16;
     constexpr int kD = NKSL < kDepth ? NKSL : kDepth;
@@ -150,26 +153,42 @@ __global__ __launch_bounds__(R * 64) void skinny_kernel(
     };
     half8 adec[PRE ? NKSL : 1][4];
 
-    if constexpr (!PRE) {
-        // Activations first (loads complete in issue order, so the preparation
-        // waits only for them), then the weights' first kD k-steps.
-        load_activations();
-        csv = __builtin_bit_cast(float4v, bload16(rcs, (uint32_t)(nb * 16 + kg * 4) * 4, 0));
+    // Activations first (loads complete in issue order, so waiting for them
+    // leaves the weights in flight), then the weights' first kD k-steps.
+    load_activations();
+    csv = __builtin_bit_cast(float4v, bload16(rcs, (uint32_t)(nb * 16 + kg * 4) * 4, 0));
 #pragma unroll
-        for (int j = 0; j < kD; ++j) load_weights(j);
-        draw_ticket();
-        __builtin_amdgcn_sched_barrier(0);
-    } else {
-        // Weights first, each k-step decoded to FP16 registers as it arrives, so
-        // the decode overlaps the stream; the activations are requested right
-        // after the last weight load and only the matrix instructions remain
-        // once they are in.
+    for (int j = 0; j < kD; ++j) load_weights(j);
+    draw_ticket();
+    __builtin_amdgcn_sched_barrier(0);
+
+    // Global scale computed here (nvfp4_linear without a given scale): the S
+    // workgroups of a group hold the S slices of the same activations; each
+    // publishes its slice's max|x| as soon as its slice is in and collects the
+    // others' later.  A slice not published after kAmaxSpin polls is reduced
+    // here instead, so no workgroup depends on another one running.
+    const bool exchange = QUANT && !g_given;
+    uint32_t* gslots = slots + (size_t)grp * S;
+    float mine = 0.0f;
+    if (exchange) {
+        float part = 0.0f;
 #pragma unroll
-        for (int j = 0; j < kD; ++j) load_weights(j);
-        csv = __builtin_bit_cast(float4v, bload16(rcs, (uint32_t)(nb * 16 + kg * 4) * 4, 0));
-        draw_ticket();
-        if constexpr (NKSL <= kD) load_activations();
-        __builtin_amdgcn_sched_barrier(0);
+        for (int u = 0; u < (QUANT ? kBPT : 0); ++u) {
+            float v[16];
+            widen(raw[u], v);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) part = fmaxf(part, __builtin_fabsf(v[i]));
+        }
+        mine = block_max_r<R>(part, s_red);
+        if (S > 1 && threadIdx.x == 0)   // (sign bit set: a published word is never zero)
+            __hip_atomic_store(gslots + slice, __float_as_uint(mine) | 0x80000000u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    }
+
+    if constexpr (PRE) {
+        // Decode the weights to FP16 registers as they arrive, while the slice
+        // maxima of the other workgroups travel; only the matrix instructions
+        // remain once the activations are prepared.
 #pragma unroll
         for (int j = 0; j < NKSL; ++j) {
 #pragma unroll
@@ -178,69 +197,49 @@ __global__ __launch_bounds__(R * 64) void skinny_kernel(
                 asm volatile("" : "+v"(adec[j][c]));   // decode now, not next to its use
             }
             if (j + kD < NKSL) load_weights(j + kD);
-            if (j + kD == NKSL - 1) load_activations();
             __builtin_amdgcn_sched_barrier(0);
         }
     }
-    const float g_in = (QUANT && !g_given) ? 0.0f : g_x[0];
+
+    float gx = (QUANT && !g_given) ? 0.0f : g_x[0];
+    if (exchange) {
+        if (threadIdx.x < (unsigned)S) {
+            float got = mine;
+            if ((int)threadIdx.x != slice) {
+                uint32_t w = 0;
+                for (int i = 0; i < amax_polls && w == 0; ++i) {
+                    w = __hip_atomic_load(gslots + threadIdx.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    if (w == 0) __builtin_amdgcn_s_sleep(2);
+                }
+                got = w != 0 ? __uint_as_float(w & 0x7FFFFFFFu) : -1.0f;
+            }
+            s_slotmax[threadIdx.x] = got;
+        }
+        __syncthreads();
+        float amax = 0.0f;
+        for (int t = 0; t < S; ++t) {
+            const float m_t = s_slotmax[t];
+            if (m_t >= 0.0f) {
+                amax = fmaxf(amax, m_t);
+            } else {   // this workgroup reduces slice t itself
+                float p = 0.0f;
+                for (int b = threadIdx.x; b < M * kSliceBlocks; b += kThreads) {
+                    const int m = b / kSliceBlocks, kb = b - m * kSliceBlocks;
+                    const T* src = x + (int64_t)m * ld_x + (int64_t)(t * kSliceBlocks + kb) * 16;
+                    float v[16];
+                    load8(src, v);
+                    load8(src + 8, v + 8);
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) p = fmaxf(p, __builtin_fabsf(v[i]));
+                }
+                amax = fmaxf(amax, block_max_r<R>(p, s_red));
+            }
+        }
+        gx = global_scale_from_amax(amax);
+        if (blockIdx.x == 0 && threadIdx.x == 0) g_x[0] = gx;
+    }
 
     // The activations of the slice, once per workgroup, as exact FP16 in LDS.
-    float gx = g_in;
-    if constexpr (QUANT) {
-        if (!g_given) {
-            // The S workgroups of a group hold the S slices of the same activations:
-            // publish this slice's max|x| and collect the others'.  A slice whose
-            // workgroup has not published after kAmaxSpin polls is read and reduced
-            // here instead, so no workgroup depends on another one running.
-            float part = 0.0f;
-#pragma unroll
-            for (int u = 0; u < kBPT; ++u) {
-                float v[16];
-                widen(raw[u], v);
-#pragma unroll
-                for (int i = 0; i < 16; ++i) part = fmaxf(part, __builtin_fabsf(v[i]));
-            }
-            const float mine = block_max_r<R>(part, s_red);
-            uint32_t* gslots = slots + (size_t)grp * S;
-            if (S > 1 && threadIdx.x == 0)   // (sign bit set: a published word is never zero)
-                __hip_atomic_store(gslots + slice, __float_as_uint(mine) | 0x80000000u, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-            if (threadIdx.x < (unsigned)S) {
-                float got = mine;
-                if ((int)threadIdx.x != slice) {
-                    uint32_t w = 0;
-                    for (int i = 0; i < kAmaxSpin && w == 0; ++i) {
-                        w = __hip_atomic_load(gslots + threadIdx.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        if (w == 0) __builtin_amdgcn_s_sleep(2);
-                    }
-                    got = w != 0 ? __uint_as_float(w & 0x7FFFFFFFu) : -1.0f;
-                }
-                s_slotmax[threadIdx.x] = got;
-            }
-            __syncthreads();
-            float amax = 0.0f;
-            for (int t = 0; t < S; ++t) {
-                const float m_t = s_slotmax[t];
-                if (m_t >= 0.0f) {
-                    amax = fmaxf(amax, m_t);
-                } else {   // (rare) this workgroup reduces slice t itself
-                    float p = 0.0f;
-                    for (int b = threadIdx.x; b < M * kSliceBlocks; b += kThreads) {
-                        const int m = b / kSliceBlocks, kb = b - m * kSliceBlocks;
-                        const T* src = x + (int64_t)m * ld_x + (int64_t)(t * kSliceBlocks + kb) * 16;
-                        float v[16];
-                        load8(src, v);
-                        load8(src + 8, v + 8);
-#pragma unroll
-                        for (int i = 0; i < 16; ++i) p = fmaxf(p, __builtin_fabsf(v[i]));
-                    }
-                    amax = fmaxf(amax, block_max_r<R>(p, s_red));
-                }
-            }
-            gx = global_scale_from_amax(amax);
-            if (blockIdx.x == 0 && threadIdx.x == 0) g_x[0] = gx;
-        }
-    }
 #pragma unroll
     for (int u = 0; u < kBPT; ++u) {
         const int b = threadIdx.x + u * kThreads;
@@ -438,13 +437,15 @@ struct SkinnyArgs {
     uint32_t* slots;
     float* partials;
     int S;
+    int amax_polls;
 };
 
 template <typename T, int NKSL, int R, bool QUANT>
 void launch_one(dim3 grid, hipStream_t stream, const SkinnyArgs& a) {
-    hipLaunchKernelGGL((skinny_kernel<T, NKSL, R, QUANT, (NKSL <= kMaxPre)>), grid, dim3(R * 64), 0, stream, a.M,
-                       a.K, static_cast<const T*>(a.x), a.ld_x, a.g_x, a.g_given, a.x_codes, a.x_scales, a.wc, a.wsc,
-                       a.cs, a.N, a.n_pad, a.y, a.ld_y, a.counters, a.slots, a.partials, a.S);
+    hipLaunchKernelGGL((skinny_kernel<T, NKSL, R, QUANT, (QUANT && NKSL <= kMaxPre / sizeof(T) * 2)>), grid, dim3(R * 64), 0,
+                       stream, a.M, a.K, static_cast<const T*>(a.x), a.ld_x, a.g_x, a.g_given, a.x_codes, a.x_scales,
+                       a.wc, a.wsc, a.cs, a.N, a.n_pad, a.y, a.ld_y, a.counters, a.slots, a.partials, a.S,
+                       a.amax_polls);
 }
 
 template <typename T, bool QUANT, int R>
@@ -516,6 +517,8 @@ hipError_t launch_skinny(int64_t M, const void* x, int in_dtype, int64_t ld_x, f
     a.slots = a.counters + p.groups;
     a.partials = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + counters_bytes(p));
     a.S = p.S;
+    a.amax_polls = kAmaxSpin;
+    if (const char* e = std::getenv("NVFP4_AMAX_POLLS")) a.amax_polls = std::atoi(e);   // testing the fallback
     if (!quantize) return launch_plan<uint16_t, false>(p, stream, a);
     if (in_dtype == NVFP4_IN_BF16) return launch_plan<uint16_t, true>(p, stream, a);
     return launch_plan<float, true>(p, stream, a);

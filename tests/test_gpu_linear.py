@@ -124,3 +124,17 @@ def test_alternating_inputs_see_fresh_codes():
     torch.cuda.synchronize()
     for i, o in enumerate(outs):
         assert torch.equal(o, want[i % 2]), f"call {i}"
+
+
+@pytest.mark.parametrize("shape", ["decode", "3x2048x300"])
+def test_amax_fallback_when_peers_do_not_publish(shape, monkeypatch):
+    """The few-token kernel takes the global amax from the slice maxima its peer workgroups publish;
+    with a poll bound of zero every workgroup reduces all slices itself. Same bits either way."""
+    monkeypatch.setenv("NVFP4_AMAX_POLLS", "0")
+    if shape == "decode":
+        wl = workloads.make_decode()
+        _check(wl.x, "bf16", wl.w, "bf16", "decode, amax fallback", calls=2)
+    else:
+        x = workloads.random_matrix(1301, 3, 2048, dtype="bf16")
+        w = workloads.random_matrix(1302, 300, 2048, 0.05, dtype="bf16")
+        _check(x, "bf16", [w], "bf16", "3x2048x300, amax fallback", calls=2)
