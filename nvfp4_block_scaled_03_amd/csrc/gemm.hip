@@ -27,11 +27,14 @@ namespace nvfp4 {
 // Tiled GEMM: a workgroup of 2x2 wavefronts computes a (2*TM*32) x (2*TN*32)
 // output tile; each wavefront a TM x TN grid of 32x32x16 FP16 instructions.
 //
-// Operands move global -> registers -> LDS in a two-stage ring: while the
-// wavefronts decode and multiply k-step ks out of one LDS stage, the packed
-// codes and scales of k-step ks+1 are already in registers (16-byte buffer
-// loads issued a whole compute phase earlier) and are written to the other
-// stage after a barrier.  Each operand byte is fetched once per workgroup.
+// Operands move global -> LDS by buffer loads that write LDS directly (no
+// register staging), into a four-stage ring: the loads of k-step ks+3 are
+// issued at the start of k-step ks, so each has two k-steps to arrive.  The
+// wavefronts read their fragments one half k-step ahead (the second half of
+// ks while multiplying the first, the first half of ks+1 while multiplying the
+// second), and decode each 8-element chunk while the previous chunk's matrix
+// instructions run.  One barrier per k-step.  Each operand byte is fetched
+// once per workgroup.
 //
 // LDS stage layout (bytes), "lane" = l32 + 32*h of the consuming wavefront:
 //   A codes  [row block 8][half p 2][lane 64][16]  rows rb*32+l32, bytes h*32+p*16 of the k-step
@@ -60,12 +63,6 @@ struct TileGeom {
     static constexpr int AS_WORDS = A_SC / 4 / 256, BS_WORDS = B_SC / 4 / 256;
 };
 
-template <int TM, int TN>
-struct Staging {
-    uint4 a[TileGeom<TM, TN>::A_CHUNKS], b[TileGeom<TM, TN>::B_CHUNKS];
-    uint32_t as[TileGeom<TM, TN>::AS_WORDS], bs[TileGeom<TM, TN>::BS_WORDS];
-};
-
 struct TileSrc {
     rsrc_t ac, as, bc, bs;
     uint32_t a_lane, as_lane, b_lane, bs_lane;   // per-lane offsets inside a 32-row / 32-column block
@@ -73,82 +70,136 @@ struct TileSrc {
     uint32_t a_blk, as_blk, b_blk, bs_blk;       // advance per 32-row / 32-column block
 };
 
-// Global -> registers for k-step ks.  Thread t of wavefront w stages slabs w, w+4, ...
+// One buffer load that writes LDS directly: lane l's 16 (or 4) bytes land at
+// lds + 16*l (4*l).  lds must be the same for the whole wavefront.
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+__device__ __forceinline__ void dma16(rsrc_t r, uint8_t* lds, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, (int)voff, (int)soff, 0, 0);
+}
+__device__ __forceinline__ void dma4(rsrc_t r, uint8_t* lds, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 4, (int)voff, (int)soff, 0, 0);
+}
+
+// A scalar offset past the end of every buffer: the load touches no memory and
+// writes zeros, so steps beyond the last k-step keep the load count per step
+// constant (the vmcnt bookkeeping below relies on it) at no memory cost.
+constexpr uint32_t kDeadOffset = 0x80000000u;
+
+// Global -> LDS stage for k-step ks.  Wavefront w moves slabs w, w+4, ...;
+// a slab is 1 KB of codes or 256 B of scales.
 template <int TM, int TN>
-__device__ __forceinline__ void stage_load(Staging<TM, TN>& st, const TileSrc& s, uint32_t ks, int wave) {
+__device__ __forceinline__ void stage_dma(uint8_t* stage, const TileSrc& s, uint32_t ks, bool live, int wave) {
     using G = TileGeom<TM, TN>;
 #pragma unroll
     for (int u = 0; u < G::A_CHUNKS; ++u) {
         const int slab = wave + 4 * u, rb = slab >> 1, p = slab & 1;
-        st.a[u] = bload16(s.ac, s.a_lane, s.a_tile + rb * s.a_blk + ks * 64 + p * 16);
+        dma16(s.ac, stage + slab * 1024, s.a_lane, live ? s.a_tile + rb * s.a_blk + ks * 64 + p * 16 : kDeadOffset);
     }
 #pragma unroll
     for (int u = 0; u < G::B_CHUNKS; ++u) {
         const int slab = wave + 4 * u, cb = slab >> 1, p = slab & 1;
-        st.b[u] = bload16(s.bc, s.b_lane, s.b_tile + cb * s.b_blk + ks * 1024 + p * 256);
+        dma16(s.bc, stage + G::A_CODES + slab * 1024, s.b_lane,
+              live ? s.b_tile + cb * s.b_blk + ks * 1024 + p * 256 : kDeadOffset);
     }
 #pragma unroll
-    for (int u = 0; u < G::AS_WORDS; ++u)
-        st.as[u] = bload4(s.as, s.as_lane, s.as_tile + (wave + 4 * u) * s.as_blk + ks * 8);
+    for (int u = 0; u < G::AS_WORDS; ++u) {
+        const int slab = wave + 4 * u;
+        dma4(s.as, stage + G::A_CODES + G::B_CODES + slab * 256, s.as_lane,
+             live ? s.as_tile + slab * s.as_blk + ks * 8 : kDeadOffset);
+    }
 #pragma unroll
-    for (int u = 0; u < G::BS_WORDS; ++u)
-        st.bs[u] = bload4(s.bs, s.bs_lane, s.bs_tile + (wave + 4 * u) * s.bs_blk + ks * 128);
+    for (int u = 0; u < G::BS_WORDS; ++u) {
+        const int slab = wave + 4 * u;
+        dma4(s.bs, stage + G::A_CODES + G::B_CODES + G::A_SC + slab * 256, s.bs_lane,
+             live ? s.bs_tile + slab * s.bs_blk + ks * 128 : kDeadOffset);
+    }
 }
 
-template <int TM, int TN>
-__device__ __forceinline__ void stage_store(uint8_t* stage, const Staging<TM, TN>& st, int wave, int lane) {
-    using G = TileGeom<TM, TN>;
-#pragma unroll
-    for (int u = 0; u < G::A_CHUNKS; ++u)
-        *reinterpret_cast<uint4*>(stage + (wave + 4 * u) * 1024 + lane * 16) = st.a[u];
-#pragma unroll
-    for (int u = 0; u < G::B_CHUNKS; ++u)
-        *reinterpret_cast<uint4*>(stage + G::A_CODES + (wave + 4 * u) * 1024 + lane * 16) = st.b[u];
-#pragma unroll
-    for (int u = 0; u < G::AS_WORDS; ++u)
-        *reinterpret_cast<uint32_t*>(stage + G::A_CODES + G::B_CODES + (wave + 4 * u) * 256 + lane * 4) = st.as[u];
-#pragma unroll
-    for (int u = 0; u < G::BS_WORDS; ++u)
-        *reinterpret_cast<uint32_t*>(stage + G::A_CODES + G::B_CODES + G::A_SC + (wave + 4 * u) * 256 + lane * 4) =
-            st.bs[u];
+// Wait until at most n of this wavefront's buffer loads are outstanding
+// (they complete in issue order); the other counters are left alone.
+template <int n>
+__device__ __forceinline__ void wait_vmem() {
+    static_assert(n >= 0 && n < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// Decode and multiply one k-step held in an LDS stage.
+// Raw fragments of one wavefront for half p of a k-step, and the block scales
+// of a whole k-step, read from an LDS stage.
 template <int TM, int TN>
-__device__ __forceinline__ void stage_compute(float16v (&acc)[TM][TN], const uint8_t* stage, int wm, int wn,
-                                              int lane) {
+struct Frags {
+    uint4 a[TM], b[TN];
+};
+template <int TM, int TN>
+__device__ __forceinline__ void read_half(Frags<TM, TN>& f, const uint8_t* stage, int p, int wm, int wn, int lane) {
     using G = TileGeom<TM, TN>;
-    uint32_t asc[TM], bsc[TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
-        asc[i] = *reinterpret_cast<const uint32_t*>(stage + G::A_CODES + G::B_CODES + (wm * TM + i) * 256 + lane * 4);
+        f.a[i] = *reinterpret_cast<const uint4*>(stage + ((wm * TM + i) * 2 + p) * 1024 + lane * 16);
 #pragma unroll
     for (int j = 0; j < TN; ++j)
-        bsc[j] = *reinterpret_cast<const uint32_t*>(stage + G::A_CODES + G::B_CODES + G::A_SC +
-                                                    (wn * TN + j) * 256 + lane * 4);
+        f.b[j] = *reinterpret_cast<const uint4*>(stage + G::A_CODES + ((wn * TN + j) * 2 + p) * 1024 + lane * 16);
+}
+template <int TM, int TN>
+struct Scales {
+    uint32_t a[TM], b[TN];
+};
+template <int TM, int TN>
+__device__ __forceinline__ void read_scales(Scales<TM, TN>& sc, const uint8_t* stage, int wm, int wn, int lane) {
+    using G = TileGeom<TM, TN>;
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-        uint4 av[TM], bv[TN];
+    for (int i = 0; i < TM; ++i)
+        sc.a[i] = *reinterpret_cast<const uint32_t*>(stage + G::A_CODES + G::B_CODES + (wm * TM + i) * 256 + lane * 4);
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
-            av[i] = *reinterpret_cast<const uint4*>(stage + ((wm * TM + i) * 2 + p) * 1024 + lane * 16);
+    for (int j = 0; j < TN; ++j)
+        sc.b[j] = *reinterpret_cast<const uint32_t*>(stage + G::A_CODES + G::B_CODES + G::A_SC + (wn * TN + j) * 256 +
+                                                     lane * 4);
+}
+
+// Decoded operands of one 8-element chunk c of half p.
+template <int TM, int TN>
+struct Chunk {
+    half8 a[TM], b[TN];
+};
+template <int TM, int TN>
+__device__ __forceinline__ void decode_chunk(Chunk<TM, TN>& d, const Frags<TM, TN>& f, const Scales<TM, TN>& sc, int p,
+                                             int c) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) d.a[i] = decode8(word_of(f.a[i], c), scale_byte(sc.a[i], 2 * p + (c >> 1)));
+#pragma unroll
+    for (int j = 0; j < TN; ++j) d.b[j] = decode8(word_of(f.b[j], c), scale_byte(sc.b[j], 2 * p + (c >> 1)));
+}
+template <int TM, int TN>
+__device__ __forceinline__ void mma_chunk(float16v (&acc)[TM][TN], const Chunk<TM, TN>& d) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-            bv[j] = *reinterpret_cast<const uint4*>(stage + G::A_CODES + ((wn * TN + j) * 2 + p) * 1024 + lane * 16);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(d.a[i], d.b[j], acc[i][j], 0, 0, 0);
+}
+
+// One k-step held in stage `cur`, as 8 chunks (p = q >> 2, c = q & 3).  On
+// entry f[0] holds half 0 of this k-step, sc[0] its scales and d[0] its chunk 0
+// decoded; on exit the same holds for the next k-step, read from `nxt`.
+template <int TM, int TN>
+__device__ __forceinline__ void kstep(float16v (&acc)[TM][TN], Frags<TM, TN> (&f)[2], Scales<TM, TN> (&sc)[2],
+                                      Chunk<TM, TN> (&d)[2], const uint8_t* cur, const uint8_t* nxt, int wm, int wn,
+                                      int lane) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            half8 a[TM], b[TN];
-#pragma unroll
-            for (int i = 0; i < TM; ++i) a[i] = decode8(word_of(av[i], c), scale_byte(asc[i], 2 * p + (c >> 1)));
-#pragma unroll
-            for (int j = 0; j < TN; ++j) b[j] = decode8(word_of(bv[j], c), scale_byte(bsc[j], 2 * p + (c >> 1)));
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+    for (int q = 0; q < 8; ++q) {
+        if (q == 0) read_half<TM, TN>(f[1], cur, 1, wm, wn, lane);
+        if (q == 4) {
+            read_half<TM, TN>(f[0], nxt, 0, wm, wn, lane);
+            read_scales<TM, TN>(sc[1], nxt, wm, wn, lane);
         }
+        if (q < 7) {
+            const int p = (q + 1) >> 2, c = (q + 1) & 3;
+            decode_chunk<TM, TN>(d[(q + 1) & 1], f[p], sc[0], p, c);
+        } else {
+            decode_chunk<TM, TN>(d[0], f[0], sc[1], 0, 0);
+        }
+        mma_chunk<TM, TN>(acc, d[q & 1]);
     }
+    sc[0] = sc[1];
 }
 
 template <int TM, int TN>
@@ -161,7 +212,13 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(int64_t M, const uint8_t
                                                         int64_t n_pad, int64_t K, float* __restrict__ y,
                                                         int64_t ld_y, int tiles_m, int tiles_n) {
     using G = TileGeom<TM, TN>;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * G::STAGE];
+    // Four separate arrays rather than one: the compiler then tells the stages
+    // apart and waits only for the loads that target the stage being read.
+    __shared__ __attribute__((aligned(16))) uint8_t st0[G::STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t st1[G::STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t st2[G::STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t st3[G::STAGE];
+    uint8_t* const stg[4] = {st0, st1, st2, st3};
 
     // hardware id -> logical id: the workgroups of one XCD get consecutive logical ids
     const int nwg = tiles_m * tiles_n;
@@ -209,19 +266,34 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(int64_t M, const uint8_t
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    Staging<TM, TN> st;
-    stage_load<TM, TN>(st, s, 0, wave);
-    stage_store<TM, TN>(lds, st, wave, lane);
-    if (KS > 1) stage_load<TM, TN>(st, s, 1, wave);
-    __syncthreads();
-    for (uint32_t ks = 0; ks < KS; ++ks) {
-        uint8_t* cur = lds + (ks & 1) * G::STAGE;
-        stage_compute<TM, TN>(acc, cur, wm, wn, lane);
-        if (ks + 1 < KS) {
-            __syncthreads();                                  // everyone is done with the other stage
-            stage_store<TM, TN>(lds + ((ks + 1) & 1) * G::STAGE, st, wave, lane);
-            if (ks + 2 < KS) stage_load<TM, TN>(st, s, ks + 2, wave);
-            __syncthreads();                                  // stage ks+1 is complete
+    // Ring invariant at the top of k-step t: k-steps up to t+1 are in LDS and
+    // visible to every wavefront, k-step t+2 is in flight.
+    constexpr int kLoadsPerStep = G::A_CHUNKS + G::B_CHUNKS + G::AS_WORDS + G::BS_WORDS;
+    stage_dma<TM, TN>(stg[0], s, 0, true, wave);
+    stage_dma<TM, TN>(stg[1], s, 1, KS > 1, wave);
+    stage_dma<TM, TN>(stg[2], s, 2, KS > 2, wave);
+    wait_vmem<kLoadsPerStep>();
+    __builtin_amdgcn_s_barrier();
+
+    Frags<TM, TN> f[2];
+    Scales<TM, TN> sc[2];
+    Chunk<TM, TN> d[2];
+    read_half<TM, TN>(f[0], stg[0], 0, wm, wn, lane);
+    read_scales<TM, TN>(sc[0], stg[0], wm, wn, lane);
+    decode_chunk<TM, TN>(d[0], f[0], sc[0], 0, 0);
+    // The k-step count is rounded up to a multiple of 4 so the loop body has no
+    // branches (the compiler's per-stage wait tracking does not survive them);
+    // the extra k-steps load zeros (scale 0) and add nothing.
+    const uint32_t KS4 = (KS + 3) & ~3u;
+    for (uint32_t t0 = 0; t0 < KS4; t0 += 4) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const uint32_t t = t0 + u;
+            // stage (t+3)%4 was last read during k-step t-1, before the last barrier
+            stage_dma<TM, TN>(stg[(u + 3) & 3], s, t + 3, t + 3 < KS, wave);
+            kstep<TM, TN>(acc, f, sc, d, stg[u], stg[(u + 1) & 3], wm, wn, lane);
+            wait_vmem<kLoadsPerStep>();   // k-step t+2 has landed; t+3 may still be in flight
+            __builtin_amdgcn_s_barrier();
         }
     }
 
@@ -257,7 +329,8 @@ hipError_t launch_gemm(int64_t M, const uint8_t* a_codes, const uint8_t* a_scale
         return launch_skinny(M, nullptr, NVFP4_IN_BF16, 0, const_cast<float*>(g_x), NVFP4_G_GIVEN,
                              const_cast<uint8_t*>(a_codes), const_cast<uint8_t*>(a_scales), false, d, y, ld_y, ws,
                              stream);
-    } else if (M <= 128) {
+    }
+    if (M <= 128) {
         const int tiles_m = (int)((M + 127) / 128), tiles_n = (int)(d.n_padded / 128);
         hipLaunchKernelGGL((gemm_tile_kernel<2, 2>), dim3(tiles_m * tiles_n), dim3(256), 0, stream, M, a_codes,
                            a_scales, g_x, wc, wsc, cs, d.n, d.n_padded, d.k, y, ld_y, tiles_m, tiles_n);
