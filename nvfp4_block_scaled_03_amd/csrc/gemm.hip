@@ -140,11 +140,11 @@ __device__ __forceinline__ void read_half(Frags<TM, TN>& f, const uint8_t* stage
         f.b[j] = *reinterpret_cast<const uint4*>(stage + G::A_CODES + ((wn * TN + j) * 2 + p) * 1024 + lane * 16);
 }
 template <int TM, int TN>
-struct Scales {
+struct RawScales {
     uint32_t a[TM], b[TN];
 };
 template <int TM, int TN>
-__device__ __forceinline__ void read_scales(Scales<TM, TN>& sc, const uint8_t* stage, int wm, int wn, int lane) {
+__device__ __forceinline__ void read_raw_scales(RawScales<TM, TN>& sc, const uint8_t* stage, int wm, int wn, int lane) {
     using G = TileGeom<TM, TN>;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -155,51 +155,117 @@ __device__ __forceinline__ void read_scales(Scales<TM, TN>& sc, const uint8_t* s
                                                      lane * 4);
 }
 
+// Block scales of one k-step as FP16 pairs.  The 7 magnitude bits of an E4M3
+// byte placed at FP16 bits 13..7 give S * 2^-8 exactly (an FP16 subnormal for
+// the E4M3 subnormals).  lo holds bytes 0 and 2 of a lane's scale word, hi
+// bytes 1 and 3, so 16-element block i (0..3) has its scale in half i >> 1 of
+// (i & 1 ? hi : lo).
+struct ScalePair {
+    uint32_t lo, hi;
+};
+__device__ __forceinline__ ScalePair split_scales(uint32_t w) {
+    return {(w << 7) & 0x3F803F80u, (w >> 1) & 0x3F803F80u};
+}
+__device__ __forceinline__ half2v block_scale(const ScalePair& sp, int i) {
+    const half2v pr = __builtin_bit_cast(half2v, (i & 1) ? sp.hi : sp.lo);
+    return (i >> 1) ? half2v{pr[1], pr[1]} : half2v{pr[0], pr[0]};
+}
+template <int TM, int TN>
+struct Scales {
+    ScalePair a[TM], b[TN];
+};
+template <int TM, int TN>
+__device__ __forceinline__ void split_all(Scales<TM, TN>& out, const RawScales<TM, TN>& in) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) out.a[i] = split_scales(in.a[i]);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) out.b[j] = split_scales(in.b[j]);
+}
+
+// Two elements of a chunk: the conversion's power-of-two scale makes each code
+// exactly code * 256, and the packed multiply by S * 2^-8 gives code * S
+// exactly (at most 6 significant bits, inside [2^-10, 2688]).
+template <int BYTE>
+__device__ __forceinline__ half2v dec2(uint32_t w, half2v s2) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, BYTE) * s2;
+}
+
 // Decoded operands of one 8-element chunk c of half p.
 template <int TM, int TN>
 struct Chunk {
     half8 a[TM], b[TN];
 };
+
+// Piece k (0 .. 2*(TM+TN)-1) of decoding chunk c of half p: half (k & 1) of
+// operand k >> 1 (A rows first, then B columns).
+template <int TM, int TN>
+__device__ __forceinline__ void decode_piece(Chunk<TM, TN>& d, const Frags<TM, TN>& f, const Scales<TM, TN>& sc,
+                                             int p, int c, int k) {
+    const int o = k >> 1, blk = 2 * p + (c >> 1);
+    const bool is_a = o < TM;
+    const uint32_t w = is_a ? word_of(f.a[o], c) : word_of(f.b[o - TM], c);
+    const half2v s2 = block_scale(is_a ? sc.a[o] : sc.b[o - TM], blk);
+    half8& v = is_a ? d.a[o] : d.b[o - TM];
+    if ((k & 1) == 0) {
+        const half2v e0 = dec2<0>(w, s2), e1 = dec2<1>(w, s2);
+        v.s0 = e0[0]; v.s1 = e0[1]; v.s2 = e1[0]; v.s3 = e1[1];
+    } else {
+        const half2v e2 = dec2<2>(w, s2), e3 = dec2<3>(w, s2);
+        v.s4 = e2[0]; v.s5 = e2[1]; v.s6 = e3[0]; v.s7 = e3[1];
+    }
+}
 template <int TM, int TN>
 __device__ __forceinline__ void decode_chunk(Chunk<TM, TN>& d, const Frags<TM, TN>& f, const Scales<TM, TN>& sc, int p,
                                              int c) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i) d.a[i] = decode8(word_of(f.a[i], c), scale_byte(sc.a[i], 2 * p + (c >> 1)));
-#pragma unroll
-    for (int j = 0; j < TN; ++j) d.b[j] = decode8(word_of(f.b[j], c), scale_byte(sc.b[j], 2 * p + (c >> 1)));
-}
-template <int TM, int TN>
-__device__ __forceinline__ void mma_chunk(float16v (&acc)[TM][TN], const Chunk<TM, TN>& d) {
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(d.a[i], d.b[j], acc[i][j], 0, 0, 0);
+    for (int k = 0; k < 2 * (TM + TN); ++k) decode_piece<TM, TN>(d, f, sc, p, c, k);
 }
 
 // One k-step held in stage `cur`, as 8 chunks (p = q >> 2, c = q & 3).  On
-// entry f[0] holds half 0 of this k-step, sc[0] its scales and d[0] its chunk 0
+// entry f[0] holds half 0 of this k-step, sc its scales and d[0] its chunk 0
 // decoded; on exit the same holds for the next k-step, read from `nxt`.
+//
+// The instruction order is fixed by hand (the scheduler may not move anything
+// across the fences): each matrix instruction of chunk q is followed by an
+// equal share of the decode of chunk q+1, so the vector ALU work runs while
+// the matrix core is busy.  LDS reads are issued a whole half k-step before
+// their data is decoded; the scales of the next k-step are split during
+// chunk 5.
 template <int TM, int TN>
-__device__ __forceinline__ void kstep(float16v (&acc)[TM][TN], Frags<TM, TN> (&f)[2], Scales<TM, TN> (&sc)[2],
+__device__ __forceinline__ void kstep(float16v (&acc)[TM][TN], Frags<TM, TN> (&f)[2], Scales<TM, TN>& sc,
                                       Chunk<TM, TN> (&d)[2], const uint8_t* cur, const uint8_t* nxt, int wm, int wn,
                                       int lane) {
+    constexpr int kMma = TM * TN, kPieces = 2 * (TM + TN), kOps = TM + TN;
+    static_assert(kPieces % kMma == 0 || kMma % kPieces == 0, "pieces must spread evenly");
+    RawScales<TM, TN> raw;
+    Scales<TM, TN> nsc;
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
         if (q == 0) read_half<TM, TN>(f[1], cur, 1, wm, wn, lane);
         if (q == 4) {
             read_half<TM, TN>(f[0], nxt, 0, wm, wn, lane);
-            read_scales<TM, TN>(sc[1], nxt, wm, wn, lane);
+            read_raw_scales<TM, TN>(raw, nxt, wm, wn, lane);
         }
-        if (q < 7) {
-            const int p = (q + 1) >> 2, c = (q + 1) & 3;
-            decode_chunk<TM, TN>(d[(q + 1) & 1], f[p], sc[0], p, c);
-        } else {
-            decode_chunk<TM, TN>(d[0], f[0], sc[1], 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        // next chunk: (q+1) of this k-step, or chunk 0 of the next one
+        const int np = q < 7 ? (q + 1) >> 2 : 0, nc = q < 7 ? (q + 1) & 3 : 0;
+        Chunk<TM, TN>& nd = d[(q + 1) & 1];
+        const Frags<TM, TN>& nf = f[np];
+#pragma unroll
+        for (int m = 0; m < kMma; ++m) {
+            const int i = m / TN, j = m % TN;
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(d[q & 1].a[i], d[q & 1].b[j], acc[i][j], 0, 0, 0);
+            if (q == 5 && m < kOps) {
+                if (m < TM) nsc.a[m] = split_scales(raw.a[m]);
+                else nsc.b[m - TM] = split_scales(raw.b[m - TM]);
+            }
+#pragma unroll
+            for (int k = m * kPieces / kMma; k < (m + 1) * kPieces / kMma; ++k)
+                decode_piece<TM, TN>(nd, nf, q < 7 ? sc : nsc, np, nc, k);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        mma_chunk<TM, TN>(acc, d[q & 1]);
     }
-    sc[0] = sc[1];
+    sc = nsc;
 }
 
 template <int TM, int TN>
@@ -276,11 +342,15 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(int64_t M, const uint8_t
     __builtin_amdgcn_s_barrier();
 
     Frags<TM, TN> f[2];
-    Scales<TM, TN> sc[2];
     Chunk<TM, TN> d[2];
-    read_half<TM, TN>(f[0], stg[0], 0, wm, wn, lane);
-    read_scales<TM, TN>(sc[0], stg[0], wm, wn, lane);
-    decode_chunk<TM, TN>(d[0], f[0], sc[0], 0, 0);
+    Scales<TM, TN> sc;
+    {
+        RawScales<TM, TN> raw;
+        read_half<TM, TN>(f[0], stg[0], 0, wm, wn, lane);
+        read_raw_scales<TM, TN>(raw, stg[0], wm, wn, lane);
+        split_all<TM, TN>(sc, raw);
+    }
+    decode_chunk<TM, TN>(d[0], f[0], sc, 0, 0);
     // The k-step count is rounded up to a multiple of 4 so the loop body has no
     // branches (the compiler's per-stage wait tracking does not survive them);
     // the extra k-steps load zeros (scale 0) and add nothing.

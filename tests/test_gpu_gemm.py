@@ -68,6 +68,14 @@ def test_tiled_ragged_fused(M):
     check_dense(x, "bf16", ws, "bf16", f"tiled fused M={M}")
 
 
+@pytest.mark.parametrize("M,K", [(40, 128), (260, 128), (260, 256), (260, 384), (40, 896)])
+def test_tiled_short_and_odd_k(M, K):
+    """k-step counts of 1, 2, 3 and 7: the tile kernels' load ring runs past the last k-step."""
+    x = workloads.random_matrix(700 + K + M, M, K, dtype="bf16")
+    ws = [workloads.random_matrix(800 + K, 300, K, 0.05, dtype="bf16")]
+    check_dense(x, "bf16", ws, "bf16", f"tiled M={M} K={K}")
+
+
 def test_fused_module_mix_skinny():
     x = workloads.random_matrix(501, 7, 512, dtype="bf16")
     ws = [workloads.random_matrix(502 + i, r, 512, s, dtype="bf16")
