@@ -247,8 +247,7 @@ nvfp4_status nvfp4_gemm(int64_t M, const uint8_t* a_codes, const uint8_t* a_scal
 size_t nvfp4_linear_workspace_bytes(int64_t M, int in_dtype, const nvfp4_weight_desc* w) {
     if (w == nullptr || M < 0 || w->k <= 0 || w->n_padded <= 0) return 0;
     (void)in_dtype;
-    const size_t skinny = nvfp4::skinny_applies(M, *w) ? nvfp4::skinny_workspace_bytes(*w) : 0;
-    return skinny + nvfp4_quantize_workspace_bytes(M, w->k);
+    return nvfp4::gemm_workspace_bytes(M, *w) + nvfp4_quantize_workspace_bytes(M, w->k);
 }
 
 nvfp4_status nvfp4_linear(const void* x, int in_dtype, int64_t M, int64_t ld_x, uint8_t* x_codes, uint8_t* x_scales,
@@ -290,15 +289,15 @@ nvfp4_status nvfp4_linear(const void* x, int in_dtype, int64_t M, int64_t ld_x, 
     const int64_t esize = in_dtype == NVFP4_IN_BF16 ? 2 : 4;
     const bool skinny = nvfp4::skinny_applies(M, *w);
     const bool fused = skinny && M * ld_x * esize <= INT32_MAX;
-    float* partials = reinterpret_cast<float*>(wsb + (skinny ? nvfp4::skinny_workspace_bytes(*w) : 0));
+    const size_t gemm_ws = nvfp4::gemm_workspace_bytes(M, *w);   // the product's part comes first
+    float* partials = reinterpret_cast<float*>(wsb + gemm_ws);
     const int n_partials = nvfp4::quantize_partials_count(M, K);
     if (M == 0 || !fused) {
         hipError_t e = nvfp4::launch_quantize(x, in_dtype, M, K, ld_x, x_codes, x_scales, g_x, g_mode, partials,
                                               n_partials, s);
         if (e != hipSuccess) return fail(NVFP4_ERR_HIP, "linear quantize launch: %s", hipGetErrorString(e));
         if (M == 0) return ok();
-        return launched(nvfp4::launch_gemm(M, x_codes, x_scales, g_x, *w, y, ld_y, skinny ? workspace : nullptr,
-                                           skinny ? nvfp4::skinny_workspace_bytes(*w) : 0, s),
+        return launched(nvfp4::launch_gemm(M, x_codes, x_scales, g_x, *w, y, ld_y, workspace, gemm_ws, s),
                         "linear gemm launch");
     }
     return launched(nvfp4::launch_skinny(M, x, in_dtype, ld_x, g_x, g_mode, x_codes, x_scales, true, *w, y, ld_y,

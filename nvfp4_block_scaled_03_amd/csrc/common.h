@@ -31,6 +31,7 @@ constexpr int kPackNAlign = 256;   // n is padded to a multiple of this
 constexpr int64_t kMaxCodeBytes = int64_t(1) << 31;   // per operand: the GEMMs use 32-bit byte offsets
 constexpr size_t kBlobHeader = 256;
 
+constexpr int kComputeUnits = 256;   // MI355X: the work splits are sized for this many
 // Few-token products: at most 16 tokens (one 16-column matrix-instruction tile).
 constexpr int kSkinnyM = 16;
 constexpr int kMaxAmaxPartials = 1024;   // upper bound of quantize_partials_count

@@ -19,6 +19,8 @@
 // per-lane offset, and the per-k-step / per-tile advance in a scalar offset.
 // Reads past the end of a tensor return zero, which is how rows beyond M (a
 // ragged last tile) contribute nothing without any clamping.
+#include <algorithm>
+
 #include "common.h"
 
 namespace nvfp4 {
@@ -85,34 +87,45 @@ __device__ __forceinline__ void dma4(rsrc_t r, uint8_t* lds, uint32_t voff, uint
 // constant (the vmcnt bookkeeping below relies on it) at no memory cost.
 constexpr uint32_t kDeadOffset = 0x80000000u;
 
-// Global -> LDS stage for k-step ks.  Wavefront w moves slabs w, w+4, ...;
-// a slab is 1 KB of codes or 256 B of scales.
+// Global -> LDS stage for k-step ks, one load at a time: load idx (0 ..
+// kLoads-1) of wavefront w moves slab w + 4*u of the A codes, B codes, A
+// scales or B scales (a slab is 1 KB of codes or 256 B of scales).
 template <int TM, int TN>
-__device__ __forceinline__ void stage_dma(uint8_t* stage, const TileSrc& s, uint32_t ks, bool live, int wave) {
+struct DmaPlan {
     using G = TileGeom<TM, TN>;
-#pragma unroll
-    for (int u = 0; u < G::A_CHUNKS; ++u) {
-        const int slab = wave + 4 * u, rb = slab >> 1, p = slab & 1;
+    static constexpr int kLoads = G::A_CHUNKS + G::B_CHUNKS + G::AS_WORDS + G::BS_WORDS;
+};
+template <int TM, int TN>
+__device__ __forceinline__ void dma_one(uint8_t* stage, const TileSrc& s, uint32_t ks, bool live, int wave, int idx) {
+    using G = TileGeom<TM, TN>;
+    if (idx < G::A_CHUNKS) {
+        const int slab = wave + 4 * idx, rb = slab >> 1, p = slab & 1;
         dma16(s.ac, stage + slab * 1024, s.a_lane, live ? s.a_tile + rb * s.a_blk + ks * 64 + p * 16 : kDeadOffset);
+        return;
     }
-#pragma unroll
-    for (int u = 0; u < G::B_CHUNKS; ++u) {
-        const int slab = wave + 4 * u, cb = slab >> 1, p = slab & 1;
+    idx -= G::A_CHUNKS;
+    if (idx < G::B_CHUNKS) {
+        const int slab = wave + 4 * idx, cb = slab >> 1, p = slab & 1;
         dma16(s.bc, stage + G::A_CODES + slab * 1024, s.b_lane,
               live ? s.b_tile + cb * s.b_blk + ks * 1024 + p * 256 : kDeadOffset);
+        return;
     }
-#pragma unroll
-    for (int u = 0; u < G::AS_WORDS; ++u) {
-        const int slab = wave + 4 * u;
+    idx -= G::B_CHUNKS;
+    if (idx < G::AS_WORDS) {
+        const int slab = wave + 4 * idx;
         dma4(s.as, stage + G::A_CODES + G::B_CODES + slab * 256, s.as_lane,
              live ? s.as_tile + slab * s.as_blk + ks * 8 : kDeadOffset);
+        return;
     }
+    idx -= G::AS_WORDS;
+    const int slab = wave + 4 * idx;
+    dma4(s.bs, stage + G::A_CODES + G::B_CODES + G::A_SC + slab * 256, s.bs_lane,
+         live ? s.bs_tile + slab * s.bs_blk + ks * 128 : kDeadOffset);
+}
+template <int TM, int TN>
+__device__ __forceinline__ void stage_dma(uint8_t* stage, const TileSrc& s, uint32_t ks, bool live, int wave) {
 #pragma unroll
-    for (int u = 0; u < G::BS_WORDS; ++u) {
-        const int slab = wave + 4 * u;
-        dma4(s.bs, stage + G::A_CODES + G::B_CODES + G::A_SC + slab * 256, s.bs_lane,
-             live ? s.bs_tile + slab * s.bs_blk + ks * 128 : kDeadOffset);
-    }
+    for (int idx = 0; idx < DmaPlan<TM, TN>::kLoads; ++idx) dma_one<TM, TN>(stage, s, ks, live, wave, idx);
 }
 
 // Wait until at most n of this wavefront's buffer loads are outstanding
@@ -228,14 +241,17 @@ __device__ __forceinline__ void decode_chunk(Chunk<TM, TN>& d, const Frags<TM, T
 // The instruction order is fixed by hand (the scheduler may not move anything
 // across the fences): each matrix instruction of chunk q is followed by an
 // equal share of the decode of chunk q+1, so the vector ALU work runs while
-// the matrix core is busy.  LDS reads are issued a whole half k-step before
+// the matrix core is busy; the loads of k-step t+3 into dma_stage ride on the
+// first matrix instructions of the k-step the same way.  LDS reads are issued a whole half k-step before
 // their data is decoded; the scales of the next k-step are split during
 // chunk 5.
 template <int TM, int TN>
 __device__ __forceinline__ void kstep(float16v (&acc)[TM][TN], Frags<TM, TN> (&f)[2], Scales<TM, TN>& sc,
                                       Chunk<TM, TN> (&d)[2], const uint8_t* cur, const uint8_t* nxt, int wm, int wn,
-                                      int lane) {
+                                      int lane, uint8_t* dma_stage, const TileSrc& src, uint32_t dma_ks, bool dma_live,
+                                      int wave) {
     constexpr int kMma = TM * TN, kPieces = 2 * (TM + TN), kOps = TM + TN;
+    constexpr int kLoads = DmaPlan<TM, TN>::kLoads;
     static_assert(kPieces % kMma == 0 || kMma % kPieces == 0, "pieces must spread evenly");
     RawScales<TM, TN> raw;
     Scales<TM, TN> nsc;
@@ -255,6 +271,7 @@ __device__ __forceinline__ void kstep(float16v (&acc)[TM][TN], Frags<TM, TN> (&f
         for (int m = 0; m < kMma; ++m) {
             const int i = m / TN, j = m % TN;
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(d[q & 1].a[i], d[q & 1].b[j], acc[i][j], 0, 0, 0);
+            if (q * kMma + m < kLoads) dma_one<TM, TN>(dma_stage, src, dma_ks, dma_live, wave, q * kMma + m);
             if (q == 5 && m < kOps) {
                 if (m < TM) nsc.a[m] = split_scales(raw.a[m]);
                 else nsc.b[m - TM] = split_scales(raw.b[m - TM]);
@@ -268,44 +285,41 @@ __device__ __forceinline__ void kstep(float16v (&acc)[TM][TN], Frags<TM, TN> (&f
     sc = nsc;
 }
 
-template <int TM, int TN>
-__global__ __launch_bounds__(256) void gemm_tile_kernel(int64_t M, const uint8_t* __restrict__ a_codes,
-                                                        const uint8_t* __restrict__ a_scales,
-                                                        const float* __restrict__ g_x,
-                                                        const uint8_t* __restrict__ w_codes,
-                                                        const uint8_t* __restrict__ w_scales,
-                                                        const float* __restrict__ colscale, int64_t N,
-                                                        int64_t n_pad, int64_t K, float* __restrict__ y,
-                                                        int64_t ld_y, int tiles_m, int tiles_n) {
-    using G = TileGeom<TM, TN>;
-    // Four separate arrays rather than one: the compiler then tells the stages
-    // apart and waits only for the loads that target the stage being read.
-    __shared__ __attribute__((aligned(16))) uint8_t st0[G::STAGE];
-    __shared__ __attribute__((aligned(16))) uint8_t st1[G::STAGE];
-    __shared__ __attribute__((aligned(16))) uint8_t st2[G::STAGE];
-    __shared__ __attribute__((aligned(16))) uint8_t st3[G::STAGE];
-    uint8_t* const stg[4] = {st0, st1, st2, st3};
-
-    // hardware id -> logical id: the workgroups of one XCD get consecutive logical ids
-    const int nwg = tiles_m * tiles_n;
-    const int hw = blockIdx.x;
-    const int per_xcd = (nwg + kXcds - 1) / kXcds;
-    const int full = nwg - (per_xcd - 1) * kXcds;   // XCDs that get per_xcd workgroups
+// ---------------------------------------------------------------------------
+// Work split: one workgroup per output tile, 256 x 256 (one workgroup per
+// compute unit: 147 KB of LDS, all 512 registers of each SIMD) or 128 x 128
+// (two per compute unit).  The host picks the shape that finishes first,
+// counting rounds of workgroups over the compute units: small products get
+// the small tiles, so that more compute units have work.  Every output element
+// sums its k-steps in the same order with either shape, so the choice never
+// changes a result.
+// ---------------------------------------------------------------------------
+// logical workgroup id: the workgroups of one XCD (hardware ids go round-robin
+// over the XCDs) get consecutive logical ids
+__device__ __forceinline__ int xcd_order(int hw, int n) {
+    const int per_xcd = (n + kXcds - 1) / kXcds;
+    const int full = n - (per_xcd - 1) * kXcds;   // XCDs that get per_xcd workgroups
     const int xcd = hw % kXcds, slot = hw / kXcds;
-    const int lid = (xcd < full ? xcd * per_xcd : full * per_xcd + (xcd - full) * (per_xcd - 1)) + slot;
-    // grouped order: kGroupM tile rows at a time, column-major inside the group
+    return (xcd < full ? xcd * per_xcd : full * per_xcd + (xcd - full) * (per_xcd - 1)) + slot;
+}
+
+// Tile lid in grouped order: kGroupM tile rows at a time, column-major inside the group.
+__device__ __forceinline__ void tile_coords(int lid, int tiles_m, int tiles_n, int& tm, int& tn) {
     const int group = lid / (kGroupM * tiles_n);
     const int first_m = group * kGroupM;
     const int gm = min(tiles_m - first_m, kGroupM);
     const int in_group = lid - group * kGroupM * tiles_n;
-    const int tm = first_m + in_group % gm;
-    const int tn = in_group / gm;
+    tm = first_m + in_group % gm;
+    tn = in_group / gm;
+}
 
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int wm = wave >> 1, wn = wave & 1;
+// Per-lane and per-block source offsets (the per-tile ones are set by point_at).
+template <int TM, int TN>
+__device__ __forceinline__ TileSrc make_src(int64_t M, int64_t K, int64_t n_pad, const uint8_t* a_codes,
+                                            const uint8_t* a_scales, const uint8_t* w_codes, const uint8_t* w_scales,
+                                            int lane) {
     const int l32 = lane & 31, h = lane >> 5;
     const uint32_t KS = (uint32_t)(K / kPackK);
-
     TileSrc s;
     s.ac = make_rsrc(a_codes, (uint64_t)M * K / 2);        // rows >= M read as zero
     s.as = make_rsrc(a_scales, (uint64_t)M * K / 16);
@@ -319,12 +333,24 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(int64_t M, const uint8_t
     s.as_blk = 32 * (uint32_t)(K / 16);
     s.b_blk = 2 * KS * 1024;     // 32 columns = two 16-row packed blocks
     s.bs_blk = 2 * KS * 128;
-    s.a_tile = (uint32_t)tm * G::RB * s.a_blk;
-    s.as_tile = (uint32_t)tm * G::RB * s.as_blk;
-    s.b_tile = (uint32_t)tn * G::CB * s.b_blk;
-    s.bs_tile = (uint32_t)tn * G::CB * s.bs_blk;
+    return s;
+}
+// Source offsets of tile (tm, tn) starting at k-step k0.
+template <int TM, int TN>
+__device__ __forceinline__ void point_at(TileSrc& s, int tm, int tn, uint32_t k0) {
+    using G = TileGeom<TM, TN>;
+    s.a_tile = (uint32_t)tm * G::RB * s.a_blk + k0 * 64;
+    s.as_tile = (uint32_t)tm * G::RB * s.as_blk + k0 * 8;
+    s.b_tile = (uint32_t)tn * G::CB * s.b_blk + k0 * 1024;
+    s.bs_tile = (uint32_t)tn * G::CB * s.bs_blk + k0 * 128;
+}
 
-    float16v acc[TM][TN];
+// Multiply one tile over nsteps k-steps (the source offsets already point at
+// the first one) into acc.  On return no load is in flight and every
+// wavefront is past its last LDS read.
+template <int TM, int TN>
+__device__ __forceinline__ void tile_product(float16v (&acc)[TM][TN], uint8_t* const (&stg)[4], const TileSrc& s,
+                                             uint32_t nsteps, int wave, int wm, int wn, int lane) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -334,10 +360,10 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(int64_t M, const uint8_t
 
     // Ring invariant at the top of k-step t: k-steps up to t+1 are in LDS and
     // visible to every wavefront, k-step t+2 is in flight.
-    constexpr int kLoadsPerStep = G::A_CHUNKS + G::B_CHUNKS + G::AS_WORDS + G::BS_WORDS;
+    constexpr int kLoadsPerStep = DmaPlan<TM, TN>::kLoads;
     stage_dma<TM, TN>(stg[0], s, 0, true, wave);
-    stage_dma<TM, TN>(stg[1], s, 1, KS > 1, wave);
-    stage_dma<TM, TN>(stg[2], s, 2, KS > 2, wave);
+    stage_dma<TM, TN>(stg[1], s, 1, nsteps > 1, wave);
+    stage_dma<TM, TN>(stg[2], s, 2, nsteps > 2, wave);
     wait_vmem<kLoadsPerStep>();
     __builtin_amdgcn_s_barrier();
 
@@ -354,19 +380,29 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(int64_t M, const uint8_t
     // The k-step count is rounded up to a multiple of 4 so the loop body has no
     // branches (the compiler's per-stage wait tracking does not survive them);
     // the extra k-steps load zeros (scale 0) and add nothing.
-    const uint32_t KS4 = (KS + 3) & ~3u;
-    for (uint32_t t0 = 0; t0 < KS4; t0 += 4) {
+    const uint32_t n4 = (nsteps + 3) & ~3u;
+    for (uint32_t t0 = 0; t0 < n4; t0 += 4) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const uint32_t t = t0 + u;
-            // stage (t+3)%4 was last read during k-step t-1, before the last barrier
-            stage_dma<TM, TN>(stg[(u + 3) & 3], s, t + 3, t + 3 < KS, wave);
-            kstep<TM, TN>(acc, f, sc, d, stg[u], stg[(u + 1) & 3], wm, wn, lane);
+            // stage (t+3)%4 was last read during k-step t-1, before the last barrier;
+            // kstep issues the loads of k-step t+3 into it
+            kstep<TM, TN>(acc, f, sc, d, stg[u], stg[(u + 1) & 3], wm, wn, lane, stg[(u + 3) & 3], s, t + 3,
+                          t + 3 < nsteps, wave);
             wait_vmem<kLoadsPerStep>();   // k-step t+2 has landed; t+3 may still be in flight
             __builtin_amdgcn_s_barrier();
         }
     }
+    wait_vmem<0>();   // the zero loads past the end, before the stages are reused
+}
 
+// Y = acc * g_x * colscale for one tile (rows >= M and columns >= N skipped).
+template <int TM, int TN>
+__device__ __forceinline__ void store_tile(const float16v (&acc)[TM][TN], int tm, int tn, int64_t M, int64_t N,
+                                           const float* __restrict__ g_x, const float* __restrict__ colscale,
+                                           float* __restrict__ y, int64_t ld_y, int wm, int wn, int lane) {
+    using G = TileGeom<TM, TN>;
+    const int l32 = lane & 31, h = lane >> 5;
     const float gx = g_x[0];
     const int64_t n0 = (int64_t)tn * G::BN + wn * (TN * 32) + l32;
 #pragma unroll
@@ -385,31 +421,75 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(int64_t M, const uint8_t
     }
 }
 
+#define NVFP4_TILE_KERNEL_ARGS                                                                                   \
+    int64_t M, const uint8_t *__restrict__ a_codes, const uint8_t *__restrict__ a_scales,                        \
+        const float *__restrict__ g_x, const uint8_t *__restrict__ w_codes, const uint8_t *__restrict__ w_scales, \
+        const float *__restrict__ colscale, int64_t N, int64_t n_pad, int64_t K, float *__restrict__ y,           \
+        int64_t ld_y
+
+// One whole tile per workgroup.
+template <int TM, int TN>
+__global__ __launch_bounds__(256) void gemm_tile_kernel(NVFP4_TILE_KERNEL_ARGS, int tiles_m, int tiles_n) {
+    using G = TileGeom<TM, TN>;
+    // Four separate arrays rather than one: the compiler then tells the stages
+    // apart and waits only for the loads that target the stage being read.
+    __shared__ __attribute__((aligned(16))) uint8_t st0[G::STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t st1[G::STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t st2[G::STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t st3[G::STAGE];
+    uint8_t* const stg[4] = {st0, st1, st2, st3};
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int wm = wave >> 1, wn = wave & 1;
+
+    int tm, tn;
+    tile_coords(xcd_order(blockIdx.x, tiles_m * tiles_n), tiles_m, tiles_n, tm, tn);
+    TileSrc s = make_src<TM, TN>(M, K, n_pad, a_codes, a_scales, w_codes, w_scales, lane);
+    point_at<TM, TN>(s, tm, tn, 0);
+    float16v acc[TM][TN];
+    tile_product<TM, TN>(acc, stg, s, (uint32_t)(K / kPackK), wave, wm, wn, lane);
+    store_tile<TM, TN>(acc, tm, tn, M, N, g_x, colscale, y, ld_y, wm, wn, lane);
+}
+
+// Host side.  Time per round of workgroups, relative: a round of 128 x 128
+// tiles (two per compute unit) takes about 0.53 of a round of 256 x 256 tiles
+// (measured on MI355X over K = 4096; the ratio barely moves with K).
+constexpr int kTileRoundsSmall = 53, kTileRoundsLarge = 100;
+
+static bool small_tiles(int64_t M, const nvfp4_weight_desc& d) {
+    if (M <= 128) return true;
+    const int64_t big = ((M + 255) / 256) * (d.n_padded / 256), small = ((M + 127) / 128) * (d.n_padded / 128);
+    const int64_t rounds_big = (big + kComputeUnits - 1) / kComputeUnits;
+    const int64_t rounds_small = (small + 2 * kComputeUnits - 1) / (2 * kComputeUnits);
+    return rounds_small * kTileRoundsSmall < rounds_big * kTileRoundsLarge;
+}
+
 size_t gemm_workspace_bytes(int64_t M, const nvfp4_weight_desc& d) {
     return skinny_applies(M, d) ? skinny_workspace_bytes(d) : 0;
 }
 
-hipError_t launch_gemm(int64_t M, const uint8_t* a_codes, const uint8_t* a_scales, const float* g_x,
-                       const nvfp4_weight_desc& d, float* y, int64_t ld_y, void* ws, size_t, hipStream_t stream) {
+template <int TM, int TN>
+static hipError_t launch_tiles(int64_t M, const uint8_t* a_codes, const uint8_t* a_scales, const float* g_x,
+                               const nvfp4_weight_desc& d, float* y, int64_t ld_y, hipStream_t stream) {
+    constexpr int BM = 64 * TM, BN = 64 * TN;
     const uint8_t* blob = static_cast<const uint8_t*>(d.blob);
     const uint8_t* wc = blob + d.codes_offset;
     const uint8_t* wsc = blob + d.scales_offset;
     const float* cs = reinterpret_cast<const float*>(blob + d.colscale_offset);
+    const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)(d.n_padded / BN);
+    hipLaunchKernelGGL((gemm_tile_kernel<TM, TN>), dim3(tiles_m * tiles_n), dim3(256), 0, stream, M, a_codes,
+                       a_scales, g_x, wc, wsc, cs, d.n, d.n_padded, d.k, y, ld_y, tiles_m, tiles_n);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm(int64_t M, const uint8_t* a_codes, const uint8_t* a_scales, const float* g_x,
+                       const nvfp4_weight_desc& d, float* y, int64_t ld_y, void* ws, size_t, hipStream_t stream) {
     if (skinny_applies(M, d)) {
         return launch_skinny(M, nullptr, NVFP4_IN_BF16, 0, const_cast<float*>(g_x), NVFP4_G_GIVEN,
                              const_cast<uint8_t*>(a_codes), const_cast<uint8_t*>(a_scales), false, d, y, ld_y, ws,
                              stream);
     }
-    if (M <= 128) {
-        const int tiles_m = (int)((M + 127) / 128), tiles_n = (int)(d.n_padded / 128);
-        hipLaunchKernelGGL((gemm_tile_kernel<2, 2>), dim3(tiles_m * tiles_n), dim3(256), 0, stream, M, a_codes,
-                           a_scales, g_x, wc, wsc, cs, d.n, d.n_padded, d.k, y, ld_y, tiles_m, tiles_n);
-    } else {
-        const int tiles_m = (int)((M + 255) / 256), tiles_n = (int)(d.n_padded / 256);
-        hipLaunchKernelGGL((gemm_tile_kernel<4, 4>), dim3(tiles_m * tiles_n), dim3(256), 0, stream, M, a_codes,
-                           a_scales, g_x, wc, wsc, cs, d.n, d.n_padded, d.k, y, ld_y, tiles_m, tiles_n);
-    }
-    return hipGetLastError();
+    return small_tiles(M, d) ? launch_tiles<2, 2>(M, a_codes, a_scales, g_x, d, y, ld_y, stream)
+                             : launch_tiles<4, 4>(M, a_codes, a_scales, g_x, d, y, ld_y, stream);
 }
 
 }  // namespace nvfp4

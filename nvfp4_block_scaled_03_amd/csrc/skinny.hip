@@ -385,7 +385,6 @@ struct SkinnyPlan {
 
 const int kROptions[] = {4, 5, 8};
 const int kNkslOptions[] = {16, 10, 8, 5, 4, 2, 1};
-constexpr int kComputeUnits = 256;
 
 // The split whose workgroups spread most evenly over the compute units (each
 // unit's share of the weight stream sets its finishing time); ties go to fewer

@@ -76,6 +76,29 @@ def test_tiled_short_and_odd_k(M, K):
     check_dense(x, "bf16", ws, "bf16", f"tiled M={M} K={K}")
 
 
+@pytest.mark.parametrize("M,N,K", [(300, 700, 2048), (100, 700, 2048), (300, 700, 640), (160, 1000, 5120),
+                                   (1000, 600, 1024)])
+def test_medium_shapes(M, N, K):
+    """Ragged shapes between the few-token kernel and the big-tile regime (small tiles, partial row and
+    column tiles, several k-steps)."""
+    x = workloads.random_matrix(900 + M + K, M, K, dtype="bf16")
+    ws = [workloads.random_matrix(950 + N + K, N, K, 0.05, dtype="bf16")]
+    check_dense(x, "bf16", ws, "bf16", f"medium M={M} N={N} K={K}")
+
+
+def test_repeat_calls_deterministic():
+    """Repeated calls agree bit for bit."""
+    x = workloads.random_matrix(990, 160, 5120, dtype="bf16")
+    ws = [workloads.random_matrix(991, 1000, 5120, 0.05, dtype="bf16")]
+    say("gemm determinism M=160 N=1000 K=5120")
+    xc, xs, gx = nv.quantize(to_dev(x, "bf16"))
+    pw = nv.PackedWeight([nv.quantize(to_dev(w, "bf16")) for w in ws], 5120)
+    ys = [nv.gemm(xc, xs, gx, pw) for _ in range(4)]
+    torch.cuda.synchronize()
+    for t in ys[1:]:
+        assert torch.equal(t, ys[0])
+
+
 def test_fused_module_mix_skinny():
     x = workloads.random_matrix(501, 7, 512, dtype="bf16")
     ws = [workloads.random_matrix(502 + i, r, 512, s, dtype="bf16")
@@ -131,13 +154,33 @@ def test_workload_sampled(name):
 
 
 def test_fused_equals_per_module():
-    """One fused GEMM over stacked sub-modules = the per-module GEMMs side by side, bit for bit."""
+    """One fused GEMM over stacked sub-modules = the per-module GEMMs side by side, bit for bit (every output
+    sums its k-steps in the same order whatever the tile shape and count), and both within the oracle's bound."""
     wl = workloads.make_gdn(M=96)
     say("gemm fused == per-module concat")
     y, (xc, xs, gx), mods, _ = gpu_linear(wl.x, "bf16", wl.w, "bf16")
     parts = [nv.gemm(xc, xs, gx, nv.PackedWeight([m], wl.K)) for m in mods]
     torch.cuda.synchronize()
     assert torch.equal(y, torch.cat(parts, dim=1))
+    xq = ref.quantize(wl.x, "compute")
+    wq = [ref.quantize(w, "compute") for w in wl.w]
+    y_ref, a_ref = ref.gemm(xq, wq)
+    ok, worst = ref.gemm_within_tolerance(host(y), y_ref, a_ref)
+    assert ok, f"worst |dy|/sum|terms| = {worst:.3e}"
+
+
+def test_tile_shape_does_not_change_results():
+    """8192 rows run on 256 x 256 tiles; their first 256 rows alone run on 128 x 128 tiles.  The rows agree
+    bit for bit."""
+    x = workloads.random_matrix(1201, 8192, 1024, dtype="bf16")
+    ws = [workloads.random_matrix(1202, 4096, 1024, 0.05, dtype="bf16")]
+    say("gemm tile shapes: M=8192 vs its first 256 rows, N=4096 K=1024")
+    xc, xs, gx = nv.quantize(to_dev(x, "bf16"))
+    pw = nv.PackedWeight([nv.quantize(to_dev(w, "bf16")) for w in ws], 1024)
+    y_all = nv.gemm(xc, xs, gx, pw)
+    y_top = nv.gemm(xc[:256].contiguous(), xs[:256].contiguous(), gx, pw)
+    torch.cuda.synchronize()
+    assert torch.equal(y_all[:256], y_top)
 
 
 def test_shared_scale_pitfall_is_detected():
