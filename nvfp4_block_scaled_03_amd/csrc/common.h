@@ -149,16 +149,41 @@ __device__ __forceinline__ float global_scale_from_amax(float amax) {
     return g < kGFloor ? kGFloor : g;
 }
 
-// Encode one 16-element block held in v[16].
-__device__ __forceinline__ void encode_block(const float v[16], float s_enc, uint32_t& lo, uint32_t& hi,
-                                             uint32_t& scale) {
-    float bamax = 0.0f;
+// fl32(t / 6) for t >= 0 without a division: q0 = fl32(t * fl32(1/6)), the
+// exact remainder t - 6*q0 by one fused multiply-add, and one more to correct
+// q0.  For every finite t >= 2^-124 this is the correctly rounded quotient
+// (all 2^31 non-negative floats checked on the CPU); below that the quotient
+// lies under 2^-126, far below the smallest nonzero E4M3 scale, so the scale
+// it leads to (0) is the same either way.
+__device__ __forceinline__ float div6(float t) {
+    const float c = 1.0f / 6.0f;
+    const float q0 = t * c;
+    const float r = __builtin_fmaf(-q0, 6.0f, t);
+    return __builtin_fmaf(r, c, q0);
+}
+
+// r = fl32(s_enc / S) for every scale byte S (0 for S = 0): 128 entries, one
+// correctly rounded division each, shared by all the blocks of a workgroup.
+// Threads tid, tid + nthreads, ... fill it; the caller synchronises before use.
+__device__ __forceinline__ void fill_recip_table(float* tab, float s_enc, int tid, int nthreads) {
+    for (int i = tid; i < 128; i += nthreads) tab[i] = (i == 0 || i > 0x7E) ? 0.0f : s_enc / e4m3_to_f32((uint32_t)i);
+}
+
+// max |v| over one 16-element block.
+__device__ __forceinline__ float block_amax(const float v[16]) {
+    float m = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) bamax = fmaxf(bamax, __builtin_fabsf(v[i]));
+    for (int i = 0; i < 16; ++i) m = fmaxf(m, __builtin_fabsf(v[i]));
+    return m;
+}
+
+// Encode one 16-element block held in v[16], whose max |v| is bamax, with the
+// tensor's s_enc and its table of s_enc / S.
+__device__ __forceinline__ void encode_block(const float v[16], float bamax, float s_enc, const float* rtab,
+                                             uint32_t& lo, uint32_t& hi, uint32_t& scale) {
     const float t = bamax * s_enc;
-    const float u = t / kE2M1Max;
-    const uint32_t S = e4m3_rne_sat(u);
-    const float r = (S == 0u) ? 0.0f : s_enc / e4m3_to_f32(S);
+    const uint32_t S = e4m3_rne_sat(div6(t));
+    const float r = rtab[S];
     float q[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) q[i] = v[i] * r;

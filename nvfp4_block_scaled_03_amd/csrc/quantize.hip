@@ -7,6 +7,7 @@
 //   2. encode: every workgroup reduces the partials itself (a few KB from L2),
 //      derives g and s_enc = fl32(1/g), and encodes 16-element blocks along K:
 //      bamax -> E4M3 scale of fl32(fl32(bamax*s_enc)/6) -> r = fl32(s_enc/S)
+//      (from a 128-entry table per workgroup)
 //      -> E2M1 code of fl32(x*r) per element -> two codes per byte.
 // The block structure and per-tensor scale follow "Why Gated DeltaNet Survives
 // 4-Bit Quantization" (sections "Why the 'Fragile' Recurrence is Actually
@@ -59,6 +60,7 @@ __global__ __launch_bounds__(kQThreads) void encode_kernel(const T* __restrict__
                                                            float* __restrict__ g_io, int g_given,
                                                            const float* __restrict__ partials, int n_partials) {
     __shared__ float s_senc;
+    __shared__ float rtab[128];
     if (g_given) {
         if (threadIdx.x == 0) s_senc = 1.0f / g_io[0];
         __syncthreads();
@@ -74,6 +76,8 @@ __global__ __launch_bounds__(kQThreads) void encode_kernel(const T* __restrict__
         __syncthreads();
     }
     const float s_enc = s_senc;
+    fill_recip_table(rtab, s_enc, threadIdx.x, kQThreads);
+    __syncthreads();
     const int64_t bpr = K / 16;                 // blocks per row
     const int64_t nblk = rows * bpr;
     const bool dense = (ld == K);
@@ -89,7 +93,7 @@ __global__ __launch_bounds__(kQThreads) void encode_kernel(const T* __restrict__
         load8(src, v);
         load8(src + 8, v + 8);
         uint32_t lo, hi, S;
-        encode_block(v, s_enc, lo, hi, S);
+        encode_block(v, block_amax(v), s_enc, rtab, lo, hi, S);
         *reinterpret_cast<uint2*>(codes + b * 8) = make_uint2(lo, hi);
         scales[b] = (uint8_t)S;
     }
@@ -141,12 +145,16 @@ __global__ __launch_bounds__(kSmallThreads) void quantize_small_kernel(const T* 
 #pragma unroll
     for (int i = 1; i < P; ++i)
         if ((int)blockIdx.x == i) mine = raw[i];
+    __shared__ float rtab[128];
+    const float s_enc = 1.0f / g;
+    fill_recip_table(rtab, s_enc, threadIdx.x, kSmallThreads);
+    __syncthreads();
     const int b = threadIdx.x + (int)blockIdx.x * kSmallThreads;
     if (b < nblk) {
         float v[16];
         widen(mine, v);
         uint32_t lo, hi, S;
-        encode_block(v, 1.0f / g, lo, hi, S);
+        encode_block(v, block_amax(v), s_enc, rtab, lo, hi, S);
         *reinterpret_cast<uint2*>(codes + (int64_t)b * 8) = make_uint2(lo, hi);
         scales[b] = (uint8_t)S;
     }

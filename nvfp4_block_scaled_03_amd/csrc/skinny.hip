@@ -88,6 +88,7 @@ __global__ __launch_bounds__(R * 64) void skinny_kernel(
     __shared__ float s_red[R];
     __shared__ float s_slotmax[kMaxSlices];
     __shared__ uint32_t s_ticket;
+    __shared__ float rtab[QUANT ? 128 : 1];
 
     const int grp = blockIdx.x / S, slice = blockIdx.x - grp * S;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -170,14 +171,15 @@ __global__ __launch_bounds__(R * 64) void skinny_kernel(
     const bool exchange = QUANT && !g_given;
     uint32_t* gslots = slots + (size_t)grp * S;
     float mine = 0.0f;
+    float bam[QUANT ? kBPT : 1];   // max |x| of each of this thread's blocks
     if (exchange) {
         float part = 0.0f;
 #pragma unroll
         for (int u = 0; u < (QUANT ? kBPT : 0); ++u) {
             float v[16];
             widen(raw[u], v);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) part = fmaxf(part, __builtin_fabsf(v[i]));
+            bam[u] = block_amax(v);
+            part = fmaxf(part, bam[u]);
         }
         mine = block_max_r<R>(part, s_red);
         if (S > 1 && threadIdx.x == 0)   // (sign bit set: a published word is never zero)
@@ -239,6 +241,13 @@ __global__ __launch_bounds__(R * 64) void skinny_kernel(
         if (blockIdx.x == 0 && threadIdx.x == 0) g_x[0] = gx;
     }
 
+    float s_enc = 0.0f;
+    if constexpr (QUANT) {
+        s_enc = 1.0f / gx;
+        fill_recip_table(rtab, s_enc, threadIdx.x, kThreads);
+        __syncthreads();
+    }
+
     // The activations of the slice, once per workgroup, as exact FP16 in LDS.
 #pragma unroll
     for (int u = 0; u < kBPT; ++u) {
@@ -250,7 +259,7 @@ __global__ __launch_bounds__(R * 64) void skinny_kernel(
             float v[16];
             widen(raw[u], v);
             uint32_t c_lo, c_hi, S8;
-            encode_block(v, 1.0f / gx, c_lo, c_hi, S8);
+            encode_block(v, exchange ? bam[u] : block_amax(v), s_enc, rtab, c_lo, c_hi, S8);
             const _Float16 s16 = e4m3_to_f16(S8);
             lo = decode8(c_lo, s16);
             hi = decode8(c_hi, s16);

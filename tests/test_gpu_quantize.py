@@ -92,6 +92,9 @@ EDGE_CASES = {
         [workloads.random_matrix(7, 4, 32) * F32(1e-7), workloads.random_matrix(8, 4, 32) * F32(40)], axis=1),
     "fp32_subnormals": lambda: workloads.random_matrix(9, 8, 64) * F32(1e-40),
     "huge": lambda: workloads.random_matrix(10, 8, 64) * F32(1e30),
+    "subnormal_blocks_in_normal_tensor": lambda: np.concatenate(
+        [workloads.random_matrix(16, 8, 32) * F32(1e-44), workloads.random_matrix(17, 8, 32) * F32(3e-39),
+         workloads.random_matrix(18, 8, 32)], axis=1),
     "g_floor": lambda: workloads.random_matrix(11, 8, 64) * F32(1e-36),
     "signed_zeros": lambda: np.tile(np.array([0.0, -0.0] * 8, F32), (2, 2)),
     "heavy_tail": lambda: (np.random.default_rng(12).standard_t(1.5, size=(64, 256)) * 10).astype(F32),
