@@ -58,14 +58,6 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t s) {
     return e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
 }
 
-// Two FP32 values -> one byte of E2M1 codes (first value in the low nibble).
-// The gfx950 conversion with a unit scale rounds to nearest with ties to the
-// even code, saturates at 6 and keeps the sign bit of values that round to 0;
-// that is the encoding rule used throughout, bit for bit.
-__device__ __forceinline__ uint32_t e2m1_pair(float lo, float hi) {
-    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, lo, hi, 1.0f, 0) & 0xFFu;
-}
-
 // E4M3 byte -> FP16 (exact).  Placing the 7 magnitude bits at FP16 bits 13..7
 // gives S * 2^-8 (FP16 subnormal for E4M3 subnormals); scaling by 2^8 is exact.
 __device__ __forceinline__ _Float16 e4m3_to_f16(uint32_t s) {
@@ -187,12 +179,19 @@ __device__ __forceinline__ void encode_block(const float v[16], float bamax, flo
     float q[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) q[i] = v[i] * r;
+    // Two elements per conversion, first in the low nibble; each writes one byte
+    // of the word and keeps the other three.  The gfx950 conversion with a unit
+    // scale rounds to nearest with ties to the even code, saturates at 6 and
+    // keeps the sign of values that round to 0: the encoding rule, bit for bit.
     uint32_t a = 0, b = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        a |= e2m1_pair(q[2 * i], q[2 * i + 1]) << (8 * i);
-        b |= e2m1_pair(q[8 + 2 * i], q[8 + 2 * i + 1]) << (8 * i);
-    }
+    a = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(a, q[0], q[1], 1.0f, 0);
+    a = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(a, q[2], q[3], 1.0f, 1);
+    a = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(a, q[4], q[5], 1.0f, 2);
+    a = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(a, q[6], q[7], 1.0f, 3);
+    b = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(b, q[8], q[9], 1.0f, 0);
+    b = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(b, q[10], q[11], 1.0f, 1);
+    b = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(b, q[12], q[13], 1.0f, 2);
+    b = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(b, q[14], q[15], 1.0f, 3);
     lo = a;
     hi = b;
     scale = S;
