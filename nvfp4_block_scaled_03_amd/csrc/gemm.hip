@@ -31,18 +31,20 @@ namespace nvfp4 {
 //
 // Operands move global -> LDS by buffer loads that write LDS directly (no
 // register staging), into a four-stage ring: the loads of k-step ks+3 are
-// issued at the start of k-step ks, so each has two k-steps to arrive.  The
+// issued during k-step ks, between its first matrix instructions, so each has
+// two k-steps to arrive.  The
 // wavefronts read their fragments one half k-step ahead (the second half of
 // ks while multiplying the first, the first half of ks+1 while multiplying the
 // second), and decode each 8-element chunk while the previous chunk's matrix
 // instructions run.  One barrier per k-step.  Each operand byte is fetched
 // once per workgroup.
 //
-// LDS stage layout (bytes), "lane" = l32 + 32*h of the consuming wavefront:
-//   A codes  [row block 8][half p 2][lane 64][16]  rows rb*32+l32, bytes h*32+p*16 of the k-step
-//   B codes  [col block 8][half p 2][lane 64][16]  packed unit kg = 2h+p of column cb*32+l32
-//   A scales [row block 8][lane 64][4]             block scales 4h..4h+3 of the row
-//   B scales [col block 8][lane 64][4]
+// LDS stage layout (bytes), "lane" = l32 + 32*h of the consuming wavefront,
+// RB = 2*TM row blocks and CB = 2*TN column blocks of 32:
+//   A codes  [row block RB][half p 2][lane 64][16]  rows rb*32+l32, bytes h*32+p*16 of the k-step
+//   B codes  [col block CB][half p 2][lane 64][16]  packed unit kg = 2h+p of column cb*32+l32
+//   A scales [row block RB][lane 64][4]             block scales 4h..4h+3 of the row
+//   B scales [col block CB][lane 64][4]
 // so every fragment read is one ds_read_b128 (or b32) of a contiguous,
 // bank-conflict-free 1 KB (256 B) span.
 //
