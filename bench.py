@@ -144,6 +144,16 @@ def main():
         nv.nvfp4_linear(x, codes, scales, g, weights[i % copies].desc, y, lin_ws, M=M, ld_x=K, in_dtype=in_dtype,
                         ld_y=N)
 
+    # the same layer without per-tensor scaling (the nGPT recipe): g given as 1, no amax pass
+    codes1, scales1, g1 = nv.empty_quantized(M, K, dev)
+    g1.fill_(1.0)
+    y1 = torch.empty((M, N), dtype=torch.float32, device=dev)
+    lin_ws1 = nv.linear_workspace(M, xdt, packed, dev)
+
+    def step_given(i):
+        nv.nvfp4_linear(x, codes1, scales1, g1, weights[i % copies].desc, y1, lin_ws1, nv.NVFP4_G_GIVEN, M=M, ld_x=K,
+                        in_dtype=in_dtype, ld_y=N)
+
     def gemm_only(i):
         nv.nvfp4_gemm(M, codes, scales, g, weights[i % copies].desc, y, N, gemm_ws)
 
@@ -199,6 +209,7 @@ def main():
     k_steps = max(steps, rot)
     t_gemm = timed(gemm_only, k_steps, min(warmup, k_steps)) / k_steps
     t_quant = timed(quant_only, k_steps, min(warmup, k_steps)) / k_steps
+    t_given = timed(step_given, k_steps, min(warmup, k_steps)) / k_steps
 
     flops = 2.0 * M * N * K
     tflops = flops / t_step / 1e12
@@ -244,6 +255,9 @@ def main():
     y_ref, a_ref = ref.gemm_dequantized(ref.dequantize(xq), np.concatenate(parts))
     yd = y[torch.from_numpy(rows).to(dev)][:, torch.from_numpy(cols).to(dev)].cpu().numpy()
     y_ok, worst = ref.gemm_within_tolerance(yd, y_ref, a_ref)
+    xq1 = ref.quantize(wl.x[rows], g_mode="given", g=1.0)
+    given_ok = bool(np.array_equal(codes1[torch.from_numpy(rows).to(dev)].cpu().numpy(), xq1.codes) and
+                    np.array_equal(scales1[torch.from_numpy(rows).to(dev)].cpu().numpy(), xq1.scales))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -268,9 +282,12 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "step_breakdown_us": {"step (nvfp4_linear)": t_step * 1e6, "launches_per_step": 1 if skinny else 3,
-                              "quantize alone": t_quant * 1e6, "gemm alone": t_gemm * 1e6},
+                              "quantize alone": t_quant * 1e6, "gemm alone": t_gemm * 1e6,
+                              "step with g given (no amax pass)": t_given * 1e6,
+                              "tflops with g given": flops / t_given / 1e12},
         "step_gbs": (x_in_bytes + w_bytes + x_q_bytes + M * N * 4) / t_step / 1e9,
         "parity": {"codes_scales_bit_exact": codes_ok, "gemm_within_1e-5": bool(y_ok), "worst_ratio": worst,
+                   "g_given_codes_scales_bit_exact": given_ok,
                    "rows_checked": int(len(rows)), "cols_checked": int(len(cols))},
     }
     print(json.dumps(out), flush=True)

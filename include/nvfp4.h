@@ -244,6 +244,42 @@ nvfp4_status nvfp4_linear(const void* x, int in_dtype, int64_t M, int64_t ld_x, 
                           uint8_t* x_scales, float* g_x, int g_mode, const nvfp4_weight_desc* w, float* y,
                           int64_t ld_y, void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Gate epilogue of a fused Gated DeltaNet input projection ("Why Gated
+ * DeltaNet Survives 4-Bit Quantization", section "The gates are shielded by
+ * their parameterization": the state decay is exp(-exp(A) * softplus(a + b))
+ * and the write strength a sigmoid).  The two small gate projections sit in
+ * the same fused weight as q, k, v, z; the epilogue turns their output columns
+ * into the gates as Y is written, so no second pass over Y is needed:
+ *
+ *   column a_col + h (0 <= h < n_a):  exp(-exp(a_log[h]) * softplus(y + dt_bias[h]))
+ *   column b_col + h (0 <= h < n_b):  1 / (1 + exp(-y))
+ *   every other column:               y unchanged (the same bits as without gates)
+ *
+ * y is the product's FP32 output (global scales applied); the gates are
+ * evaluated in FP32 (softplus and the sigmoid in their overflow-free forms).
+ * a_col, n_a, b_col, n_b: two disjoint column ranges inside [0, w->n), n >= 0
+ * a_log, dt_bias        : device, n_a FP32 values each (may be NULL when n_a == 0)
+ * ------------------------------------------------------------------------- */
+typedef struct nvfp4_gdn_gates {
+    int64_t a_col, n_a;
+    int64_t b_col, n_b;
+    const float* a_log;
+    const float* dt_bias;
+} nvfp4_gdn_gates;
+
+/* nvfp4_gemm / nvfp4_linear with the gate epilogue; same arguments, workspace
+ * sizes and behaviour otherwise.  NVFP4_ERR_INVALID_ARG for a NULL gates
+ * pointer or missing parameters, NVFP4_ERR_SHAPE for ranges outside [0, w->n)
+ * or overlapping. */
+nvfp4_status nvfp4_gemm_gated(int64_t M, const uint8_t* a_codes, const uint8_t* a_scales, const float* g_x,
+                              const nvfp4_weight_desc* w, const nvfp4_gdn_gates* gates, float* y, int64_t ld_y,
+                              void* workspace, size_t workspace_bytes, void* stream);
+nvfp4_status nvfp4_linear_gated(const void* x, int in_dtype, int64_t M, int64_t ld_x, uint8_t* x_codes,
+                                uint8_t* x_scales, float* g_x, int g_mode, const nvfp4_weight_desc* w,
+                                const nvfp4_gdn_gates* gates, float* y, int64_t ld_y, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -66,6 +66,29 @@ class WeightDesc(ctypes.Structure):
     ]
 
 
+class GdnGatesDesc(ctypes.Structure):
+    """Mirror of ``nvfp4_gdn_gates``."""
+    _fields_ = [
+        ("a_col", ctypes.c_int64),
+        ("n_a", ctypes.c_int64),
+        ("b_col", ctypes.c_int64),
+        ("n_b", ctypes.c_int64),
+        ("a_log", ctypes.c_void_p),
+        ("dt_bias", ctypes.c_void_p),
+    ]
+
+
+class GdnGates:
+    """Gate epilogue of a fused Gated DeltaNet projection: decay columns [a_col, a_col + n_a) become
+    exp(-exp(a_log[h]) * softplus(y + dt_bias[h])), write-strength columns [b_col, b_col + n_b) become
+    sigmoid(y).  a_log and dt_bias are FP32 device tensors of n_a values (kept alive by this object)."""
+
+    def __init__(self, a_col: int, n_a: int, b_col: int, n_b: int, a_log: torch.Tensor, dt_bias: torch.Tensor):
+        self.a_log = a_log.contiguous().float()
+        self.dt_bias = dt_bias.contiguous().float()
+        self.desc = GdnGatesDesc(a_col, n_a, b_col, n_b, self.a_log.data_ptr(), self.dt_bias.data_ptr())
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
@@ -89,6 +112,10 @@ def _load():
         "nvfp4_linear_workspace_bytes": (c_sz, [c_i64, c_int, ctypes.POINTER(WeightDesc)]),
         "nvfp4_linear": (c_int, [c_vp, c_int, c_i64, c_i64, c_vp, c_vp, c_vp, c_int, ctypes.POINTER(WeightDesc), c_vp,
                                  c_i64, c_vp, c_sz, c_vp]),
+        "nvfp4_gemm_gated": (c_int, [c_i64, c_vp, c_vp, c_vp, ctypes.POINTER(WeightDesc),
+                                     ctypes.POINTER(GdnGatesDesc), c_vp, c_i64, c_vp, c_sz, c_vp]),
+        "nvfp4_linear_gated": (c_int, [c_vp, c_int, c_i64, c_i64, c_vp, c_vp, c_vp, c_int, ctypes.POINTER(WeightDesc),
+                                       ctypes.POINTER(GdnGatesDesc), c_vp, c_i64, c_vp, c_sz, c_vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -185,12 +212,19 @@ def nvfp4_gemm_workspace_bytes(M: int, desc: WeightDesc) -> int:
     return _lib.nvfp4_gemm_workspace_bytes(M, ctypes.byref(desc))
 
 
-def nvfp4_gemm(M: int, a_codes, a_scales, g_x, desc: WeightDesc, y, ld_y=None, workspace=None, stream=None):
+def nvfp4_gemm(M: int, a_codes, a_scales, g_x, desc: WeightDesc, y, ld_y=None, workspace=None, stream=None,
+               gates: "GdnGates | None" = None):
+    """nvfp4_gemm, or nvfp4_gemm_gated when gates are given."""
     if ld_y is None:
         ld_y = y.stride(0) if y.dim() == 2 and y.shape[0] > 1 else desc.n
     ws_bytes = workspace.numel() * workspace.element_size() if isinstance(workspace, torch.Tensor) else 0
-    _check(_lib.nvfp4_gemm(M, _ptr(a_codes), _ptr(a_scales), _ptr(g_x), ctypes.byref(desc), _ptr(y), ld_y,
-                           _ptr(workspace), ws_bytes, _stream(stream)))
+    if gates is None:
+        _check(_lib.nvfp4_gemm(M, _ptr(a_codes), _ptr(a_scales), _ptr(g_x), ctypes.byref(desc), _ptr(y), ld_y,
+                               _ptr(workspace), ws_bytes, _stream(stream)))
+    else:
+        _check(_lib.nvfp4_gemm_gated(M, _ptr(a_codes), _ptr(a_scales), _ptr(g_x), ctypes.byref(desc),
+                                     ctypes.byref(gates.desc), _ptr(y), ld_y, _ptr(workspace), ws_bytes,
+                                     _stream(stream)))
 
 
 def nvfp4_linear_workspace_bytes(M: int, in_dtype: int, desc: WeightDesc) -> int:
@@ -198,8 +232,9 @@ def nvfp4_linear_workspace_bytes(M: int, in_dtype: int, desc: WeightDesc) -> int
 
 
 def nvfp4_linear(x, x_codes, x_scales, g_x, desc: WeightDesc, y, workspace, g_mode=NVFP4_G_COMPUTE, stream=None, *,
-                 M=None, ld_x=None, in_dtype=None, ld_y=None):
-    """Quantize x [M, K] and multiply by a packed weight in one call (workspace zero-filled before first use)."""
+                 M=None, ld_x=None, in_dtype=None, ld_y=None, gates: "GdnGates | None" = None):
+    """Quantize x [M, K] and multiply by a packed weight in one call (workspace zero-filled before first use);
+    nvfp4_linear_gated when gates are given."""
     if M is None:
         M = x.shape[0]
         ld_x = x.stride(0) if M > 1 else x.shape[1]
@@ -207,8 +242,13 @@ def nvfp4_linear(x, x_codes, x_scales, g_x, desc: WeightDesc, y, workspace, g_mo
     if ld_y is None:
         ld_y = y.stride(0) if y.dim() == 2 and y.shape[0] > 1 else desc.n
     ws_bytes = workspace.numel() * workspace.element_size()
-    _check(_lib.nvfp4_linear(_ptr(x), in_dtype, M, ld_x, _ptr(x_codes), _ptr(x_scales), _ptr(g_x), g_mode,
-                             ctypes.byref(desc), _ptr(y), ld_y, _ptr(workspace), ws_bytes, _stream(stream)))
+    if gates is None:
+        _check(_lib.nvfp4_linear(_ptr(x), in_dtype, M, ld_x, _ptr(x_codes), _ptr(x_scales), _ptr(g_x), g_mode,
+                                 ctypes.byref(desc), _ptr(y), ld_y, _ptr(workspace), ws_bytes, _stream(stream)))
+    else:
+        _check(_lib.nvfp4_linear_gated(_ptr(x), in_dtype, M, ld_x, _ptr(x_codes), _ptr(x_scales), _ptr(g_x), g_mode,
+                                       ctypes.byref(desc), ctypes.byref(gates.desc), _ptr(y), ld_y, _ptr(workspace),
+                                       ws_bytes, _stream(stream)))
 
 
 # ---------------------------------------------------------------------------
@@ -281,8 +321,9 @@ def linear_workspace(M: int, x_dtype, w: "PackedWeight", device="cuda") -> torch
     return torch.zeros((nvfp4_linear_workspace_bytes(M, in_dtype, w.desc),), dtype=torch.uint8, device=device)
 
 
-def linear(x: torch.Tensor, w: "PackedWeight", workspace=None, g=None, stream=None):
-    """Y = NVFP4(x) . W^T in one call; returns (y, codes, scales, g)."""
+def linear(x: torch.Tensor, w: "PackedWeight", workspace=None, g=None, stream=None, gates=None):
+    """Y = NVFP4(x) . W^T in one call (through the GDN gate epilogue when gates are given);
+    returns (y, codes, scales, g)."""
     M, K = x.shape
     codes, scales, gt = empty_quantized(M, K, x.device)
     if g is not None:
@@ -291,15 +332,15 @@ def linear(x: torch.Tensor, w: "PackedWeight", workspace=None, g=None, stream=No
         workspace = linear_workspace(M, x.dtype, w, x.device)
     y = torch.empty((M, w.n), dtype=torch.float32, device=x.device)
     nvfp4_linear(x, codes, scales, gt, w.desc, y, workspace, NVFP4_G_GIVEN if g is not None else NVFP4_G_COMPUTE,
-                 stream)
+                 stream, gates=gates)
     return y, codes, scales, gt
 
 
-def gemm(a_codes, a_scales, g_x, w: PackedWeight, y=None, stream=None):
+def gemm(a_codes, a_scales, g_x, w: PackedWeight, y=None, stream=None, gates=None):
     M = a_codes.shape[0]
     if y is None:
         y = torch.empty((M, w.n), dtype=torch.float32, device=a_codes.device)
     ws_bytes = nvfp4_gemm_workspace_bytes(M, w.desc)
     ws = torch.zeros((ws_bytes,), dtype=torch.uint8, device=a_codes.device) if ws_bytes else None
-    nvfp4_gemm(M, a_codes, a_scales, g_x, w.desc, y, None, ws, stream)
+    nvfp4_gemm(M, a_codes, a_scales, g_x, w.desc, y, None, ws, stream, gates=gates)
     return y

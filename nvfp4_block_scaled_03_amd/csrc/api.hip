@@ -218,9 +218,9 @@ size_t nvfp4_gemm_workspace_bytes(int64_t M, const nvfp4_weight_desc* w) {
     return nvfp4::gemm_workspace_bytes(M, *w);
 }
 
-nvfp4_status nvfp4_gemm(int64_t M, const uint8_t* a_codes, const uint8_t* a_scales, const float* g_x,
-                        const nvfp4_weight_desc* w, float* y, int64_t ld_y, void* workspace, size_t workspace_bytes,
-                        void* stream) {
+static nvfp4_status gemm_impl(int64_t M, const uint8_t* a_codes, const uint8_t* a_scales, const float* g_x,
+                              const nvfp4_weight_desc* w, const nvfp4::GateParams& gp, float* y, int64_t ld_y,
+                              void* workspace, size_t workspace_bytes, void* stream) {
     nvfp4_status st = check_desc(w);
     if (st != NVFP4_OK) return st;
     if (M < 0) return fail(NVFP4_ERR_SHAPE, "M must be >= 0 (got %lld)", (long long)M);
@@ -239,9 +239,49 @@ nvfp4_status nvfp4_gemm(int64_t M, const uint8_t* a_codes, const uint8_t* a_scal
                     workspace_bytes);
     st = check_device();
     if (st != NVFP4_OK) return st;
-    return launched(nvfp4::launch_gemm(M, a_codes, a_scales, g_x, *w, y, ld_y, workspace, workspace_bytes,
+    return launched(nvfp4::launch_gemm(M, a_codes, a_scales, g_x, *w, y, ld_y, workspace, workspace_bytes, gp,
                                        static_cast<hipStream_t>(stream)),
                     "gemm launch");
+}
+
+// Gate parameters -> the kernels' form, after checking them against the weight.
+static nvfp4_status gate_params(const nvfp4_gdn_gates* g, const nvfp4_weight_desc* w, nvfp4::GateParams& gp) {
+    if (g == nullptr) return fail(NVFP4_ERR_INVALID_ARG, "gates is NULL");
+    if (w == nullptr) return fail(NVFP4_ERR_INVALID_ARG, "w is NULL");
+    if (g->n_a < 0 || g->n_b < 0 || g->a_col < 0 || g->b_col < 0 || g->a_col > w->n - g->n_a ||
+        g->b_col > w->n - g->n_b)
+        return fail(NVFP4_ERR_SHAPE, "gate columns [%lld, +%lld) and [%lld, +%lld) must lie inside [0, %lld)",
+                    (long long)g->a_col, (long long)g->n_a, (long long)g->b_col, (long long)g->n_b, (long long)w->n);
+    if (g->n_a > 0 && g->n_b > 0 && g->a_col < g->b_col + g->n_b && g->b_col < g->a_col + g->n_a)
+        return fail(NVFP4_ERR_SHAPE, "decay and write-strength columns overlap");
+    if (g->n_a > 0 && (g->a_log == nullptr || g->dt_bias == nullptr))
+        return fail(NVFP4_ERR_INVALID_ARG, "a_log and dt_bias must be non-NULL when n_a > 0");
+    if (g->n_a > 0 && (!aligned(g->a_log, 4) || !aligned(g->dt_bias, 4)))
+        return fail(NVFP4_ERR_UNSUPPORTED, "a_log and dt_bias must be 4-byte aligned");
+    gp.a_col = (int32_t)g->a_col;   // < w->n < 2^31 (a packed weight holds at most 2 GiB of codes)
+    gp.n_a = (int32_t)g->n_a;
+    gp.b_col = (int32_t)g->b_col;
+    gp.n_b = (int32_t)g->n_b;
+    gp.a_log = g->a_log;
+    gp.dt_bias = g->dt_bias;
+    return NVFP4_OK;
+}
+
+nvfp4_status nvfp4_gemm(int64_t M, const uint8_t* a_codes, const uint8_t* a_scales, const float* g_x,
+                        const nvfp4_weight_desc* w, float* y, int64_t ld_y, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+    return gemm_impl(M, a_codes, a_scales, g_x, w, nvfp4::GateParams{}, y, ld_y, workspace, workspace_bytes, stream);
+}
+
+nvfp4_status nvfp4_gemm_gated(int64_t M, const uint8_t* a_codes, const uint8_t* a_scales, const float* g_x,
+                              const nvfp4_weight_desc* w, const nvfp4_gdn_gates* gates, float* y, int64_t ld_y,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+    nvfp4_status st = check_desc(w);
+    if (st != NVFP4_OK) return st;
+    nvfp4::GateParams gp;
+    st = gate_params(gates, w, gp);
+    if (st != NVFP4_OK) return st;
+    return gemm_impl(M, a_codes, a_scales, g_x, w, gp, y, ld_y, workspace, workspace_bytes, stream);
 }
 
 size_t nvfp4_linear_workspace_bytes(int64_t M, int in_dtype, const nvfp4_weight_desc* w) {
@@ -250,9 +290,10 @@ size_t nvfp4_linear_workspace_bytes(int64_t M, int in_dtype, const nvfp4_weight_
     return nvfp4::gemm_workspace_bytes(M, *w) + nvfp4_quantize_workspace_bytes(M, w->k);
 }
 
-nvfp4_status nvfp4_linear(const void* x, int in_dtype, int64_t M, int64_t ld_x, uint8_t* x_codes, uint8_t* x_scales,
-                          float* g_x, int g_mode, const nvfp4_weight_desc* w, float* y, int64_t ld_y,
-                          void* workspace, size_t workspace_bytes, void* stream) {
+static nvfp4_status linear_impl(const void* x, int in_dtype, int64_t M, int64_t ld_x, uint8_t* x_codes,
+                                uint8_t* x_scales, float* g_x, int g_mode, const nvfp4_weight_desc* w,
+                                const nvfp4::GateParams& gp, float* y, int64_t ld_y, void* workspace,
+                                size_t workspace_bytes, void* stream) {
     nvfp4_status st = check_desc(w);
     if (st != NVFP4_OK) return st;
     const int64_t K = w->k;
@@ -297,12 +338,32 @@ nvfp4_status nvfp4_linear(const void* x, int in_dtype, int64_t M, int64_t ld_x, 
                                               n_partials, s);
         if (e != hipSuccess) return fail(NVFP4_ERR_HIP, "linear quantize launch: %s", hipGetErrorString(e));
         if (M == 0) return ok();
-        return launched(nvfp4::launch_gemm(M, x_codes, x_scales, g_x, *w, y, ld_y, workspace, gemm_ws, s),
+        return launched(nvfp4::launch_gemm(M, x_codes, x_scales, g_x, *w, y, ld_y, workspace, gemm_ws, gp, s),
                         "linear gemm launch");
     }
     return launched(nvfp4::launch_skinny(M, x, in_dtype, ld_x, g_x, g_mode, x_codes, x_scales, true, *w, y, ld_y,
-                                         workspace, s),
+                                         workspace, gp, s),
                     "linear launch");
+}
+
+nvfp4_status nvfp4_linear(const void* x, int in_dtype, int64_t M, int64_t ld_x, uint8_t* x_codes, uint8_t* x_scales,
+                          float* g_x, int g_mode, const nvfp4_weight_desc* w, float* y, int64_t ld_y,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+    return linear_impl(x, in_dtype, M, ld_x, x_codes, x_scales, g_x, g_mode, w, nvfp4::GateParams{}, y, ld_y,
+                       workspace, workspace_bytes, stream);
+}
+
+nvfp4_status nvfp4_linear_gated(const void* x, int in_dtype, int64_t M, int64_t ld_x, uint8_t* x_codes,
+                                uint8_t* x_scales, float* g_x, int g_mode, const nvfp4_weight_desc* w,
+                                const nvfp4_gdn_gates* gates, float* y, int64_t ld_y, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+    nvfp4_status st = check_desc(w);
+    if (st != NVFP4_OK) return st;
+    nvfp4::GateParams gp;
+    st = gate_params(gates, w, gp);
+    if (st != NVFP4_OK) return st;
+    return linear_impl(x, in_dtype, M, ld_x, x_codes, x_scales, g_x, g_mode, w, gp, y, ld_y, workspace,
+                       workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -262,10 +262,37 @@ hipError_t launch_pack(const nvfp4_weight_desc& d, const uint8_t* const* codes,
 hipError_t launch_unpack(const nvfp4_weight_desc& d, uint8_t* codes, uint8_t* scales, float* colscale,
                          hipStream_t stream);
 
+// Gate epilogue of a fused Gated DeltaNet projection ("Why Gated DeltaNet
+// Survives 4-Bit Quantization", section "The gates are shielded by their
+// parameterization"): output columns [a_col, a_col + n_a) become the state
+// decay exp(-exp(A) * softplus(y + bias)) of their head, columns
+// [b_col, b_col + n_b) the write strength sigmoid(y).  The kernels take it as a
+// compile-time option, so products without gates carry none of it.
+struct GateParams {
+    int32_t a_col = 0, n_a = 0, b_col = 0, n_b = 0;   // columns fit 31 bits (the packed weight is <= 2 GiB)
+    const float* a_log = nullptr;
+    const float* dt_bias = nullptr;
+};
+
+// FP32, with softplus and the sigmoid in forms that cannot overflow.
+__device__ __forceinline__ float gate(float y, int64_t n, const GateParams& gp) {
+    const uint32_t ha = (uint32_t)((int32_t)n - gp.a_col), hb = (uint32_t)((int32_t)n - gp.b_col);
+    if (ha < (uint32_t)gp.n_a) {
+        const float z = y + gp.dt_bias[ha];
+        const float sp = z > 0.0f ? z + log1pf(expf(-z)) : log1pf(expf(z));
+        return expf(-(expf(gp.a_log[ha]) * sp));
+    }
+    if (hb < (uint32_t)gp.n_b) {
+        const float e = expf(-__builtin_fabsf(y));
+        return y >= 0.0f ? 1.0f / (1.0f + e) : e / (1.0f + e);
+    }
+    return y;
+}
+
 size_t gemm_workspace_bytes(int64_t M, const nvfp4_weight_desc& d);
 hipError_t launch_gemm(int64_t M, const uint8_t* a_codes, const uint8_t* a_scales, const float* g_x,
                        const nvfp4_weight_desc& d, float* y, int64_t ld_y, void* ws, size_t ws_bytes,
-                       hipStream_t stream);
+                       const GateParams& gp, hipStream_t stream);
 
 // Few-token products (skinny.hip).  The workspace starts with one 32-bit counter
 // per 64-row weight group, which must be zero before first use (each call
@@ -274,6 +301,6 @@ bool skinny_applies(int64_t M, const nvfp4_weight_desc& d);
 size_t skinny_workspace_bytes(const nvfp4_weight_desc& d);
 hipError_t launch_skinny(int64_t M, const void* x, int in_dtype, int64_t ld_x, float* g_x, int g_mode,
                          uint8_t* x_codes, uint8_t* x_scales, bool quantize, const nvfp4_weight_desc& d, float* y,
-                         int64_t ld_y, void* ws, hipStream_t stream);
+                         int64_t ld_y, void* ws, const GateParams& gp, hipStream_t stream);
 
 }  // namespace nvfp4

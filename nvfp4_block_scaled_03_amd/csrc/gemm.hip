@@ -398,11 +398,13 @@ __device__ __forceinline__ void tile_product(float16v (&acc)[TM][TN], uint8_t* c
     wait_vmem<0>();   // the zero loads past the end, before the stages are reused
 }
 
-// Y = acc * g_x * colscale for one tile (rows >= M and columns >= N skipped).
-template <int TM, int TN>
+// Y = acc * g_x * colscale for one tile (rows >= M and columns >= N skipped),
+// through the gate epilogue.
+template <int TM, int TN, bool GATED>
 __device__ __forceinline__ void store_tile(const float16v (&acc)[TM][TN], int tm, int tn, int64_t M, int64_t N,
                                            const float* __restrict__ g_x, const float* __restrict__ colscale,
-                                           float* __restrict__ y, int64_t ld_y, int wm, int wn, int lane) {
+                                           float* __restrict__ y, int64_t ld_y, const GateParams& gp, int wm, int wn,
+                                           int lane) {
     using G = TileGeom<TM, TN>;
     const int l32 = lane & 31, h = lane >> 5;
     const float gx = g_x[0];
@@ -417,7 +419,11 @@ __device__ __forceinline__ void store_tile(const float16v (&acc)[TM][TN], int tm
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int64_t m = (int64_t)tm * G::BM + wm * (TM * 32) + i * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
-                if (m < M) y[m * ld_y + n] = acc[i][j][r] * cs;
+                if (m < M) {
+                    float v = acc[i][j][r] * cs;
+                    if constexpr (GATED) v = gate(v, n, gp);
+                    y[m * ld_y + n] = v;
+                }
             }
         }
     }
@@ -430,8 +436,9 @@ __device__ __forceinline__ void store_tile(const float16v (&acc)[TM][TN], int tm
         int64_t ld_y
 
 // One whole tile per workgroup.
-template <int TM, int TN>
-__global__ __launch_bounds__(256) void gemm_tile_kernel(NVFP4_TILE_KERNEL_ARGS, int tiles_m, int tiles_n) {
+template <int TM, int TN, bool GATED>
+__global__ __launch_bounds__(256) void gemm_tile_kernel(NVFP4_TILE_KERNEL_ARGS, GateParams gp, int tiles_m,
+                                                        int tiles_n) {
     using G = TileGeom<TM, TN>;
     // Four separate arrays rather than one: the compiler then tells the stages
     // apart and waits only for the loads that target the stage being read.
@@ -449,7 +456,7 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(NVFP4_TILE_KERNEL_ARGS, 
     point_at<TM, TN>(s, tm, tn, 0);
     float16v acc[TM][TN];
     tile_product<TM, TN>(acc, stg, s, (uint32_t)(K / kPackK), wave, wm, wn, lane);
-    store_tile<TM, TN>(acc, tm, tn, M, N, g_x, colscale, y, ld_y, wm, wn, lane);
+    store_tile<TM, TN, GATED>(acc, tm, tn, M, N, g_x, colscale, y, ld_y, gp, wm, wn, lane);
 }
 
 // Host side.  Time per round of workgroups, relative: a round of 128 x 128
@@ -471,27 +478,30 @@ size_t gemm_workspace_bytes(int64_t M, const nvfp4_weight_desc& d) {
 
 template <int TM, int TN>
 static hipError_t launch_tiles(int64_t M, const uint8_t* a_codes, const uint8_t* a_scales, const float* g_x,
-                               const nvfp4_weight_desc& d, float* y, int64_t ld_y, hipStream_t stream) {
+                               const nvfp4_weight_desc& d, float* y, int64_t ld_y, const GateParams& gp,
+                               hipStream_t stream) {
     constexpr int BM = 64 * TM, BN = 64 * TN;
     const uint8_t* blob = static_cast<const uint8_t*>(d.blob);
     const uint8_t* wc = blob + d.codes_offset;
     const uint8_t* wsc = blob + d.scales_offset;
     const float* cs = reinterpret_cast<const float*>(blob + d.colscale_offset);
     const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)(d.n_padded / BN);
-    hipLaunchKernelGGL((gemm_tile_kernel<TM, TN>), dim3(tiles_m * tiles_n), dim3(256), 0, stream, M, a_codes,
-                       a_scales, g_x, wc, wsc, cs, d.n, d.n_padded, d.k, y, ld_y, tiles_m, tiles_n);
+    auto kern = (gp.n_a > 0 || gp.n_b > 0) ? gemm_tile_kernel<TM, TN, true> : gemm_tile_kernel<TM, TN, false>;
+    hipLaunchKernelGGL(kern, dim3(tiles_m * tiles_n), dim3(256), 0, stream, M, a_codes,
+                       a_scales, g_x, wc, wsc, cs, d.n, d.n_padded, d.k, y, ld_y, gp, tiles_m, tiles_n);
     return hipGetLastError();
 }
 
 hipError_t launch_gemm(int64_t M, const uint8_t* a_codes, const uint8_t* a_scales, const float* g_x,
-                       const nvfp4_weight_desc& d, float* y, int64_t ld_y, void* ws, size_t, hipStream_t stream) {
+                       const nvfp4_weight_desc& d, float* y, int64_t ld_y, void* ws, size_t, const GateParams& gp,
+                       hipStream_t stream) {
     if (skinny_applies(M, d)) {
         return launch_skinny(M, nullptr, NVFP4_IN_BF16, 0, const_cast<float*>(g_x), NVFP4_G_GIVEN,
                              const_cast<uint8_t*>(a_codes), const_cast<uint8_t*>(a_scales), false, d, y, ld_y, ws,
-                             stream);
+                             gp, stream);
     }
-    return small_tiles(M, d) ? launch_tiles<2, 2>(M, a_codes, a_scales, g_x, d, y, ld_y, stream)
-                             : launch_tiles<4, 4>(M, a_codes, a_scales, g_x, d, y, ld_y, stream);
+    return small_tiles(M, d) ? launch_tiles<2, 2>(M, a_codes, a_scales, g_x, d, y, ld_y, gp, stream)
+                             : launch_tiles<4, 4>(M, a_codes, a_scales, g_x, d, y, ld_y, gp, stream);
 }
 
 }  // namespace nvfp4

@@ -237,3 +237,29 @@ def test_linear_validation():
     assert call(d=None) == nv.NVFP4_ERR_INVALID_ARG
     if _no_gpu():
         assert call() == nv.NVFP4_ERR_NO_DEVICE
+
+
+def test_gated_validation():
+    """The gate epilogue's arguments are checked on the host before anything is launched."""
+    d = make_desc()          # n = sum of the module rows
+
+    def gg(a_col=0, n_a=4, b_col=8, n_b=4, a_log=FAKE, dt_bias=FAKE, gates=True):
+        g = nv.GdnGatesDesc(a_col, n_a, b_col, n_b, a_log, dt_bias)
+        return nv.lib.nvfp4_gemm_gated(32, FAKE, FAKE, FAKE, ctypes.byref(d), ctypes.byref(g) if gates else None,
+                                       FAKE, d.n, None, 0, None)
+    assert gg(gates=False) == nv.NVFP4_ERR_INVALID_ARG
+    assert gg(a_log=None) == nv.NVFP4_ERR_INVALID_ARG
+    assert gg(dt_bias=None) == nv.NVFP4_ERR_INVALID_ARG
+    assert gg(n_a=-1) == nv.NVFP4_ERR_SHAPE
+    assert gg(a_col=d.n - 2) == nv.NVFP4_ERR_SHAPE             # runs past the last column
+    assert gg(b_col=d.n) == nv.NVFP4_ERR_SHAPE
+    assert gg(b_col=2) == nv.NVFP4_ERR_SHAPE                   # overlaps the decay columns
+    assert gg(a_log=FAKE + 2) == nv.NVFP4_ERR_UNSUPPORTED
+    assert gg(n_a=0, a_log=None, dt_bias=None) != nv.NVFP4_ERR_INVALID_ARG   # no decay columns: no parameters
+    g = nv.GdnGatesDesc(0, 4, 8, 4, FAKE, FAKE)
+    assert nv.lib.nvfp4_linear_gated(FAKE, nv.NVFP4_IN_BF16, 16, d.k, FAKE, FAKE, FAKE, 0, ctypes.byref(d), None,
+                                     FAKE, d.n, FAKE, 1 << 30, None) == nv.NVFP4_ERR_INVALID_ARG
+    if _no_gpu():
+        assert gg() == nv.NVFP4_ERR_NO_DEVICE
+        assert nv.lib.nvfp4_linear_gated(FAKE, nv.NVFP4_IN_BF16, 16, d.k, FAKE, FAKE, FAKE, 0, ctypes.byref(d),
+                                         ctypes.byref(g), FAKE, d.n, FAKE, 1 << 30, None) == nv.NVFP4_ERR_NO_DEVICE

@@ -125,6 +125,34 @@ def make_gdn(seed: int = SEEDS["gdn"], M: int | None = None) -> Workload:
     return Workload("gdn", x, "bf16", ws, "bf16", [m for m, _ in mods])
 
 
+@dataclass
+class GdnGates:
+    """Parameters of the gate epilogue of the fused GDN projection: its decay columns
+    [a_col, a_col + n_a) and write-strength columns [b_col, b_col + n_b), and per decay
+    head the A parameter (entering as exp(A)) and the bias added inside the softplus."""
+    a_col: int
+    n_a: int
+    b_col: int
+    n_b: int
+    a_log: np.ndarray     # FP32 [n_a]
+    dt_bias: np.ndarray   # FP32 [n_a]
+
+
+def gdn_gate_params(seed: int = SEEDS["gdn"] + 1000, modules=None) -> GdnGates:
+    """A ~ log U(1, 16) per head (the usual initialisation of exp(A) in 1..16), bias ~ U(-6.9, -2.3)
+    (softplus of it spans the usual 1e-3..0.1 step sizes).  Columns: the a and b modules of
+    the fused projection (the 5th and 6th, after q, k, v, z)."""
+    mods = SHAPES["gdn"][2] if modules is None else modules
+    offs = np.cumsum([0] + [r for _, r in mods])
+    names = [m for m, _ in mods]
+    ia, ib = names.index("a"), names.index("b")
+    n_a = mods[ia][1]
+    c = np.random.SeedSequence(seed).spawn(2)
+    a_log = np.log(_rng(c[0]).uniform(1.0, 16.0, n_a)).astype(np.float32)
+    dt_bias = _rng(c[1]).uniform(-6.9, -2.3, n_a).astype(np.float32)
+    return GdnGates(int(offs[ia]), n_a, int(offs[ib]), mods[ib][1], a_log, dt_bias)
+
+
 def _hypersphere_rows(rng, rows, cols):
     z = rng.standard_normal((rows, cols))             # FP64
     z += 1e-3                                         # shared positive mean component
