@@ -154,6 +154,18 @@ def main():
         nv.nvfp4_linear(x, codes1, scales1, g1, weights[i % copies].desc, y1, lin_ws1, nv.NVFP4_G_GIVEN, M=M, ld_x=K,
                         in_dtype=in_dtype, ld_y=N)
 
+    # the GDN projection with its gate epilogue fused (decay and write-strength columns)
+    gate_p = workloads.gdn_gate_params() if name == "gdn" else None
+    if gate_p is not None:
+        gates = nv.GdnGates(gate_p.a_col, gate_p.n_a, gate_p.b_col, gate_p.n_b,
+                            torch.from_numpy(gate_p.a_log).to(dev), torch.from_numpy(gate_p.dt_bias).to(dev))
+        yg = torch.empty((M, N), dtype=torch.float32, device=dev)
+        codes_g, scales_g, g_g = nv.empty_quantized(M, K, dev)
+
+        def step_gated(i):
+            nv.nvfp4_linear(x, codes_g, scales_g, g_g, weights[i % copies].desc, yg, lin_ws, M=M, ld_x=K,
+                            in_dtype=in_dtype, ld_y=N, gates=gates)
+
     def gemm_only(i):
         nv.nvfp4_gemm(M, codes, scales, g, weights[i % copies].desc, y, N, gemm_ws)
 
@@ -210,6 +222,7 @@ def main():
     t_gemm = timed(gemm_only, k_steps, min(warmup, k_steps)) / k_steps
     t_quant = timed(quant_only, k_steps, min(warmup, k_steps)) / k_steps
     t_given = timed(step_given, k_steps, min(warmup, k_steps)) / k_steps
+    t_gated = timed(step_gated, k_steps, min(warmup, k_steps)) / k_steps if gate_p is not None else None
 
     flops = 2.0 * M * N * K
     tflops = flops / t_step / 1e12
@@ -255,6 +268,17 @@ def main():
     y_ref, a_ref = ref.gemm_dequantized(ref.dequantize(xq), np.concatenate(parts))
     yd = y[torch.from_numpy(rows).to(dev)][:, torch.from_numpy(cols).to(dev)].cpu().numpy()
     y_ok, worst = ref.gemm_within_tolerance(yd, y_ref, a_ref)
+    gated_ok, gated_worst = None, None
+    if gate_p is not None:   # gate columns of the sampled rows against the gate oracle
+        from oracle import gdn_gates as gref
+        ia, ib = wl.module_names.index("a"), wl.module_names.index("b")
+        wab = np.concatenate([ref.dequantize(ref.quantize(wl.w[ia])), ref.dequantize(ref.quantize(wl.w[ib]))])
+        yab, aab = ref.gemm_dequantized(ref.dequantize(xq), wab)
+        gargs = (0, gate_p.n_a, gate_p.b_col - gate_p.a_col, gate_p.n_b, gate_p.a_log.astype(np.float64),
+                 gate_p.dt_bias.astype(np.float64))
+        gcols = torch.arange(gate_p.a_col, gate_p.b_col + gate_p.n_b, device=dev)
+        got = yg[torch.from_numpy(rows).to(dev)][:, gcols].cpu().numpy()
+        gated_ok, gated_worst = gref.within(got, gref.apply_gates(yab, *gargs), gref.gates_tolerance(yab, aab, *gargs))
     xq1 = ref.quantize(wl.x[rows], g_mode="given", g=1.0)
     given_ok = bool(np.array_equal(codes1[torch.from_numpy(rows).to(dev)].cpu().numpy(), xq1.codes) and
                     np.array_equal(scales1[torch.from_numpy(rows).to(dev)].cpu().numpy(), xq1.scales))
@@ -284,10 +308,12 @@ def main():
         "step_breakdown_us": {"step (nvfp4_linear)": t_step * 1e6, "launches_per_step": 1 if skinny else 3,
                               "quantize alone": t_quant * 1e6, "gemm alone": t_gemm * 1e6,
                               "step with g given (no amax pass)": t_given * 1e6,
-                              "tflops with g given": flops / t_given / 1e12},
+                              "tflops with g given": flops / t_given / 1e12,
+                              "step with GDN gates fused": t_gated * 1e6 if t_gated else None},
         "step_gbs": (x_in_bytes + w_bytes + x_q_bytes + M * N * 4) / t_step / 1e9,
         "parity": {"codes_scales_bit_exact": codes_ok, "gemm_within_1e-5": bool(y_ok), "worst_ratio": worst,
                    "g_given_codes_scales_bit_exact": given_ok,
+                   "gdn_gates_within_bound": gated_ok, "gdn_gates_worst_ratio": gated_worst,
                    "rows_checked": int(len(rows)), "cols_checked": int(len(cols))},
     }
     print(json.dumps(out), flush=True)

@@ -274,6 +274,12 @@ struct GateParams {
     const float* dt_bias = nullptr;
 };
 
+// Whether any column of [n0, n1) is a gate column (wave-uniform when n0, n1 are).
+__device__ __forceinline__ bool gates_touch(int64_t n0, int64_t n1, const GateParams& gp) {
+    return (gp.n_a > 0 && n0 < gp.a_col + gp.n_a && gp.a_col < n1) ||
+           (gp.n_b > 0 && n0 < gp.b_col + gp.n_b && gp.b_col < n1);
+}
+
 // FP32, with softplus and the sigmoid in forms that cannot overflow.
 __device__ __forceinline__ float gate(float y, int64_t n, const GateParams& gp) {
     const uint32_t ha = (uint32_t)((int32_t)n - gp.a_col), hb = (uint32_t)((int32_t)n - gp.b_col);

@@ -398,13 +398,11 @@ __device__ __forceinline__ void tile_product(float16v (&acc)[TM][TN], uint8_t* c
     wait_vmem<0>();   // the zero loads past the end, before the stages are reused
 }
 
-// Y = acc * g_x * colscale for one tile (rows >= M and columns >= N skipped),
-// through the gate epilogue.
 template <int TM, int TN, bool GATED>
-__device__ __forceinline__ void store_tile(const float16v (&acc)[TM][TN], int tm, int tn, int64_t M, int64_t N,
-                                           const float* __restrict__ g_x, const float* __restrict__ colscale,
-                                           float* __restrict__ y, int64_t ld_y, const GateParams& gp, int wm, int wn,
-                                           int lane) {
+__device__ __forceinline__ void store_tile_cols(const float16v (&acc)[TM][TN], int tm, int tn, int64_t M, int64_t N,
+                                                const float* __restrict__ g_x, const float* __restrict__ colscale,
+                                                float* __restrict__ y, int64_t ld_y, const GateParams& gp, int wm,
+                                                int wn, int lane) {
     using G = TileGeom<TM, TN>;
     const int l32 = lane & 31, h = lane >> 5;
     const float gx = g_x[0];
@@ -427,6 +425,24 @@ __device__ __forceinline__ void store_tile(const float16v (&acc)[TM][TN], int tm
             }
         }
     }
+}
+
+// Y = acc * g_x * colscale for one tile (rows >= M and columns >= N skipped),
+// through the gate epilogue.
+template <int TM, int TN, bool GATED>
+__device__ __forceinline__ void store_tile(const float16v (&acc)[TM][TN], int tm, int tn, int64_t M, int64_t N,
+                                           const float* __restrict__ g_x, const float* __restrict__ colscale,
+                                           float* __restrict__ y, int64_t ld_y, const GateParams& gp, int wm, int wn,
+                                           int lane) {
+    using G = TileGeom<TM, TN>;
+    if constexpr (GATED) {
+        // only the tiles that hold gate columns take the gated stores
+        if (gates_touch((int64_t)tn * G::BN, (int64_t)(tn + 1) * G::BN, gp)) {
+            store_tile_cols<TM, TN, true>(acc, tm, tn, M, N, g_x, colscale, y, ld_y, gp, wm, wn, lane);
+            return;
+        }
+    }
+    store_tile_cols<TM, TN, false>(acc, tm, tn, M, N, g_x, colscale, y, ld_y, gp, wm, wn, lane);
 }
 
 #define NVFP4_TILE_KERNEL_ARGS                                                                                   \

@@ -298,13 +298,15 @@ __global__ __launch_bounds__(R * 64) void skinny_kernel(
 
     // Lane holds rows 4*kg..4*kg+3 of block nb for token r16.
     const int64_t n_base = (int64_t)nb * 16 + kg * 4;
+    bool gated = false;   // only the row blocks that hold gate columns take the gated stores
+    if constexpr (GATED) gated = gates_touch((int64_t)nb * 16, (int64_t)nb * 16 + 16, gp);
     if (S == 1) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int64_t n = n_base + r;
             if (r16 < M && n < N) {
                 float v = acc[r] * (gx * csv[r]);
-                if constexpr (GATED) v = gate(v, n, gp);
+                if (GATED && gated) v = gate(v, n, gp);
                 y[(int64_t)r16 * ld_y + n] = v;
             }
         }
@@ -374,7 +376,7 @@ __global__ __launch_bounds__(R * 64) void skinny_kernel(
         const int64_t n = n_base + r;
         if (r16 < M && n < N) {
             float v = sum[r] * (gx * csv[r]);
-            if constexpr (GATED) v = gate(v, n, gp);
+            if (GATED && gated) v = gate(v, n, gp);
             y[(int64_t)r16 * ld_y + n] = v;
         }
     }
