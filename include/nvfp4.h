@@ -118,6 +118,37 @@ nvfp4_status nvfp4_quantize(const void* x, int in_dtype, int64_t rows, int64_t K
                             void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Quantize along the other axis: unquantized [rows][cols] tensor x ->
+ * canonical NVFP4 encoding of its transpose x^T ([cols][rows], blocks of 16
+ * consecutive rows of x).
+ *
+ * End-to-end NVFP4 training ("Normalized Architectures are Natively 4-Bit",
+ * abstract and section "Approach") also runs the backward products in NVFP4:
+ * dX = dY * W contracts over W's rows and dW = dY^T * X over the token axis,
+ * so W, dY and X each need the encoding of their transpose.  The result is
+ * bit for bit nvfp4_quantize of x^T: same g (the amax does not depend on the
+ * orientation), same block rule, same per-element rule.
+ *
+ * x        : device, rows x cols elements of in_dtype, row r at x + r*ld_x;
+ *            aligned to the element size (rows that start on 16-byte
+ *            boundaries are read with vector loads, others element by element)
+ * rows     : >= 0, multiple of 16 (the blocked axis)
+ * cols     : >= 0 (rows == 0 or cols == 0: empty; g = 1 in COMPUTE mode)
+ * ld_x     : >= cols
+ * codes    : device, 8-byte aligned, cols * rows/2 bytes, written ([cols][rows/2])
+ * scales   : device, cols * rows/16 bytes, written ([cols][rows/16])
+ * g        : device, one float; written in COMPUTE mode, read in GIVEN mode
+ * workspace: device, >= nvfp4_quantize_workspace_bytes(rows, cols) bytes in
+ *            COMPUTE mode (may be NULL in GIVEN mode); no initialisation needed
+ * Errors: NVFP4_ERR_SHAPE for a bad rows/cols/ld_x, NVFP4_ERR_UNSUPPORTED for
+ * misaligned pointers or strides, NVFP4_ERR_WORKSPACE for a short workspace;
+ * nothing is launched then.
+ * ------------------------------------------------------------------------- */
+nvfp4_status nvfp4_quantize_t(const void* x, int in_dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                              uint8_t* codes, uint8_t* scales, float* g, int g_mode,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Packed weights.
  *
  * A projection is a stack of n_modules sub-modules (e.g. q,k,v,z,a,b of a

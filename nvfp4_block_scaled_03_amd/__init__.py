@@ -102,6 +102,7 @@ def _load():
         "nvfp4_device_check": (c_int, []),
         "nvfp4_quantize_workspace_bytes": (c_sz, [c_i64, c_i64]),
         "nvfp4_quantize": (c_int, [c_vp, c_int, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_int, c_vp, c_sz, c_vp]),
+        "nvfp4_quantize_t": (c_int, [c_vp, c_int, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_int, c_vp, c_sz, c_vp]),
         "nvfp4_packed_weight_bytes": (c_sz, [c_int, ctypes.POINTER(c_i64), c_i64]),
         "nvfp4_pack_weights": (c_int, [c_int, ctypes.POINTER(c_i64), c_i64, ctypes.POINTER(c_vp),
                                        ctypes.POINTER(c_vp), ctypes.POINTER(c_vp), c_vp, c_sz,
@@ -182,6 +183,21 @@ def nvfp4_quantize(x, codes, scales, g, g_mode=NVFP4_G_COMPUTE, workspace=None, 
     ws_bytes = workspace.numel() * workspace.element_size() if isinstance(workspace, torch.Tensor) else 0
     _check(_lib.nvfp4_quantize(_ptr(x), in_dtype, rows, K, ld_x, _ptr(codes), _ptr(scales), _ptr(g), g_mode,
                                _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def nvfp4_quantize_t(x, codes, scales, g, g_mode=NVFP4_G_COMPUTE, workspace=None, stream=None):
+    """Encode x^T: x [rows, cols] (float32 or bfloat16, rows a multiple of 16) into codes [cols, rows/2],
+    scales [cols, rows/16] and g."""
+    rows, cols = x.shape
+    if x.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("x must be float32 or bfloat16")
+    if cols > 1 and x.stride(-1) != 1:
+        raise ValueError("x must have unit stride along its columns")
+    ld_x = x.stride(0) if rows > 1 else cols
+    in_dtype = NVFP4_IN_BF16 if x.dtype == torch.bfloat16 else NVFP4_IN_F32
+    ws_bytes = workspace.numel() * workspace.element_size() if isinstance(workspace, torch.Tensor) else 0
+    _check(_lib.nvfp4_quantize_t(_ptr(x), in_dtype, rows, cols, ld_x, _ptr(codes), _ptr(scales), _ptr(g), g_mode,
+                                 _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def nvfp4_packed_weight_bytes(module_rows: Sequence[int], K: int) -> int:
@@ -276,6 +292,23 @@ def quantize(x: torch.Tensor, g=None, stream=None):
         else:
             gt.fill_(float(g))
         nvfp4_quantize(x, codes, scales, gt, NVFP4_G_GIVEN, None, stream)
+    return codes, scales, gt
+
+
+def quantize_t(x: torch.Tensor, g=None, stream=None):
+    """NVFP4 encoding of x^T for x [rows, cols]: codes [cols, rows/2], scales [cols, rows/16] and g
+    (computed from x's amax when g is None, otherwise the given value)."""
+    rows, cols = x.shape
+    codes, scales, gt = empty_quantized(cols, rows, x.device)
+    if g is None:
+        ws = torch.empty((max(nvfp4_quantize_workspace_bytes(rows, cols), 1),), dtype=torch.uint8, device=x.device)
+        nvfp4_quantize_t(x, codes, scales, gt, NVFP4_G_COMPUTE, ws, stream)
+    else:
+        if isinstance(g, torch.Tensor):
+            gt.copy_(g.reshape(1))
+        else:
+            gt.fill_(float(g))
+        nvfp4_quantize_t(x, codes, scales, gt, NVFP4_G_GIVEN, None, stream)
     return codes, scales, gt
 
 

@@ -161,6 +161,40 @@ nvfp4_status nvfp4_quantize(const void* x, int in_dtype, int64_t rows, int64_t K
                     "quantize launch");
 }
 
+nvfp4_status nvfp4_quantize_t(const void* x, int in_dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                              uint8_t* codes, uint8_t* scales, float* g, int g_mode, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+    if (in_dtype != NVFP4_IN_F32 && in_dtype != NVFP4_IN_BF16)
+        return fail(NVFP4_ERR_INVALID_ARG, "unknown input dtype %d", in_dtype);
+    if (g_mode != NVFP4_G_COMPUTE && g_mode != NVFP4_G_GIVEN)
+        return fail(NVFP4_ERR_INVALID_ARG, "unknown g mode %d", g_mode);
+    if (g == nullptr) return fail(NVFP4_ERR_INVALID_ARG, "g is NULL");
+    if (rows < 0 || cols < 0 || rows % 16 != 0)
+        return fail(NVFP4_ERR_SHAPE, "need cols >= 0 and rows >= 0 a multiple of 16 (rows=%lld cols=%lld)",
+                    (long long)rows, (long long)cols);
+    if (ld_x < cols) return fail(NVFP4_ERR_SHAPE, "ld_x (%lld) < cols (%lld)", (long long)ld_x, (long long)cols);
+    if (rows > 0 && ld_x > INT64_MAX / rows) return fail(NVFP4_ERR_SHAPE, "tensor too large");
+    const int esize = in_dtype == NVFP4_IN_BF16 ? 2 : 4;
+    if (rows > 0 && cols > 0) {
+        if (x == nullptr || codes == nullptr || scales == nullptr)
+            return fail(NVFP4_ERR_INVALID_ARG, "x, codes and scales must be non-NULL");
+        if (!aligned(x, esize)) return fail(NVFP4_ERR_UNSUPPORTED, "x must be aligned to its element size");
+        if (!aligned(codes, 8)) return fail(NVFP4_ERR_UNSUPPORTED, "codes must be 8-byte aligned");
+    }
+    const int n_partials = nvfp4::quantize_partials_count(rows, cols);
+    if (g_mode == NVFP4_G_COMPUTE && rows > 0 && cols > 0) {
+        const size_t need = nvfp4_quantize_workspace_bytes(rows, cols);
+        if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 4))
+            return fail(NVFP4_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+    }
+    nvfp4_status st = check_device();
+    if (st != NVFP4_OK) return st;
+    return launched(nvfp4::launch_quantize_t(x, in_dtype, rows, cols, ld_x, codes, scales, g, g_mode,
+                                             static_cast<float*>(workspace), n_partials,
+                                             static_cast<hipStream_t>(stream)),
+                    "quantize_t launch");
+}
+
 size_t nvfp4_packed_weight_bytes(int n_modules, const int64_t* module_rows, int64_t K) {
     nvfp4_weight_desc d;
     if (!blob_layout(n_modules, module_rows, K, &d)) return 0;

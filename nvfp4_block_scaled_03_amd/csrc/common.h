@@ -255,6 +255,9 @@ int quantize_partials_count(int64_t rows, int64_t K);
 hipError_t launch_quantize(const void* x, int in_dtype, int64_t rows, int64_t K, int64_t ld_x,
                            uint8_t* codes, uint8_t* scales, float* g, int g_mode,
                            float* partials, int n_partials, hipStream_t stream);
+hipError_t launch_quantize_t(const void* x, int in_dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                             uint8_t* codes, uint8_t* scales, float* g, int g_mode, float* partials, int n_partials,
+                             hipStream_t stream);
 
 hipError_t launch_pack(const nvfp4_weight_desc& d, const uint8_t* const* codes,
                        const uint8_t* const* scales, const float* const* g_w, uint8_t* blob,

@@ -27,9 +27,13 @@ constexpr int kMaxPartials = kMaxAmaxPartials;
 constexpr int kSegVec = 4;
 constexpr int64_t kSegElems = (int64_t)kQThreads * 8 * kSegVec;
 
+__device__ __forceinline__ float elem_f32(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
+__device__ __forceinline__ float elem_f32(float v) { return v; }
+
 template <typename T>
 __global__ __launch_bounds__(kQThreads) void amax_partials_kernel(const T* __restrict__ x, int64_t rows, int64_t K,
-                                                                  int64_t ld, float* __restrict__ partials) {
+                                                                  int64_t ld, float* __restrict__ partials,
+                                                                  int vec = 1) {
     // A contiguous tensor is one long row.
     if (ld == K) { K = rows * K; rows = 1; ld = K; }
     const int64_t seg_per_row = (K + kSegElems - 1) / kSegElems;
@@ -42,11 +46,14 @@ __global__ __launch_bounds__(kQThreads) void amax_partials_kernel(const T* __res
 #pragma unroll
         for (int u = 0; u < kSegVec; ++u) {
             const int64_t c = c0 + ((int64_t)u * kQThreads + threadIdx.x) * 8;
-            if (c < K) {
+            if (vec && c + 8 <= K) {
                 float v[8];
                 load8(row + c, v);
 #pragma unroll
                 for (int i = 0; i < 8; ++i) m = fmaxf(m, __builtin_fabsf(v[i]));
+            } else if (c < K) {          // x^T encoding only: row tails, or rows not 16-byte aligned
+                const int64_t e = c + 8 < K ? c + 8 : K;
+                for (int64_t i = c; i < e; ++i) m = fmaxf(m, __builtin_fabsf(elem_f32(row[i])));
             }
         }
     }
@@ -100,6 +107,88 @@ __global__ __launch_bounds__(kQThreads) void encode_kernel(const T* __restrict__
 }
 
 __global__ void write_unit_g_kernel(float* g) { g[0] = 1.0f; }
+
+// ---------------------------------------------------------------------------
+// The encoding of x^T (blocks of 16 consecutive rows of x, one output row per
+// column of x): the other operand orientation of the training GEMMs
+// (dX = dY.W needs W quantized along its rows, dW = dY^T.X needs dY and X
+// quantized along their rows).  Same global scale (the amax is the same), same
+// block rule.
+//
+// No LDS: each lane loads a 16-row x 16-byte patch of x (16 row vectors, all
+// in flight at once), which holds kVec whole blocks of x^T, one per column,
+// and encodes them from its registers.  A wavefront is 8 row groups x 8
+// column lanes, so each load instruction reads eight 128-byte row segments;
+// a workgroup of 4 wavefronts covers 512 rows x 8*kVec columns and writes,
+// per output row, 256 consecutive code bytes (two cache lines, merged in L2
+// from the 32 lanes that share the column).  Narrower segments measured
+// faster than 256- or 512-byte ones.
+// ---------------------------------------------------------------------------
+constexpr int kTLanesC = 8;                 // lanes across columns (128-byte row segments)
+constexpr int kTRows = 4 * (64 / kTLanesC) * 16;   // rows per workgroup tile (512)
+
+template <typename T>
+__global__ __launch_bounds__(kQThreads) void encode_t_kernel(const T* __restrict__ x, int64_t rows, int64_t cols,
+                                                             int64_t ld, uint8_t* __restrict__ codes,
+                                                             uint8_t* __restrict__ scales, float* __restrict__ g_io,
+                                                             int g_given, const float* __restrict__ partials,
+                                                             int n_partials, int vec) {
+    __shared__ float s_senc;
+    __shared__ float rtab[128];
+    if (g_given) {
+        if (threadIdx.x == 0) s_senc = 1.0f / g_io[0];
+    } else {
+        float m = 0.0f;
+        for (int i = threadIdx.x; i < n_partials; i += kQThreads) m = fmaxf(m, partials[i]);
+        m = block_max<kQThreads>(m);
+        if (threadIdx.x == 0) {
+            const float g = global_scale_from_amax(m);
+            s_senc = 1.0f / g;
+            if (blockIdx.x == 0) g_io[0] = g;
+        }
+    }
+    __syncthreads();
+    const float s_enc = s_senc;
+    fill_recip_table(rtab, s_enc, threadIdx.x, kQThreads);
+    __syncthreads();
+
+    constexpr int kVec = 16 / (int)sizeof(T);                 // columns per lane (one 16-byte vector)
+    constexpr int kRG = 64 / kTLanesC;                         // row groups per wavefront
+    constexpr int kTCols = kTLanesC * kVec;
+    const int64_t tiles_r = (rows + kTRows - 1) / kTRows, tiles_c = (cols + kTCols - 1) / kTCols;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int cl = lane % kTLanesC, rg = lane / kTLanesC;
+    for (int64_t tile_id = blockIdx.x; tile_id < tiles_r * tiles_c; tile_id += gridDim.x) {
+        // column-major tile order: workgroups launched together finish whole output rows
+        // (measured faster than row-major or grouped orders, whose reads are more sequential)
+        const int64_t tr = tile_id % tiles_r, tc = tile_id / tiles_r;
+        const int64_t r0 = tr * kTRows + (w * kRG + rg) * 16;       // this lane's 16 rows
+        const int64_t c0 = tc * kTCols + (int64_t)kVec * cl;        // and kVec columns
+        if (r0 >= rows || c0 >= cols) continue;
+        const T* src = x + r0 * ld + c0;
+        T e[16][kVec];
+        if (vec && c0 + kVec <= cols) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) *reinterpret_cast<uint4*>(e[i]) = *reinterpret_cast<const uint4*>(src + i * ld);
+        } else {                                 // ragged last columns or unaligned rows
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+#pragma unroll
+                for (int k = 0; k < kVec; ++k) e[i][k] = c0 + k < cols ? src[i * ld + k] : T(0);
+        }
+#pragma unroll
+        for (int k = 0; k < kVec; ++k) {
+            if (c0 + k >= cols) break;
+            float v[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) v[i] = elem_f32(e[i][k]);
+            uint32_t lo, hi, sc;
+            encode_block(v, block_amax(v), s_enc, rtab, lo, hi, sc);
+            *reinterpret_cast<uint2*>(codes + (c0 + k) * (rows / 2) + r0 / 2) = make_uint2(lo, hi);
+            scales[(c0 + k) * (rows / 16) + r0 / 16] = (uint8_t)sc;
+        }
+    }
+}
 
 // Small tensors (at most kSmallThreads * P blocks) in one launch: every one of
 // the P workgroups loads the whole tensor (thread t holds blocks t, t + 1024,
@@ -205,6 +294,39 @@ static int encode_grid(int64_t rows, int64_t K) {
     const int64_t cap = 256 * 16;  // ~16 workgroups per CU, the rest by grid stride
     if (wg > cap) wg = cap;
     return (int)(wg < 1 ? 1 : wg);
+}
+
+hipError_t launch_quantize_t(const void* x, int in_dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                             uint8_t* codes, uint8_t* scales, float* g, int g_mode, float* partials, int n_partials,
+                             hipStream_t stream) {
+    const int given = (g_mode == NVFP4_G_GIVEN);
+    if (rows == 0 || cols == 0) {
+        if (!given) hipLaunchKernelGGL(write_unit_g_kernel, dim3(1), dim3(1), 0, stream, g);
+        return hipGetLastError();
+    }
+    // 16-byte vector loads need an aligned base and (unless the tensor is dense) an aligned row stride
+    const int esize = in_dtype == NVFP4_IN_BF16 ? 2 : 4;
+    const int64_t tcols = kTLanesC * (16 / esize);
+    const int64_t tiles = ((rows + kTRows - 1) / kTRows) * ((cols + tcols - 1) / tcols);
+    const int grid = (int)(tiles < (1 << 24) ? tiles : (1 << 24));   // one tile per workgroup in practice
+    const int vec = (reinterpret_cast<uintptr_t>(x) % 16 == 0) && (ld_x == cols || (ld_x * esize) % 16 == 0);
+    const int vec_rows = (reinterpret_cast<uintptr_t>(x) % 16 == 0) && (ld_x * esize) % 16 == 0;
+    if (in_dtype == NVFP4_IN_BF16) {
+        const uint16_t* xp = static_cast<const uint16_t*>(x);
+        if (!given)
+            hipLaunchKernelGGL(amax_partials_kernel<uint16_t>, dim3(n_partials), dim3(kQThreads), 0, stream,
+                               xp, rows, cols, ld_x, partials, vec);
+hipLaunchKernelGGL(encode_t_kernel<uint16_t>, dim3(grid), dim3(kQThreads), 0, stream,
+                           xp, rows, cols, ld_x, codes, scales, g, given, partials, n_partials, vec_rows);
+    } else {
+        const float* xp = static_cast<const float*>(x);
+        if (!given)
+            hipLaunchKernelGGL(amax_partials_kernel<float>, dim3(n_partials), dim3(kQThreads), 0, stream,
+                               xp, rows, cols, ld_x, partials, vec);
+hipLaunchKernelGGL(encode_t_kernel<float>, dim3(grid), dim3(kQThreads), 0, stream,
+                           xp, rows, cols, ld_x, codes, scales, g, given, partials, n_partials, vec_rows);
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_quantize(const void* x, int in_dtype, int64_t rows, int64_t K, int64_t ld_x,

@@ -237,6 +237,18 @@ def quantize(x: np.ndarray, g_mode: str = "compute", g: float | None = None) -> 
     return Quantized(pack_nibbles(nib), S.astype(np.uint8), g32, nibbles=nib)
 
 
+def quantize_t(x: np.ndarray, g_mode: str = "compute", g: float | None = None) -> Quantized:
+    """NVFP4 encoding of x^T for x [rows, cols]: blocks of 16 consecutive rows of x.
+
+    The backward products of end-to-end NVFP4 training ("Normalized Architectures are
+    Natively 4-Bit", abstract and section "Approach") contract over the other axis of
+    their operands (dX = dY . W over W's rows, dW = dY^T . X over the tokens), so each
+    of those operands is quantized as its transpose.  Definition: ``quantize`` applied
+    to x^T (the amax, hence g, does not depend on the orientation).
+    """
+    return quantize(np.ascontiguousarray(np.asarray(x, dtype=F32).T), g_mode, g)
+
+
 def unpack_codes(codes: np.ndarray) -> np.ndarray:
     """uint8 [rows, K/2] -> one code per element [rows, K] (low nibble = even element)."""
     codes = np.asarray(codes, dtype=np.uint8)

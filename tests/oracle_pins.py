@@ -462,6 +462,55 @@ def check_tolerance_fn(ref):
     assert not ref.gemm_within_tolerance(y + [[0, 0, 1e-30]], y, a)[0]
 
 
+def check_transpose_columns(ref):
+    """The encoding of x^T, column by column: output row c is the row quantizer applied to column c of x
+    with the whole tensor's g (amax over every element, whatever the orientation)."""
+    rng = np.random.default_rng(31)
+    x = (rng.standard_normal((48, 7)) * np.exp(rng.uniform(-3, 3, (48, 7)))).astype(F32)
+    x[17, 3] = F32(-40.0)
+    qt = ref.quantize_t(x)
+    assert qt.codes.shape == (7, 24) and qt.scales.shape == (7, 3)
+    assert F32(qt.g).tobytes() == ref.global_scale(F32(40.0)).tobytes()
+    for c in range(7):
+        col = ref.quantize(x[:, c][None, :], "given", qt.g)
+        assert np.array_equal(col.codes[0], qt.codes[c]) and np.array_equal(col.scales[0], qt.scales[c])
+
+
+def _grid_matrix(rng, rows, cols, scale):
+    """Values on the E2M1 grid times one power of two, with a +-6 in every run of 16 along either axis
+    (so every block in both orientations has amax 6 * scale and encodes exactly with g = 1)."""
+    mags = np.array([0, .5, 1, 1.5, 2, 3, 4, 6])
+    v = mags[rng.integers(0, 8, (rows, cols))] * rng.choice([-1.0, 1.0], (rows, cols))
+    r, c = np.indices((rows, cols))
+    v = np.where((r + c) % 16 == 0, 6.0 * np.sign(v + 0.1), v)
+    return (v * scale).astype(F32)
+
+
+def check_transpose_exact(ref):
+    """Exactly representable input: dequantizing the x^T encoding gives x^T itself; a transposed block axis
+    or a transposed layout would not."""
+    rng = np.random.default_rng(32)
+    x = _grid_matrix(rng, 32, 48, 0.25)
+    back = ref.dequantize(ref.quantize_t(x, "given", 1.0))
+    assert back.shape == (48, 32) and np.array_equal(back, x.T.astype(np.float64))
+    x[3, 5] = F32(0.3)                      # off the grid: one element of column 5 changes
+    q = ref.quantize_t(x, "given", 1.0)
+    diff = np.argwhere(ref.dequantize(q) != x.T.astype(np.float64))
+    assert len(diff) >= 1 and np.all(diff[:, 0] == 5) and np.all(diff[:, 1] < 16)
+
+
+def check_backward_products(ref):
+    """The backward products from quantize / quantize_t compositions on exactly representable operands:
+    dX = dY . W and dW = dY^T . X are exact small dyadic results."""
+    rng = np.random.default_rng(33)
+    M, N, K = 32, 48, 64
+    dy, w, x = _grid_matrix(rng, M, N, 1.0), _grid_matrix(rng, N, K, 0.5), _grid_matrix(rng, M, K, 2.0)
+    dx, _ = ref.gemm(ref.quantize(dy, "given", 1.0), [ref.quantize_t(w, "given", 1.0)])
+    assert np.array_equal(dx, dy.astype(np.float64) @ w.astype(np.float64))
+    dw, _ = ref.gemm(ref.quantize_t(dy, "given", 1.0), [ref.quantize_t(x, "given", 1.0)])
+    assert np.array_equal(dw, dy.T.astype(np.float64) @ x.astype(np.float64))
+
+
 ALL_CHECKS = [
     check_e2m1_values, check_e4m3_values, check_roundtrip, check_e4m3_bruteforce, check_e2m1_bruteforce,
     check_e2m1_thresholds, check_global_scale, check_golden_given, check_golden_computed, check_golden_op_order, check_amax_block,
@@ -469,4 +518,5 @@ ALL_CHECKS = [
     check_negation, check_zero_block, check_dequant_error_bound, check_byte_counts,
     check_gemm_bruteforce, check_gemm_constant, check_gemm_onehot, check_gemm_identity,
     check_fused_concat, check_fused_pitfall, check_tolerance_fn,
+    check_transpose_columns, check_transpose_exact, check_backward_products,
 ]

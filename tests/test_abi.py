@@ -39,7 +39,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for required in ["nvfp4_quantize", "nvfp4_pack_weights", "nvfp4_gemm", "nvfp4_last_error",
                      "nvfp4_quantize_workspace_bytes", "nvfp4_packed_weight_bytes", "nvfp4_unpack_weights",
-                     "nvfp4_gemm_workspace_bytes", "nvfp4_abi_version", "nvfp4_device_check"]:
+                     "nvfp4_gemm_workspace_bytes", "nvfp4_abi_version", "nvfp4_device_check", "nvfp4_quantize_t"]:
         assert required in names
 
 
@@ -101,6 +101,45 @@ def test_valid_calls_stop_at_device_check_without_gpu():
         pytest.skip("a GPU is visible; this host-only check would launch on fake pointers")
     assert q() == nv.NVFP4_ERR_NO_DEVICE
     assert "device" in nv.last_error()
+
+
+def qt(**kw):
+    args = dict(x=FAKE, in_dtype=nv.NVFP4_IN_BF16, rows=32, cols=40, ld_x=40, codes=FAKE, scales=FAKE, g=FAKE,
+                g_mode=nv.NVFP4_G_COMPUTE, ws=FAKE, ws_bytes=1 << 16)
+    args.update(kw)
+    return nv.lib.nvfp4_quantize_t(args["x"], args["in_dtype"], args["rows"], args["cols"], args["ld_x"],
+                                   args["codes"], args["scales"], args["g"], args["g_mode"], args["ws"],
+                                   args["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(in_dtype=7), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(g_mode=3), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(g=None), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(x=None), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(scales=None), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(rows=24), nv.NVFP4_ERR_SHAPE),                  # the blocked axis is rows
+    (dict(rows=-16), nv.NVFP4_ERR_SHAPE),
+    (dict(cols=-1), nv.NVFP4_ERR_SHAPE),
+    (dict(ld_x=32), nv.NVFP4_ERR_SHAPE),
+    (dict(x=FAKE + 1), nv.NVFP4_ERR_UNSUPPORTED),          # bf16 elements not 2-byte aligned
+    (dict(x=FAKE + 2, in_dtype=nv.NVFP4_IN_F32), nv.NVFP4_ERR_UNSUPPORTED),
+    (dict(codes=FAKE + 4), nv.NVFP4_ERR_UNSUPPORTED),
+    (dict(ws=None), nv.NVFP4_ERR_WORKSPACE),
+    (dict(ws_bytes=0), nv.NVFP4_ERR_WORKSPACE),
+])
+def test_quantize_t_validation(kw, status):
+    assert qt(**kw) == status
+    assert nv.last_error() != ""
+
+
+def test_quantize_t_valid_calls_stop_at_device_check_without_gpu():
+    if not _no_gpu():
+        pytest.skip("a GPU is visible; this host-only check would launch on fake pointers")
+    assert qt() == nv.NVFP4_ERR_NO_DEVICE
+    assert qt(rows=0, cols=0, x=None, codes=None, scales=None) == nv.NVFP4_ERR_NO_DEVICE   # empty is valid
+    assert qt(ws=None, ws_bytes=0, g_mode=nv.NVFP4_G_GIVEN, cols=13, ld_x=16) == nv.NVFP4_ERR_NO_DEVICE
+    assert qt(ld_x=43, x=FAKE + 2) == nv.NVFP4_ERR_NO_DEVICE      # any element-aligned layout is accepted
 
 
 def test_workspace_query():

@@ -184,10 +184,41 @@ def m_tolerance_loose(o):
     o.gemm_within_tolerance = lambda y, r, a, rtol=1e-3: orig(y, r, a, rtol)
 
 
+def m_t_blocks_along_columns(o):
+    """x^T encoding that blocks along x's rows' own axis and lays the result out transposed."""
+    def quantize_t(x, g_mode="compute", g=None):
+        v = np.asarray(x, F32)
+        if v.shape[1] % 16:
+            v = np.pad(v, ((0, 0), (0, 16 - v.shape[1] % 16)))
+        q = o.quantize(v, g_mode, g)
+        nib = q.nibbles[:, :x.shape[1]].T.copy()
+        sc = np.repeat(q.scales, 16, axis=1)[:, :x.shape[1]].T[:, ::16].copy()
+        return o.Quantized(o.pack_nibbles(nib), sc, q.g, nibbles=nib)
+    o.quantize_t = quantize_t
+
+
+def m_t_g_first_column(o):
+    orig = o.quantize_t
+    o.quantize_t = lambda x, g_mode="compute", g=None: orig(
+        x, "given", o.global_scale(F32(np.max(np.abs(np.asarray(x, F32)[:, 0]))))) if g_mode == "compute" \
+        else orig(x, g_mode, g)
+
+
+def m_t_no_transpose_layout(o):
+    orig = o.quantize_t
+    def quantize_t(x, g_mode="compute", g=None):
+        q = orig(x, g_mode, g)
+        rows = np.asarray(x).shape[0]
+        nib = q.nibbles.reshape(-1, rows)[::-1].copy()       # output rows in reverse column order
+        return o.Quantized(o.pack_nibbles(nib), q.scales[::-1].copy(), q.g, nibbles=nib)
+    o.quantize_t = quantize_t
+
+
 MUTANTS = [m_ties_away, m_ties_down, m_e2m1_truncate, m_no_sign, m_zero_drops_sign, m_no_sat, m_no_div6,
            m_div6_before_mul, m_recip_inverted, m_recip_no_zero_rule, m_nibble_swap, m_range_448, m_range_6,
            m_no_zero_tensor_rule, m_dequant_no_g, m_dequant_scale_shift, m_gemm_modules_reversed,
-           m_gemm_shared_scale, m_gemm_transposed, m_block_32, m_amax_per_row, m_e4m3_bias8, m_tolerance_loose]
+           m_gemm_shared_scale, m_gemm_transposed, m_block_32, m_amax_per_row, m_e4m3_bias8, m_tolerance_loose,
+           m_t_blocks_along_columns, m_t_g_first_column, m_t_no_transpose_layout]
 
 
 @pytest.mark.parametrize("mutate", MUTANTS, ids=lambda m: m.__name__)
