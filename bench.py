@@ -166,6 +166,40 @@ def main():
             nv.nvfp4_linear(x, codes_g, scales_g, g_g, weights[i % copies].desc, yg, lin_ws, M=M, ld_x=K,
                             in_dtype=in_dtype, ld_y=N, gates=gates)
 
+    # training backward of the nGPT layer (nGPT trains end to end in NVFP4): dX = dY . W and dW = dY^T . X,
+    # every operand quantized along its contraction axis inside the step (dY along N for dX; W, dY and X
+    # along their rows, i.e. transposed), the two transposed weights packed, then the two products
+    bwd = None
+    if name == "ngpt":
+        dy_np = workloads.random_matrix(workloads.SEEDS["ngpt"] + 7, M, N, 1e-3, "bf16")
+        dy = torch.from_numpy(dy_np).to(dev).to(torch.bfloat16)
+        w_full = w_dev[0] if wl.quantize_w_in_step else torch.from_numpy(wl.w[0]).to(dev).to(torch.bfloat16)
+
+        def qbufs(rows, kdim):
+            return (*nv.empty_quantized(rows, kdim, dev),
+                    torch.empty((max(nv.nvfp4_quantize_workspace_bytes(rows, kdim), 256),), dtype=torch.uint8,
+                                device=dev))
+        a_dx, wt, a_dw, xt = qbufs(M, N), qbufs(K, N), qbufs(N, M), qbufs(K, M)
+        blob_wt = torch.empty((nv.nvfp4_packed_weight_bytes([K], N),), dtype=torch.uint8, device=dev)
+        blob_xt = torch.empty((nv.nvfp4_packed_weight_bytes([K], M),), dtype=torch.uint8, device=dev)
+        dx = torch.empty((M, K), dtype=torch.float32, device=dev)
+        dw = torch.empty((N, K), dtype=torch.float32, device=dev)
+
+        def step_backward(i):
+            nv.nvfp4_quantize(dy, *a_dx[:3], nv.NVFP4_G_COMPUTE, a_dx[3], rows=M, K=N, ld_x=N,
+                              in_dtype=nv.NVFP4_IN_BF16)
+            nv.nvfp4_quantize_t(w_full, *wt[:3], nv.NVFP4_G_COMPUTE, wt[3])
+            d_wt = nv.nvfp4_pack_weights([wt[:3]], N, blob_wt)
+            nv.nvfp4_gemm(M, a_dx[0], a_dx[1], a_dx[2], d_wt, dx, K, None)
+            nv.nvfp4_quantize_t(dy, *a_dw[:3], nv.NVFP4_G_COMPUTE, a_dw[3])
+            nv.nvfp4_quantize_t(x, *xt[:3], nv.NVFP4_G_COMPUTE, xt[3])
+            d_xt = nv.nvfp4_pack_weights([xt[:3]], M, blob_xt)
+            nv.nvfp4_gemm(N, a_dw[0], a_dw[1], a_dw[2], d_xt, dw, K, None)
+
+        def quant_t_only(i):
+            nv.nvfp4_quantize_t(x, *xt[:3], nv.NVFP4_G_COMPUTE, xt[3])
+        bwd = (step_backward, quant_t_only)
+
     def gemm_only(i):
         nv.nvfp4_gemm(M, codes, scales, g, weights[i % copies].desc, y, N, gemm_ws)
 
@@ -223,6 +257,8 @@ def main():
     t_quant = timed(quant_only, k_steps, min(warmup, k_steps)) / k_steps
     t_given = timed(step_given, k_steps, min(warmup, k_steps)) / k_steps
     t_gated = timed(step_gated, k_steps, min(warmup, k_steps)) / k_steps if gate_p is not None else None
+    t_bwd = timed(bwd[0], k_steps, min(warmup, k_steps)) / k_steps if bwd else None
+    t_qt = timed(bwd[1], k_steps, min(warmup, k_steps)) / k_steps if bwd else None
 
     flops = 2.0 * M * N * K
     tflops = flops / t_step / 1e12
@@ -279,6 +315,30 @@ def main():
         gcols = torch.arange(gate_p.a_col, gate_p.b_col + gate_p.n_b, device=dev)
         got = yg[torch.from_numpy(rows).to(dev)][:, gcols].cpu().numpy()
         gated_ok, gated_worst = gref.within(got, gref.apply_gates(yab, *gargs), gref.gates_tolerance(yab, aab, *gargs))
+    bwd_parity = None
+    if bwd:   # sampled entries of dX and dW, and sampled rows of the transposed encodings, against the oracle
+        rsel = torch.from_numpy(rows).to(dev)
+        csel = np.unique(np.concatenate([[0, K - 1], rng.choice(K, 14, replace=False)]))
+        nsel = np.unique(np.concatenate([[0, N - 1], rng.choice(N, 14, replace=False)]))
+        g_dy = ref.global_scale(np.float32(np.abs(dy_np).max()))
+        g_w = ref.global_scale(np.float32(np.abs(wl.w[0]).max()))
+        g_x = ref.global_scale(np.float32(np.abs(wl.x).max()))
+        dyq = ref.quantize(dy_np[rows], "given", g_dy)
+        wtq = ref.quantize_t(wl.w[0][:, csel], "given", g_w)
+        dx_ref, dx_a = ref.gemm_dequantized(ref.dequantize(dyq), ref.dequantize(wtq))
+        dx_got = dx[rsel][:, torch.from_numpy(csel).to(dev)].cpu().numpy()
+        dx_ok, dx_worst = ref.gemm_within_tolerance(dx_got, dx_ref, dx_a)
+        dytq = ref.quantize_t(dy_np[:, nsel], "given", g_dy)
+        xtq = ref.quantize_t(wl.x[:, csel], "given", g_x)
+        dw_ref, dw_a = ref.gemm_dequantized(ref.dequantize(dytq), ref.dequantize(xtq))
+        dw_got = dw[torch.from_numpy(nsel).to(dev)][:, torch.from_numpy(csel).to(dev)].cpu().numpy()
+        dw_ok, dw_worst = ref.gemm_within_tolerance(dw_got, dw_ref, dw_a)
+        nsel_t = torch.from_numpy(nsel).to(dev)
+        t_codes_ok = bool(np.array_equal(a_dw[0][nsel_t].cpu().numpy(), dytq.codes) and
+                          np.array_equal(a_dw[1][nsel_t].cpu().numpy(), dytq.scales) and
+                          np.float32(a_dw[2].item()) == g_dy)
+        bwd_parity = {"transposed_codes_scales_bit_exact": t_codes_ok, "dX_within_1e-5": bool(dx_ok),
+                      "dX_worst_ratio": dx_worst, "dW_within_1e-5": bool(dw_ok), "dW_worst_ratio": dw_worst}
     xq1 = ref.quantize(wl.x[rows], g_mode="given", g=1.0)
     given_ok = bool(np.array_equal(codes1[torch.from_numpy(rows).to(dev)].cpu().numpy(), xq1.codes) and
                     np.array_equal(scales1[torch.from_numpy(rows).to(dev)].cpu().numpy(), xq1.scales))
@@ -309,11 +369,18 @@ def main():
                               "quantize alone": t_quant * 1e6, "gemm alone": t_gemm * 1e6,
                               "step with g given (no amax pass)": t_given * 1e6,
                               "tflops with g given": flops / t_given / 1e12,
-                              "step with GDN gates fused": t_gated * 1e6 if t_gated else None},
+                              "step with GDN gates fused": t_gated * 1e6 if t_gated else None,
+                              "backward step (dX and dW, operands quantized and packed in the step)":
+                                  t_bwd * 1e6 if t_bwd else None,
+                              "backward tflops": 2.0 * flops / t_bwd / 1e12 if t_bwd else None,
+                              "quantize_t alone (X^T, g computed)": t_qt * 1e6 if t_qt else None,
+                              "quantize_t GB/s (read x once, write codes and scales)":
+                                  (x_in_bytes + x_q_bytes) / t_qt / 1e9 if t_qt else None},
         "step_gbs": (x_in_bytes + w_bytes + x_q_bytes + M * N * 4) / t_step / 1e9,
         "parity": {"codes_scales_bit_exact": codes_ok, "gemm_within_1e-5": bool(y_ok), "worst_ratio": worst,
                    "g_given_codes_scales_bit_exact": given_ok,
                    "gdn_gates_within_bound": gated_ok, "gdn_gates_worst_ratio": gated_worst,
+                   "backward": bwd_parity,
                    "rows_checked": int(len(rows)), "cols_checked": int(len(cols))},
     }
     print(json.dumps(out), flush=True)
