@@ -149,6 +149,33 @@ nvfp4_status nvfp4_quantize_t(const void* x, int in_dtype, int64_t rows, int64_t
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Quantize behind a randomized Hadamard transform (RHT).
+ *
+ * Standard transformers trained in NVFP4 apply random Hadamard transforms
+ * before quantization; nGPT trains without them ("Normalized Architectures
+ * are Natively 4-Bit", sections "Problem" and "Approach").  Each 16-element
+ * block along the quantization axis becomes v' = H16 . D . v / 4 (D negates
+ * element i of every block when bit i of signs is set; H16 in natural order;
+ * FP32 butterflies in the stage order h = 1, 2, 4, 8), and v' is quantized
+ * exactly as nvfp4_quantize does, with g computed from the amax of the
+ * transformed tensor in COMPUTE mode.  The transform is orthogonal, so the
+ * product of two operands transformed with the same signs needs no change:
+ * quantize both with the same mask and call nvfp4_gemm as usual.
+ *
+ * nvfp4_quantize_rht   : arguments of nvfp4_quantize, plus signs
+ * nvfp4_quantize_t_rht : arguments of nvfp4_quantize_t, plus signs (blocks of
+ *                        16 rows of x, for the backward products)
+ * signs : 16-bit mask (the random draw is the caller's); larger values give
+ *         NVFP4_ERR_INVALID_ARG.  Workspace sizes: nvfp4_quantize_workspace_bytes.
+ * ------------------------------------------------------------------------- */
+nvfp4_status nvfp4_quantize_rht(const void* x, int in_dtype, int64_t rows, int64_t K, int64_t ld_x,
+                                uint32_t signs, uint8_t* codes, uint8_t* scales, float* g, int g_mode,
+                                void* workspace, size_t workspace_bytes, void* stream);
+nvfp4_status nvfp4_quantize_t_rht(const void* x, int in_dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                                  uint32_t signs, uint8_t* codes, uint8_t* scales, float* g, int g_mode,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Packed weights.
  *
  * A projection is a stack of n_modules sub-modules (e.g. q,k,v,z,a,b of a

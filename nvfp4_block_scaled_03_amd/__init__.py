@@ -103,6 +103,10 @@ def _load():
         "nvfp4_quantize_workspace_bytes": (c_sz, [c_i64, c_i64]),
         "nvfp4_quantize": (c_int, [c_vp, c_int, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_int, c_vp, c_sz, c_vp]),
         "nvfp4_quantize_t": (c_int, [c_vp, c_int, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_int, c_vp, c_sz, c_vp]),
+        "nvfp4_quantize_rht": (c_int, [c_vp, c_int, c_i64, c_i64, c_i64, ctypes.c_uint32, c_vp, c_vp, c_vp, c_int,
+                                       c_vp, c_sz, c_vp]),
+        "nvfp4_quantize_t_rht": (c_int, [c_vp, c_int, c_i64, c_i64, c_i64, ctypes.c_uint32, c_vp, c_vp, c_vp, c_int,
+                                         c_vp, c_sz, c_vp]),
         "nvfp4_packed_weight_bytes": (c_sz, [c_int, ctypes.POINTER(c_i64), c_i64]),
         "nvfp4_pack_weights": (c_int, [c_int, ctypes.POINTER(c_i64), c_i64, ctypes.POINTER(c_vp),
                                        ctypes.POINTER(c_vp), ctypes.POINTER(c_vp), c_vp, c_sz,
@@ -198,6 +202,32 @@ def nvfp4_quantize_t(x, codes, scales, g, g_mode=NVFP4_G_COMPUTE, workspace=None
     ws_bytes = workspace.numel() * workspace.element_size() if isinstance(workspace, torch.Tensor) else 0
     _check(_lib.nvfp4_quantize_t(_ptr(x), in_dtype, rows, cols, ld_x, _ptr(codes), _ptr(scales), _ptr(g), g_mode,
                                  _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def _layout(x, unit_stride_msg):
+    rows, cols = x.shape
+    if x.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("x must be float32 or bfloat16")
+    if cols > 1 and x.stride(-1) != 1:
+        raise ValueError(unit_stride_msg)
+    ld_x = x.stride(0) if rows > 1 else cols
+    return rows, cols, ld_x, NVFP4_IN_BF16 if x.dtype == torch.bfloat16 else NVFP4_IN_F32
+
+
+def nvfp4_quantize_rht(x, signs: int, codes, scales, g, g_mode=NVFP4_G_COMPUTE, workspace=None, stream=None):
+    """nvfp4_quantize of the randomized Hadamard transform of x [rows, K] (16-bit sign mask)."""
+    rows, K, ld_x, in_dtype = _layout(x, "x must have unit stride along K")
+    ws_bytes = workspace.numel() * workspace.element_size() if isinstance(workspace, torch.Tensor) else 0
+    _check(_lib.nvfp4_quantize_rht(_ptr(x), in_dtype, rows, K, ld_x, int(signs), _ptr(codes), _ptr(scales), _ptr(g),
+                                   g_mode, _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def nvfp4_quantize_t_rht(x, signs: int, codes, scales, g, g_mode=NVFP4_G_COMPUTE, workspace=None, stream=None):
+    """nvfp4_quantize_t of the randomized Hadamard transform of x^T (blocks of 16 rows of x)."""
+    rows, cols, ld_x, in_dtype = _layout(x, "x must have unit stride along its columns")
+    ws_bytes = workspace.numel() * workspace.element_size() if isinstance(workspace, torch.Tensor) else 0
+    _check(_lib.nvfp4_quantize_t_rht(_ptr(x), in_dtype, rows, cols, ld_x, int(signs), _ptr(codes), _ptr(scales),
+                                     _ptr(g), g_mode, _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def nvfp4_packed_weight_bytes(module_rows: Sequence[int], K: int) -> int:
@@ -310,6 +340,30 @@ def quantize_t(x: torch.Tensor, g=None, stream=None):
             gt.fill_(float(g))
         nvfp4_quantize_t(x, codes, scales, gt, NVFP4_G_GIVEN, None, stream)
     return codes, scales, gt
+
+
+def _quantize_with(fn, x, signs, out_rows, out_k, g, stream):
+    codes, scales, gt = empty_quantized(out_rows, out_k, x.device)
+    if g is None:
+        ws = torch.empty((max(nvfp4_quantize_workspace_bytes(*x.shape), 1),), dtype=torch.uint8, device=x.device)
+        fn(x, signs, codes, scales, gt, NVFP4_G_COMPUTE, ws, stream)
+    else:
+        if isinstance(g, torch.Tensor):
+            gt.copy_(g.reshape(1))
+        else:
+            gt.fill_(float(g))
+        fn(x, signs, codes, scales, gt, NVFP4_G_GIVEN, None, stream)
+    return codes, scales, gt
+
+
+def quantize_rht(x: torch.Tensor, signs: int, g=None, stream=None):
+    """NVFP4 codes, scales and g of the randomized Hadamard transform of x [rows, K]."""
+    return _quantize_with(nvfp4_quantize_rht, x, signs, x.shape[0], x.shape[1], g, stream)
+
+
+def quantize_t_rht(x: torch.Tensor, signs: int, g=None, stream=None):
+    """The same for x^T: codes [cols, rows/2], scales [cols, rows/16]."""
+    return _quantize_with(nvfp4_quantize_t_rht, x, signs, x.shape[1], x.shape[0], g, stream)
 
 
 class PackedWeight:

@@ -126,9 +126,10 @@ size_t nvfp4_quantize_workspace_bytes(int64_t rows, int64_t K) {
     return (size_t)round_up((int64_t)nvfp4::quantize_partials_count(rows, K) * (int64_t)sizeof(float), 256);
 }
 
-nvfp4_status nvfp4_quantize(const void* x, int in_dtype, int64_t rows, int64_t K, int64_t ld_x, uint8_t* codes,
-                            uint8_t* scales, float* g, int g_mode, void* workspace, size_t workspace_bytes,
-                            void* stream) {
+static nvfp4_status quantize_impl(const void* x, int in_dtype, int64_t rows, int64_t K, int64_t ld_x, uint8_t* codes,
+                                  uint8_t* scales, float* g, int g_mode, void* workspace, size_t workspace_bytes,
+                                  void* stream, int rht, uint32_t signs) {
+    if (rht && signs > 0xFFFFu) return fail(NVFP4_ERR_INVALID_ARG, "signs is a 16-bit mask (got 0x%x)", signs);
     if (in_dtype != NVFP4_IN_F32 && in_dtype != NVFP4_IN_BF16)
         return fail(NVFP4_ERR_INVALID_ARG, "unknown input dtype %d", in_dtype);
     if (g_mode != NVFP4_G_COMPUTE && g_mode != NVFP4_G_GIVEN)
@@ -157,13 +158,28 @@ nvfp4_status nvfp4_quantize(const void* x, int in_dtype, int64_t rows, int64_t K
     if (st != NVFP4_OK) return st;
     return launched(nvfp4::launch_quantize(x, in_dtype, rows, K, ld_x, codes, scales, g, g_mode,
                                            static_cast<float*>(workspace), n_partials,
-                                           static_cast<hipStream_t>(stream)),
+                                           static_cast<hipStream_t>(stream), rht, signs),
                     "quantize launch");
 }
 
-nvfp4_status nvfp4_quantize_t(const void* x, int in_dtype, int64_t rows, int64_t cols, int64_t ld_x,
-                              uint8_t* codes, uint8_t* scales, float* g, int g_mode, void* workspace,
-                              size_t workspace_bytes, void* stream) {
+nvfp4_status nvfp4_quantize(const void* x, int in_dtype, int64_t rows, int64_t K, int64_t ld_x, uint8_t* codes,
+                            uint8_t* scales, float* g, int g_mode, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+    return quantize_impl(x, in_dtype, rows, K, ld_x, codes, scales, g, g_mode, workspace, workspace_bytes, stream,
+                         0, 0u);
+}
+
+nvfp4_status nvfp4_quantize_rht(const void* x, int in_dtype, int64_t rows, int64_t K, int64_t ld_x, uint32_t signs,
+                                uint8_t* codes, uint8_t* scales, float* g, int g_mode, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+    return quantize_impl(x, in_dtype, rows, K, ld_x, codes, scales, g, g_mode, workspace, workspace_bytes, stream,
+                         1, signs);
+}
+
+static nvfp4_status quantize_t_impl(const void* x, int in_dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                                    uint8_t* codes, uint8_t* scales, float* g, int g_mode, void* workspace,
+                                    size_t workspace_bytes, void* stream, int rht, uint32_t signs) {
+    if (rht && signs > 0xFFFFu) return fail(NVFP4_ERR_INVALID_ARG, "signs is a 16-bit mask (got 0x%x)", signs);
     if (in_dtype != NVFP4_IN_F32 && in_dtype != NVFP4_IN_BF16)
         return fail(NVFP4_ERR_INVALID_ARG, "unknown input dtype %d", in_dtype);
     if (g_mode != NVFP4_G_COMPUTE && g_mode != NVFP4_G_GIVEN)
@@ -191,8 +207,22 @@ nvfp4_status nvfp4_quantize_t(const void* x, int in_dtype, int64_t rows, int64_t
     if (st != NVFP4_OK) return st;
     return launched(nvfp4::launch_quantize_t(x, in_dtype, rows, cols, ld_x, codes, scales, g, g_mode,
                                              static_cast<float*>(workspace), n_partials,
-                                             static_cast<hipStream_t>(stream)),
+                                             static_cast<hipStream_t>(stream), rht, signs),
                     "quantize_t launch");
+}
+
+nvfp4_status nvfp4_quantize_t(const void* x, int in_dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                              uint8_t* codes, uint8_t* scales, float* g, int g_mode, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+    return quantize_t_impl(x, in_dtype, rows, cols, ld_x, codes, scales, g, g_mode, workspace, workspace_bytes,
+                           stream, 0, 0u);
+}
+
+nvfp4_status nvfp4_quantize_t_rht(const void* x, int in_dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                                  uint32_t signs, uint8_t* codes, uint8_t* scales, float* g, int g_mode,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+    return quantize_t_impl(x, in_dtype, rows, cols, ld_x, codes, scales, g, g_mode, workspace, workspace_bytes,
+                           stream, 1, signs);
 }
 
 size_t nvfp4_packed_weight_bytes(int n_modules, const int64_t* module_rows, int64_t K) {

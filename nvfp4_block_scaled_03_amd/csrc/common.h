@@ -169,6 +169,28 @@ __device__ __forceinline__ float block_amax(const float v[16]) {
     return m;
 }
 
+// Randomized Hadamard transform of one 16-element block, in place:
+// v <- H16 . D . v / 4, D the diagonal of the sign mask (bit i negates element
+// i), H16 the Hadamard matrix in natural order.  The negation is a sign-bit
+// flip (exact); the butterflies run in the stage order h = 1, 2, 4, 8 with one
+// FP32 rounding per addition, since codes are bit-exact and that order is part
+// of the definition; the product by 1/4 is exact above the subnormal range.
+__device__ __forceinline__ void rht16(float v[16], uint32_t signs) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = __uint_as_float(__float_as_uint(v[i]) ^ (((signs >> i) & 1u) << 31));
+#pragma unroll
+    for (int h = 1; h < 16; h <<= 1)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            if (!(i & h)) {
+                const float a = v[i], b = v[i + h];
+                v[i] = a + b;
+                v[i + h] = a - b;
+            }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] *= 0.25f;
+}
+
 // Encode one 16-element block held in v[16], whose max |v| is bamax, with the
 // tensor's s_enc and its table of s_enc / S.
 __device__ __forceinline__ void encode_block(const float v[16], float bamax, float s_enc, const float* rtab,
@@ -252,12 +274,13 @@ __device__ __forceinline__ void skinny_step(float4v& acc, const uint4& wv, uint3
 
 int quantize_partials_count(int64_t rows, int64_t K);
 // Per-workgroup partial maxima of |x| (n_partials workgroups), as the first kernel of the quantizer.
+// rht != 0: every block goes through rht16 with the given sign mask first.
 hipError_t launch_quantize(const void* x, int in_dtype, int64_t rows, int64_t K, int64_t ld_x,
                            uint8_t* codes, uint8_t* scales, float* g, int g_mode,
-                           float* partials, int n_partials, hipStream_t stream);
+                           float* partials, int n_partials, hipStream_t stream, int rht = 0, uint32_t signs = 0);
 hipError_t launch_quantize_t(const void* x, int in_dtype, int64_t rows, int64_t cols, int64_t ld_x,
                              uint8_t* codes, uint8_t* scales, float* g, int g_mode, float* partials, int n_partials,
-                             hipStream_t stream);
+                             hipStream_t stream, int rht = 0, uint32_t signs = 0);
 
 hipError_t launch_pack(const nvfp4_weight_desc& d, const uint8_t* const* codes,
                        const uint8_t* const* scales, const float* const* g_w, uint8_t* blob,

@@ -61,11 +61,32 @@ __global__ __launch_bounds__(kQThreads) void amax_partials_kernel(const T* __res
     if (threadIdx.x == 0) partials[blockIdx.x] = m;
 }
 
+// Per-workgroup max |v| over transformed blocks (the global amax of the
+// transformed tensor), one partial per workgroup, blocks by grid stride.
 template <typename T>
+__global__ __launch_bounds__(kQThreads) void amax_rht_kernel(const T* __restrict__ x, int64_t rows, int64_t K,
+                                                             int64_t ld, uint32_t signs, float* __restrict__ partials) {
+    const int64_t bpr = K / 16, nblk = rows * bpr;
+    float m = 0.0f;
+    for (int64_t b = (int64_t)blockIdx.x * kQThreads + threadIdx.x; b < nblk; b += (int64_t)gridDim.x * kQThreads) {
+        const int64_t r = b / bpr;
+        const T* src = x + r * ld + (b - r * bpr) * 16;
+        float v[16];
+        load8(src, v);
+        load8(src + 8, v + 8);
+        rht16(v, signs);
+        m = fmaxf(m, block_amax(v));
+    }
+    m = block_max<kQThreads>(m);
+    if (threadIdx.x == 0) partials[blockIdx.x] = m;
+}
+
+template <typename T, bool RHT>
 __global__ __launch_bounds__(kQThreads) void encode_kernel(const T* __restrict__ x, int64_t rows, int64_t K, int64_t ld,
                                                            uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
                                                            float* __restrict__ g_io, int g_given,
-                                                           const float* __restrict__ partials, int n_partials) {
+                                                           const float* __restrict__ partials, int n_partials,
+                                                           uint32_t signs) {
     __shared__ float s_senc;
     __shared__ float rtab[128];
     if (g_given) {
@@ -99,6 +120,7 @@ __global__ __launch_bounds__(kQThreads) void encode_kernel(const T* __restrict__
         float v[16];
         load8(src, v);
         load8(src + 8, v + 8);
+        if (RHT) rht16(v, signs);
         uint32_t lo, hi, S;
         encode_block(v, block_amax(v), s_enc, rtab, lo, hi, S);
         *reinterpret_cast<uint2*>(codes + b * 8) = make_uint2(lo, hi);
@@ -127,30 +149,39 @@ __global__ void write_unit_g_kernel(float* g) { g[0] = 1.0f; }
 constexpr int kTLanesC = 8;                 // lanes across columns (128-byte row segments)
 constexpr int kTRows = 4 * (64 / kTLanesC) * 16;   // rows per workgroup tile (512)
 
-template <typename T>
+// MODE: kTEncode (plain), kTEncodeRht (transformed blocks), kTAmaxRht (no
+// encoding: max |v| of the transformed blocks, one partial per workgroup into
+// amax_out, tiles by grid stride).
+enum { kTEncode = 0, kTEncodeRht = 1, kTAmaxRht = 2 };
+
+template <typename T, int MODE>
 __global__ __launch_bounds__(kQThreads) void encode_t_kernel(const T* __restrict__ x, int64_t rows, int64_t cols,
                                                              int64_t ld, uint8_t* __restrict__ codes,
                                                              uint8_t* __restrict__ scales, float* __restrict__ g_io,
                                                              int g_given, const float* __restrict__ partials,
-                                                             int n_partials, int vec) {
+                                                             int n_partials, int vec, uint32_t signs,
+                                                             float* __restrict__ amax_out) {
     __shared__ float s_senc;
     __shared__ float rtab[128];
-    if (g_given) {
-        if (threadIdx.x == 0) s_senc = 1.0f / g_io[0];
-    } else {
-        float m = 0.0f;
-        for (int i = threadIdx.x; i < n_partials; i += kQThreads) m = fmaxf(m, partials[i]);
-        m = block_max<kQThreads>(m);
-        if (threadIdx.x == 0) {
-            const float g = global_scale_from_amax(m);
-            s_senc = 1.0f / g;
-            if (blockIdx.x == 0) g_io[0] = g;
+    float s_enc = 0.0f, m = 0.0f;
+    if (MODE != kTAmaxRht) {
+        if (g_given) {
+            if (threadIdx.x == 0) s_senc = 1.0f / g_io[0];
+        } else {
+            float pm = 0.0f;
+            for (int i = threadIdx.x; i < n_partials; i += kQThreads) pm = fmaxf(pm, partials[i]);
+            pm = block_max<kQThreads>(pm);
+            if (threadIdx.x == 0) {
+                const float g = global_scale_from_amax(pm);
+                s_senc = 1.0f / g;
+                if (blockIdx.x == 0) g_io[0] = g;
+            }
         }
+        __syncthreads();
+        s_enc = s_senc;
+        fill_recip_table(rtab, s_enc, threadIdx.x, kQThreads);
+        __syncthreads();
     }
-    __syncthreads();
-    const float s_enc = s_senc;
-    fill_recip_table(rtab, s_enc, threadIdx.x, kQThreads);
-    __syncthreads();
 
     constexpr int kVec = 16 / (int)sizeof(T);                 // columns per lane (one 16-byte vector)
     constexpr int kRG = 64 / kTLanesC;                         // row groups per wavefront
@@ -182,11 +213,20 @@ __global__ __launch_bounds__(kQThreads) void encode_t_kernel(const T* __restrict
             float v[16];
 #pragma unroll
             for (int i = 0; i < 16; ++i) v[i] = elem_f32(e[i][k]);
+            if (MODE != kTEncode) rht16(v, signs);
+            if (MODE == kTAmaxRht) {
+                m = fmaxf(m, block_amax(v));
+                continue;
+            }
             uint32_t lo, hi, sc;
             encode_block(v, block_amax(v), s_enc, rtab, lo, hi, sc);
             *reinterpret_cast<uint2*>(codes + (c0 + k) * (rows / 2) + r0 / 2) = make_uint2(lo, hi);
             scales[(c0 + k) * (rows / 16) + r0 / 16] = (uint8_t)sc;
         }
+    }
+    if (MODE == kTAmaxRht) {
+        m = block_max<kQThreads>(m);
+        if (threadIdx.x == 0) amax_out[blockIdx.x] = m;
     }
 }
 
@@ -296,9 +336,28 @@ static int encode_grid(int64_t rows, int64_t K) {
     return (int)(wg < 1 ? 1 : wg);
 }
 
+template <typename T>
+static void launch_t(const T* xp, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* codes, uint8_t* scales,
+                     float* g, int given, float* partials, int n_partials, int vec, int vec_rows, int grid, int rht,
+                     uint32_t signs, hipStream_t stream) {
+    if (!rht) {
+        if (!given)
+            hipLaunchKernelGGL(amax_partials_kernel<T>, dim3(n_partials), dim3(kQThreads), 0, stream,
+                               xp, rows, cols, ld_x, partials, vec);
+        hipLaunchKernelGGL((encode_t_kernel<T, kTEncode>), dim3(grid), dim3(kQThreads), 0, stream, xp, rows, cols,
+                           ld_x, codes, scales, g, given, partials, n_partials, vec_rows, 0u, nullptr);
+        return;
+    }
+    if (!given)
+        hipLaunchKernelGGL((encode_t_kernel<T, kTAmaxRht>), dim3(n_partials), dim3(kQThreads), 0, stream, xp, rows,
+                           cols, ld_x, nullptr, nullptr, nullptr, 0, nullptr, 0, vec_rows, signs, partials);
+    hipLaunchKernelGGL((encode_t_kernel<T, kTEncodeRht>), dim3(grid), dim3(kQThreads), 0, stream, xp, rows, cols,
+                       ld_x, codes, scales, g, given, partials, n_partials, vec_rows, signs, nullptr);
+}
+
 hipError_t launch_quantize_t(const void* x, int in_dtype, int64_t rows, int64_t cols, int64_t ld_x,
                              uint8_t* codes, uint8_t* scales, float* g, int g_mode, float* partials, int n_partials,
-                             hipStream_t stream) {
+                             hipStream_t stream, int rht, uint32_t signs) {
     const int given = (g_mode == NVFP4_G_GIVEN);
     if (rows == 0 || cols == 0) {
         if (!given) hipLaunchKernelGGL(write_unit_g_kernel, dim3(1), dim3(1), 0, stream, g);
@@ -306,38 +365,49 @@ hipError_t launch_quantize_t(const void* x, int in_dtype, int64_t rows, int64_t 
     }
     // 16-byte vector loads need an aligned base and (unless the tensor is dense) an aligned row stride
     const int esize = in_dtype == NVFP4_IN_BF16 ? 2 : 4;
+    const int vec = (reinterpret_cast<uintptr_t>(x) % 16 == 0) && (ld_x == cols || (ld_x * esize) % 16 == 0);
+    const int vec_rows = (reinterpret_cast<uintptr_t>(x) % 16 == 0) && (ld_x * esize) % 16 == 0;
     const int64_t tcols = kTLanesC * (16 / esize);
     const int64_t tiles = ((rows + kTRows - 1) / kTRows) * ((cols + tcols - 1) / tcols);
     const int grid = (int)(tiles < (1 << 24) ? tiles : (1 << 24));   // one tile per workgroup in practice
-    const int vec = (reinterpret_cast<uintptr_t>(x) % 16 == 0) && (ld_x == cols || (ld_x * esize) % 16 == 0);
-    const int vec_rows = (reinterpret_cast<uintptr_t>(x) % 16 == 0) && (ld_x * esize) % 16 == 0;
-    if (in_dtype == NVFP4_IN_BF16) {
-        const uint16_t* xp = static_cast<const uint16_t*>(x);
-        if (!given)
-            hipLaunchKernelGGL(amax_partials_kernel<uint16_t>, dim3(n_partials), dim3(kQThreads), 0, stream,
-                               xp, rows, cols, ld_x, partials, vec);
-hipLaunchKernelGGL(encode_t_kernel<uint16_t>, dim3(grid), dim3(kQThreads), 0, stream,
-                           xp, rows, cols, ld_x, codes, scales, g, given, partials, n_partials, vec_rows);
-    } else {
-        const float* xp = static_cast<const float*>(x);
-        if (!given)
-            hipLaunchKernelGGL(amax_partials_kernel<float>, dim3(n_partials), dim3(kQThreads), 0, stream,
-                               xp, rows, cols, ld_x, partials, vec);
-hipLaunchKernelGGL(encode_t_kernel<float>, dim3(grid), dim3(kQThreads), 0, stream,
-                           xp, rows, cols, ld_x, codes, scales, g, given, partials, n_partials, vec_rows);
-    }
+    if (in_dtype == NVFP4_IN_BF16)
+        launch_t(static_cast<const uint16_t*>(x), rows, cols, ld_x, codes, scales, g, given, partials, n_partials,
+                 vec, vec_rows, grid, rht, signs, stream);
+    else
+        launch_t(static_cast<const float*>(x), rows, cols, ld_x, codes, scales, g, given, partials, n_partials,
+                 vec, vec_rows, grid, rht, signs, stream);
     return hipGetLastError();
+}
+
+template <typename T>
+static void launch_rows(const T* xp, int64_t rows, int64_t K, int64_t ld_x, uint8_t* codes, uint8_t* scales,
+                        float* g, int given, float* partials, int n_partials, int grid, int rht, uint32_t signs,
+                        hipStream_t stream) {
+    if (!given) {
+        if (rht)
+            hipLaunchKernelGGL(amax_rht_kernel<T>, dim3(n_partials), dim3(kQThreads), 0, stream, xp, rows, K, ld_x,
+                               signs, partials);
+        else
+            hipLaunchKernelGGL(amax_partials_kernel<T>, dim3(n_partials), dim3(kQThreads), 0, stream, xp, rows, K,
+                               ld_x, partials, 1);
+    }
+    if (rht)
+        hipLaunchKernelGGL((encode_kernel<T, true>), dim3(grid), dim3(kQThreads), 0, stream, xp, rows, K, ld_x, codes,
+                           scales, g, given, partials, n_partials, signs);
+    else
+        hipLaunchKernelGGL((encode_kernel<T, false>), dim3(grid), dim3(kQThreads), 0, stream, xp, rows, K, ld_x,
+                           codes, scales, g, given, partials, n_partials, 0u);
 }
 
 hipError_t launch_quantize(const void* x, int in_dtype, int64_t rows, int64_t K, int64_t ld_x,
                            uint8_t* codes, uint8_t* scales, float* g, int g_mode,
-                           float* partials, int n_partials, hipStream_t stream) {
+                           float* partials, int n_partials, hipStream_t stream, int rht, uint32_t signs) {
     const int given = (g_mode == NVFP4_G_GIVEN);
     if (rows == 0) {
         if (!given) hipLaunchKernelGGL(write_unit_g_kernel, dim3(1), dim3(1), 0, stream, g);
         return hipGetLastError();
     }
-    const int p = small_blocks_per_thread(rows, K, ld_x, in_dtype);
+    const int p = rht ? 0 : small_blocks_per_thread(rows, K, ld_x, in_dtype);   // the one-launch path has no RHT
     if (p > 0) {
         if (in_dtype == NVFP4_IN_BF16)
             return launch_small<uint16_t>(p, static_cast<const uint16_t*>(x), rows, K, ld_x, codes, scales, g, given,
@@ -347,21 +417,12 @@ hipError_t launch_quantize(const void* x, int in_dtype, int64_t rows, int64_t K,
                                        stream);
     }
     const int grid = encode_grid(rows, K);
-    if (in_dtype == NVFP4_IN_BF16) {
-        const uint16_t* xp = static_cast<const uint16_t*>(x);
-        if (!given)
-            hipLaunchKernelGGL(amax_partials_kernel<uint16_t>, dim3(n_partials), dim3(kQThreads), 0, stream,
-                               xp, rows, K, ld_x, partials);
-        hipLaunchKernelGGL(encode_kernel<uint16_t>, dim3(grid), dim3(kQThreads), 0, stream,
-                           xp, rows, K, ld_x, codes, scales, g, given, partials, n_partials);
-    } else {
-        const float* xp = static_cast<const float*>(x);
-        if (!given)
-            hipLaunchKernelGGL(amax_partials_kernel<float>, dim3(n_partials), dim3(kQThreads), 0, stream,
-                               xp, rows, K, ld_x, partials);
-        hipLaunchKernelGGL(encode_kernel<float>, dim3(grid), dim3(kQThreads), 0, stream,
-                           xp, rows, K, ld_x, codes, scales, g, given, partials, n_partials);
-    }
+    if (in_dtype == NVFP4_IN_BF16)
+        launch_rows(static_cast<const uint16_t*>(x), rows, K, ld_x, codes, scales, g, given, partials, n_partials,
+                    grid, rht, signs, stream);
+    else
+        launch_rows(static_cast<const float*>(x), rows, K, ld_x, codes, scales, g, given, partials, n_partials,
+                    grid, rht, signs, stream);
     return hipGetLastError();
 }
 

@@ -39,7 +39,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for required in ["nvfp4_quantize", "nvfp4_pack_weights", "nvfp4_gemm", "nvfp4_last_error",
                      "nvfp4_quantize_workspace_bytes", "nvfp4_packed_weight_bytes", "nvfp4_unpack_weights",
-                     "nvfp4_gemm_workspace_bytes", "nvfp4_abi_version", "nvfp4_device_check", "nvfp4_quantize_t"]:
+                     "nvfp4_gemm_workspace_bytes", "nvfp4_abi_version", "nvfp4_device_check", "nvfp4_quantize_t", "nvfp4_quantize_rht", "nvfp4_quantize_t_rht"]:
         assert required in names
 
 
@@ -140,6 +140,19 @@ def test_quantize_t_valid_calls_stop_at_device_check_without_gpu():
     assert qt(rows=0, cols=0, x=None, codes=None, scales=None) == nv.NVFP4_ERR_NO_DEVICE   # empty is valid
     assert qt(ws=None, ws_bytes=0, g_mode=nv.NVFP4_G_GIVEN, cols=13, ld_x=16) == nv.NVFP4_ERR_NO_DEVICE
     assert qt(ld_x=43, x=FAKE + 2) == nv.NVFP4_ERR_NO_DEVICE      # any element-aligned layout is accepted
+
+
+def test_rht_validation():
+    args = (FAKE, nv.NVFP4_IN_BF16, 32, 64, 64)
+    tail = (FAKE, FAKE, FAKE, nv.NVFP4_G_COMPUTE, FAKE, 1 << 16, None)
+    assert nv.lib.nvfp4_quantize_rht(*args, 1 << 16, *tail) == nv.NVFP4_ERR_INVALID_ARG
+    assert "16-bit" in nv.last_error()
+    assert nv.lib.nvfp4_quantize_t_rht(*args, 0x12345, *tail) == nv.NVFP4_ERR_INVALID_ARG
+    assert nv.lib.nvfp4_quantize_rht(FAKE, nv.NVFP4_IN_BF16, 32, 40, 40, 7, *tail) == nv.NVFP4_ERR_SHAPE
+    assert nv.lib.nvfp4_quantize_t_rht(FAKE, nv.NVFP4_IN_BF16, 40, 64, 64, 7, *tail) == nv.NVFP4_ERR_SHAPE
+    if _no_gpu():
+        assert nv.lib.nvfp4_quantize_rht(*args, 0xFFFF, *tail) == nv.NVFP4_ERR_NO_DEVICE
+        assert nv.lib.nvfp4_quantize_t_rht(*args, 0, *tail) == nv.NVFP4_ERR_NO_DEVICE
 
 
 def test_workspace_query():

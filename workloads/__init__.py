@@ -192,6 +192,12 @@ def make(name: str, **kw) -> Workload:
     return MAKERS[name](**kw)
 
 
+def rht_signs(seed: int = 606) -> int:
+    """A seeded random 16-bit sign mask for the randomized Hadamard transform (the method's random draw,
+    passed to both sides as an input)."""
+    return int(_rng(np.random.SeedSequence(seed)).integers(0, 1 << 16))
+
+
 def random_matrix(seed: int, rows: int, cols: int, scale: float = 1.0, dtype: str = "f32") -> np.ndarray:
     """A plain seeded N(0, scale^2) matrix for edge-case tests (FP32, or bf16-exact FP32 values)."""
     a = np.float32(scale) * _rng(np.random.SeedSequence(seed)).standard_normal((rows, cols), dtype=np.float32)
