@@ -101,7 +101,7 @@ def main():
     small = name in ("tiny", "decode")
     steps = args.steps if args.steps is not None else (2000 if small else 20)
     # the big products keep speeding up over their first ~15 launches (clocks settle), so warm up past that
-    warmup = args.warmup if args.warmup is not None else (200 if small else 20)
+    warmup = args.warmup if args.warmup is not None else (200 if small else 50)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
@@ -121,6 +121,13 @@ def main():
     packed = nv.PackedWeight(mods, K)
     copies = 40 if name == "decode" else 1
     weights = [packed] + [packed.clone() for _ in range(copies - 1)]
+    # the standard transformer's NVFP4 recipe (randomized Hadamard transform before quantization, g computed),
+    # which nGPT does without: both operands transformed with the same signs, weights packed once
+    rht_on = name in ("ngpt", "gdn")
+    if rht_on:
+        signs = workloads.rht_signs()
+        packed_rht = nv.PackedWeight([nv.quantize_rht(w, signs) for w in w_dev], K)
+    w_first = w_dev[0] if name == "ngpt" else None     # the nGPT backward reads W
     if not wl.quantize_w_in_step:
         del w_dev
     torch.cuda.synchronize()
@@ -173,7 +180,7 @@ def main():
     if name == "ngpt":
         dy_np = workloads.random_matrix(workloads.SEEDS["ngpt"] + 7, M, N, 1e-3, "bf16")
         dy = torch.from_numpy(dy_np).to(dev).to(torch.bfloat16)
-        w_full = w_dev[0] if wl.quantize_w_in_step else torch.from_numpy(wl.w[0]).to(dev).to(torch.bfloat16)
+        w_full = w_first
 
         def qbufs(rows, kdim):
             return (*nv.empty_quantized(rows, kdim, dev),
@@ -199,6 +206,17 @@ def main():
         def quant_t_only(i):
             nv.nvfp4_quantize_t(x, *xt[:3], nv.NVFP4_G_COMPUTE, xt[3])
         bwd = (step_backward, quant_t_only)
+
+    if rht_on:
+        codes_r, scales_r, g_r = nv.empty_quantized(M, K, dev)
+        y_r = torch.empty((M, N), dtype=torch.float32, device=dev)
+
+        def step_rht(i):
+            nv.nvfp4_quantize_rht(x, signs, codes_r, scales_r, g_r, nv.NVFP4_G_COMPUTE, ws)
+            nv.nvfp4_gemm(M, codes_r, scales_r, g_r, packed_rht.desc, y_r, N, gemm_ws)
+
+        def quant_rht_only(i):
+            nv.nvfp4_quantize_rht(x, signs, codes_r, scales_r, g_r, nv.NVFP4_G_COMPUTE, ws)
 
     def gemm_only(i):
         nv.nvfp4_gemm(M, codes, scales, g, weights[i % copies].desc, y, N, gemm_ws)
@@ -257,6 +275,8 @@ def main():
     t_quant = timed(quant_only, k_steps, min(warmup, k_steps)) / k_steps
     t_given = timed(step_given, k_steps, min(warmup, k_steps)) / k_steps
     t_gated = timed(step_gated, k_steps, min(warmup, k_steps)) / k_steps if gate_p is not None else None
+    t_rht = timed(step_rht, k_steps, min(warmup, k_steps)) / k_steps if rht_on else None
+    t_qrht = timed(quant_rht_only, k_steps, min(warmup, k_steps)) / k_steps if rht_on else None
     t_bwd = timed(bwd[0], k_steps, min(warmup, k_steps)) / k_steps if bwd else None
     t_qt = timed(bwd[1], k_steps, min(warmup, k_steps)) / k_steps if bwd else None
 
@@ -315,6 +335,28 @@ def main():
         gcols = torch.arange(gate_p.a_col, gate_p.b_col + gate_p.n_b, device=dev)
         got = yg[torch.from_numpy(rows).to(dev)][:, gcols].cpu().numpy()
         gated_ok, gated_worst = gref.within(got, gref.apply_gates(yab, *gargs), gref.gates_tolerance(yab, aab, *gargs))
+    rht_parity = None
+    if rht_on:   # sampled rows of the transformed codes, and of the product against the transformed weights
+        from oracle import rht as rref
+        tx = rref.rht_blocks(wl.x, signs)
+        g_t = ref.global_scale(np.float32(np.abs(tx).max()))
+        txq = ref.quantize(tx[rows], "given", g_t)
+        del tx
+        rsel = torch.from_numpy(rows).to(dev)
+        r_codes_ok = bool(np.array_equal(codes_r[rsel].cpu().numpy(), txq.codes) and
+                          np.array_equal(scales_r[rsel].cpu().numpy(), txq.scales) and np.float32(g_r.item()) == g_t)
+        parts_r, off = [], 0
+        for w in wl.w:
+            sel = cols[(cols >= off) & (cols < off + w.shape[0])] - off
+            if len(sel):
+                tw = rref.rht_blocks(w, signs)
+                parts_r.append(ref.dequantize(ref.quantize(tw[sel], "given",
+                                                           ref.global_scale(np.float32(np.abs(tw).max())))))
+            off += w.shape[0]
+        yr_ref, ar_ref = ref.gemm_dequantized(ref.dequantize(txq), np.concatenate(parts_r))
+        yr = y_r[rsel][:, torch.from_numpy(cols).to(dev)].cpu().numpy()
+        r_ok, r_worst = ref.gemm_within_tolerance(yr, yr_ref, ar_ref)
+        rht_parity = {"codes_scales_bit_exact": r_codes_ok, "gemm_within_1e-5": bool(r_ok), "worst_ratio": r_worst}
     bwd_parity = None
     if bwd:   # sampled entries of dX and dW, and sampled rows of the transposed encodings, against the oracle
         rsel = torch.from_numpy(rows).to(dev)
@@ -370,6 +412,9 @@ def main():
                               "step with g given (no amax pass)": t_given * 1e6,
                               "tflops with g given": flops / t_given / 1e12,
                               "step with GDN gates fused": t_gated * 1e6 if t_gated else None,
+                              "step with RHT (both operands transformed, g computed)":
+                                  t_rht * 1e6 if t_rht else None,
+                              "quantize with RHT alone (g computed)": t_qrht * 1e6 if t_qrht else None,
                               "backward step (dX and dW, operands quantized and packed in the step)":
                                   t_bwd * 1e6 if t_bwd else None,
                               "backward tflops": 2.0 * flops / t_bwd / 1e12 if t_bwd else None,
@@ -380,7 +425,7 @@ def main():
         "parity": {"codes_scales_bit_exact": codes_ok, "gemm_within_1e-5": bool(y_ok), "worst_ratio": worst,
                    "g_given_codes_scales_bit_exact": given_ok,
                    "gdn_gates_within_bound": gated_ok, "gdn_gates_worst_ratio": gated_worst,
-                   "backward": bwd_parity,
+                   "backward": bwd_parity, "rht": rht_parity,
                    "rows_checked": int(len(rows)), "cols_checked": int(len(cols))},
     }
     print(json.dumps(out), flush=True)
