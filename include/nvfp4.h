@@ -81,6 +81,15 @@ typedef enum nvfp4_g_mode {
     NVFP4_G_GIVEN = 1
 } nvfp4_g_mode;
 
+/* Element type of the product's output Y. */
+typedef enum nvfp4_out_dtype {
+    NVFP4_OUT_F32 = 0,
+    /* bf16, rounded to nearest (ties to even) from the FP32 value the F32
+     * output would hold: half the bytes for a projection whose consumer reads
+     * bf16 (the GDN recurrence after the fused input projection). */
+    NVFP4_OUT_BF16 = 1
+} nvfp4_out_dtype;
+
 /* Library ABI version (NVFP4_ABI_VERSION of the build). */
 int nvfp4_abi_version(void);
 
@@ -337,6 +346,33 @@ nvfp4_status nvfp4_linear_gated(const void* x, int in_dtype, int64_t M, int64_t 
                                 uint8_t* x_scales, float* g_x, int g_mode, const nvfp4_weight_desc* w,
                                 const nvfp4_gdn_gates* gates, float* y, int64_t ld_y, void* workspace,
                                 size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Product with an output epilogue: the output type and, optionally, the GDN
+ * gates (section "The gates are shielded by their parameterization" of the
+ * Gated DeltaNet page; the projection's output feeds the recurrence).
+ *
+ * y_dtype : NVFP4_OUT_F32 or NVFP4_OUT_BF16 (else NVFP4_ERR_INVALID_ARG)
+ * reserved: must be 0
+ * gates   : NULL for none, else as for nvfp4_gemm_gated
+ * y, ld_y : device, M rows of ld_y elements of y_dtype (4- or 2-byte aligned)
+ * Everything else, workspace sizes included, as nvfp4_gemm / nvfp4_linear.
+ * A bf16 element is the round-to-nearest-even of the FP32 element the same
+ * call with NVFP4_OUT_F32 writes.
+ * ------------------------------------------------------------------------- */
+typedef struct nvfp4_epilogue {
+    int32_t y_dtype;
+    int32_t reserved;
+    const nvfp4_gdn_gates* gates;
+} nvfp4_epilogue;
+
+nvfp4_status nvfp4_gemm_ex(int64_t M, const uint8_t* a_codes, const uint8_t* a_scales, const float* g_x,
+                           const nvfp4_weight_desc* w, const nvfp4_epilogue* ep, void* y, int64_t ld_y,
+                           void* workspace, size_t workspace_bytes, void* stream);
+nvfp4_status nvfp4_linear_ex(const void* x, int in_dtype, int64_t M, int64_t ld_x, uint8_t* x_codes,
+                             uint8_t* x_scales, float* g_x, int g_mode, const nvfp4_weight_desc* w,
+                             const nvfp4_epilogue* ep, void* y, int64_t ld_y, void* workspace,
+                             size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

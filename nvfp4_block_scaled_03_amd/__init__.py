@@ -89,6 +89,24 @@ class GdnGates:
         self.desc = GdnGatesDesc(a_col, n_a, b_col, n_b, self.a_log.data_ptr(), self.dt_bias.data_ptr())
 
 
+NVFP4_OUT_F32 = 0
+NVFP4_OUT_BF16 = 1
+
+
+class EpilogueDesc(ctypes.Structure):
+    """Mirror of ``nvfp4_epilogue``."""
+    _fields_ = [("y_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32), ("gates", ctypes.c_void_p)]
+
+
+def _epilogue(y, gates):
+    """The nvfp4_epilogue for y's dtype and the optional gates (whose descriptor the caller keeps alive)."""
+    if y.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("y must be float32 or bfloat16")
+    ep = EpilogueDesc(NVFP4_OUT_BF16 if y.dtype == torch.bfloat16 else NVFP4_OUT_F32, 0,
+                      ctypes.addressof(gates.desc) if gates is not None else None)
+    return ep
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
@@ -119,6 +137,10 @@ def _load():
                                  c_i64, c_vp, c_sz, c_vp]),
         "nvfp4_gemm_gated": (c_int, [c_i64, c_vp, c_vp, c_vp, ctypes.POINTER(WeightDesc),
                                      ctypes.POINTER(GdnGatesDesc), c_vp, c_i64, c_vp, c_sz, c_vp]),
+        "nvfp4_gemm_ex": (c_int, [c_i64, c_vp, c_vp, c_vp, ctypes.POINTER(WeightDesc), ctypes.POINTER(EpilogueDesc),
+                                  c_vp, c_i64, c_vp, c_sz, c_vp]),
+        "nvfp4_linear_ex": (c_int, [c_vp, c_int, c_i64, c_i64, c_vp, c_vp, c_vp, c_int, ctypes.POINTER(WeightDesc),
+                                    ctypes.POINTER(EpilogueDesc), c_vp, c_i64, c_vp, c_sz, c_vp]),
         "nvfp4_linear_gated": (c_int, [c_vp, c_int, c_i64, c_i64, c_vp, c_vp, c_vp, c_int, ctypes.POINTER(WeightDesc),
                                        ctypes.POINTER(GdnGatesDesc), c_vp, c_i64, c_vp, c_sz, c_vp]),
     }
@@ -260,11 +282,15 @@ def nvfp4_gemm_workspace_bytes(M: int, desc: WeightDesc) -> int:
 
 def nvfp4_gemm(M: int, a_codes, a_scales, g_x, desc: WeightDesc, y, ld_y=None, workspace=None, stream=None,
                gates: "GdnGates | None" = None):
-    """nvfp4_gemm, or nvfp4_gemm_gated when gates are given."""
+    """nvfp4_gemm; nvfp4_gemm_gated when gates are given; nvfp4_gemm_ex when y is bfloat16."""
     if ld_y is None:
         ld_y = y.stride(0) if y.dim() == 2 and y.shape[0] > 1 else desc.n
     ws_bytes = workspace.numel() * workspace.element_size() if isinstance(workspace, torch.Tensor) else 0
-    if gates is None:
+    if y.dtype == torch.bfloat16:   # output epilogue entry point (bf16 Y, with or without gates)
+        ep = _epilogue(y, gates)
+        _check(_lib.nvfp4_gemm_ex(M, _ptr(a_codes), _ptr(a_scales), _ptr(g_x), ctypes.byref(desc), ctypes.byref(ep),
+                                  _ptr(y), ld_y, _ptr(workspace), ws_bytes, _stream(stream)))
+    elif gates is None:
         _check(_lib.nvfp4_gemm(M, _ptr(a_codes), _ptr(a_scales), _ptr(g_x), ctypes.byref(desc), _ptr(y), ld_y,
                                _ptr(workspace), ws_bytes, _stream(stream)))
     else:
@@ -280,7 +306,7 @@ def nvfp4_linear_workspace_bytes(M: int, in_dtype: int, desc: WeightDesc) -> int
 def nvfp4_linear(x, x_codes, x_scales, g_x, desc: WeightDesc, y, workspace, g_mode=NVFP4_G_COMPUTE, stream=None, *,
                  M=None, ld_x=None, in_dtype=None, ld_y=None, gates: "GdnGates | None" = None):
     """Quantize x [M, K] and multiply by a packed weight in one call (workspace zero-filled before first use);
-    nvfp4_linear_gated when gates are given."""
+    nvfp4_linear_gated when gates are given; nvfp4_linear_ex when y is bfloat16."""
     if M is None:
         M = x.shape[0]
         ld_x = x.stride(0) if M > 1 else x.shape[1]
@@ -288,7 +314,12 @@ def nvfp4_linear(x, x_codes, x_scales, g_x, desc: WeightDesc, y, workspace, g_mo
     if ld_y is None:
         ld_y = y.stride(0) if y.dim() == 2 and y.shape[0] > 1 else desc.n
     ws_bytes = workspace.numel() * workspace.element_size()
-    if gates is None:
+    if y.dtype == torch.bfloat16:   # output epilogue entry point (bf16 Y, with or without gates)
+        ep = _epilogue(y, gates)
+        _check(_lib.nvfp4_linear_ex(_ptr(x), in_dtype, M, ld_x, _ptr(x_codes), _ptr(x_scales), _ptr(g_x), g_mode,
+                                    ctypes.byref(desc), ctypes.byref(ep), _ptr(y), ld_y, _ptr(workspace), ws_bytes,
+                                    _stream(stream)))
+    elif gates is None:
         _check(_lib.nvfp4_linear(_ptr(x), in_dtype, M, ld_x, _ptr(x_codes), _ptr(x_scales), _ptr(g_x), g_mode,
                                  ctypes.byref(desc), _ptr(y), ld_y, _ptr(workspace), ws_bytes, _stream(stream)))
     else:
@@ -408,25 +439,26 @@ def linear_workspace(M: int, x_dtype, w: "PackedWeight", device="cuda") -> torch
     return torch.zeros((nvfp4_linear_workspace_bytes(M, in_dtype, w.desc),), dtype=torch.uint8, device=device)
 
 
-def linear(x: torch.Tensor, w: "PackedWeight", workspace=None, g=None, stream=None, gates=None):
-    """Y = NVFP4(x) . W^T in one call (through the GDN gate epilogue when gates are given);
-    returns (y, codes, scales, g)."""
+def linear(x: torch.Tensor, w: "PackedWeight", workspace=None, g=None, stream=None, gates=None,
+           out_dtype=torch.float32):
+    """Y = NVFP4(x) . W^T in one call (through the GDN gate epilogue when gates are given; Y in float32 or
+    bfloat16); returns (y, codes, scales, g)."""
     M, K = x.shape
     codes, scales, gt = empty_quantized(M, K, x.device)
     if g is not None:
         gt.fill_(float(g))
     if workspace is None:
         workspace = linear_workspace(M, x.dtype, w, x.device)
-    y = torch.empty((M, w.n), dtype=torch.float32, device=x.device)
+    y = torch.empty((M, w.n), dtype=out_dtype, device=x.device)
     nvfp4_linear(x, codes, scales, gt, w.desc, y, workspace, NVFP4_G_GIVEN if g is not None else NVFP4_G_COMPUTE,
                  stream, gates=gates)
     return y, codes, scales, gt
 
 
-def gemm(a_codes, a_scales, g_x, w: PackedWeight, y=None, stream=None, gates=None):
+def gemm(a_codes, a_scales, g_x, w: PackedWeight, y=None, stream=None, gates=None, out_dtype=torch.float32):
     M = a_codes.shape[0]
     if y is None:
-        y = torch.empty((M, w.n), dtype=torch.float32, device=a_codes.device)
+        y = torch.empty((M, w.n), dtype=out_dtype, device=a_codes.device)
     ws_bytes = nvfp4_gemm_workspace_bytes(M, w.desc)
     ws = torch.zeros((ws_bytes,), dtype=torch.uint8, device=a_codes.device) if ws_bytes else None
     nvfp4_gemm(M, a_codes, a_scales, g_x, w.desc, y, None, ws, stream, gates=gates)

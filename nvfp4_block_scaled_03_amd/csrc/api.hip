@@ -283,7 +283,7 @@ size_t nvfp4_gemm_workspace_bytes(int64_t M, const nvfp4_weight_desc* w) {
 }
 
 static nvfp4_status gemm_impl(int64_t M, const uint8_t* a_codes, const uint8_t* a_scales, const float* g_x,
-                              const nvfp4_weight_desc* w, const nvfp4::GateParams& gp, float* y, int64_t ld_y,
+                              const nvfp4_weight_desc* w, const nvfp4::Epilogue& gp, void* y, int64_t ld_y,
                               void* workspace, size_t workspace_bytes, void* stream) {
     nvfp4_status st = check_desc(w);
     if (st != NVFP4_OK) return st;
@@ -295,21 +295,21 @@ static nvfp4_status gemm_impl(int64_t M, const uint8_t* a_codes, const uint8_t* 
     if (M > (int64_t(1) << 31) || ld_y > INT64_MAX / M) return fail(NVFP4_ERR_SHAPE, "M too large");
     if (M * w->k / 2 > nvfp4::kMaxCodeBytes)
         return fail(NVFP4_ERR_UNSUPPORTED, "activation codes above 2 GiB (M*K/2 = %lld)", (long long)(M * w->k / 2));
-    if (!aligned(a_codes, 16) || !aligned(a_scales, 4) || !aligned(y, 4))
-        return fail(NVFP4_ERR_UNSUPPORTED, "a_codes must be 16-byte and a_scales 4-byte aligned");
+    if (!aligned(a_codes, 16) || !aligned(a_scales, 4) || !aligned(y, gp.out_bf16 ? 2 : 4))
+        return fail(NVFP4_ERR_UNSUPPORTED, "a_codes must be 16-byte, a_scales 4-byte and y element aligned");
     const size_t need = nvfp4::gemm_workspace_bytes(M, *w);
     if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256)))
         return fail(NVFP4_ERR_WORKSPACE, "gemm workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
                     workspace_bytes);
     st = check_device();
     if (st != NVFP4_OK) return st;
-    return launched(nvfp4::launch_gemm(M, a_codes, a_scales, g_x, *w, y, ld_y, workspace, workspace_bytes, gp,
-                                       static_cast<hipStream_t>(stream)),
+    return launched(nvfp4::launch_gemm(M, a_codes, a_scales, g_x, *w, static_cast<float*>(y), ld_y, workspace,
+                                       workspace_bytes, gp, static_cast<hipStream_t>(stream)),
                     "gemm launch");
 }
 
 // Gate parameters -> the kernels' form, after checking them against the weight.
-static nvfp4_status gate_params(const nvfp4_gdn_gates* g, const nvfp4_weight_desc* w, nvfp4::GateParams& gp) {
+static nvfp4_status gate_params(const nvfp4_gdn_gates* g, const nvfp4_weight_desc* w, nvfp4::Epilogue& gp) {
     if (g == nullptr) return fail(NVFP4_ERR_INVALID_ARG, "gates is NULL");
     if (w == nullptr) return fail(NVFP4_ERR_INVALID_ARG, "w is NULL");
     if (g->n_a < 0 || g->n_b < 0 || g->a_col < 0 || g->b_col < 0 || g->a_col > w->n - g->n_a ||
@@ -334,7 +334,7 @@ static nvfp4_status gate_params(const nvfp4_gdn_gates* g, const nvfp4_weight_des
 nvfp4_status nvfp4_gemm(int64_t M, const uint8_t* a_codes, const uint8_t* a_scales, const float* g_x,
                         const nvfp4_weight_desc* w, float* y, int64_t ld_y, void* workspace, size_t workspace_bytes,
                         void* stream) {
-    return gemm_impl(M, a_codes, a_scales, g_x, w, nvfp4::GateParams{}, y, ld_y, workspace, workspace_bytes, stream);
+    return gemm_impl(M, a_codes, a_scales, g_x, w, nvfp4::Epilogue{}, y, ld_y, workspace, workspace_bytes, stream);
 }
 
 nvfp4_status nvfp4_gemm_gated(int64_t M, const uint8_t* a_codes, const uint8_t* a_scales, const float* g_x,
@@ -342,7 +342,7 @@ nvfp4_status nvfp4_gemm_gated(int64_t M, const uint8_t* a_codes, const uint8_t* 
                               void* workspace, size_t workspace_bytes, void* stream) {
     nvfp4_status st = check_desc(w);
     if (st != NVFP4_OK) return st;
-    nvfp4::GateParams gp;
+    nvfp4::Epilogue gp;
     st = gate_params(gates, w, gp);
     if (st != NVFP4_OK) return st;
     return gemm_impl(M, a_codes, a_scales, g_x, w, gp, y, ld_y, workspace, workspace_bytes, stream);
@@ -356,8 +356,9 @@ size_t nvfp4_linear_workspace_bytes(int64_t M, int in_dtype, const nvfp4_weight_
 
 static nvfp4_status linear_impl(const void* x, int in_dtype, int64_t M, int64_t ld_x, uint8_t* x_codes,
                                 uint8_t* x_scales, float* g_x, int g_mode, const nvfp4_weight_desc* w,
-                                const nvfp4::GateParams& gp, float* y, int64_t ld_y, void* workspace,
+                                const nvfp4::Epilogue& gp, void* y_out, int64_t ld_y, void* workspace,
                                 size_t workspace_bytes, void* stream) {
+    float* y = static_cast<float*>(y_out);   // bf16 storage when gp.out_bf16 (the kernels store through store_y)
     nvfp4_status st = check_desc(w);
     if (st != NVFP4_OK) return st;
     const int64_t K = w->k;
@@ -379,8 +380,8 @@ static nvfp4_status linear_impl(const void* x, int in_dtype, int64_t M, int64_t 
         const int esize = in_dtype == NVFP4_IN_BF16 ? 2 : 4;
         if (!aligned(x, 16) || (ld_x * esize) % 16 != 0)
             return fail(NVFP4_ERR_UNSUPPORTED, "x must be 16-byte aligned with a 16-byte multiple row stride");
-        if (!aligned(x_codes, 16) || !aligned(x_scales, 4) || !aligned(y, 4))
-            return fail(NVFP4_ERR_UNSUPPORTED, "x_codes must be 16-byte and x_scales 4-byte aligned");
+        if (!aligned(x_codes, 16) || !aligned(x_scales, 4) || !aligned(y, gp.out_bf16 ? 2 : 4))
+            return fail(NVFP4_ERR_UNSUPPORTED, "x_codes must be 16-byte, x_scales 4-byte and y element aligned");
     }
     const size_t need = nvfp4_linear_workspace_bytes(M, in_dtype, w);
     if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256)))
@@ -413,8 +414,44 @@ static nvfp4_status linear_impl(const void* x, int in_dtype, int64_t M, int64_t 
 nvfp4_status nvfp4_linear(const void* x, int in_dtype, int64_t M, int64_t ld_x, uint8_t* x_codes, uint8_t* x_scales,
                           float* g_x, int g_mode, const nvfp4_weight_desc* w, float* y, int64_t ld_y,
                           void* workspace, size_t workspace_bytes, void* stream) {
-    return linear_impl(x, in_dtype, M, ld_x, x_codes, x_scales, g_x, g_mode, w, nvfp4::GateParams{}, y, ld_y,
+    return linear_impl(x, in_dtype, M, ld_x, x_codes, x_scales, g_x, g_mode, w, nvfp4::Epilogue{}, y, ld_y,
                        workspace, workspace_bytes, stream);
+}
+
+// Epilogue descriptor -> the kernels' form.
+static nvfp4_status epilogue(const nvfp4_epilogue* ep, const nvfp4_weight_desc* w, nvfp4::Epilogue& out) {
+    if (ep == nullptr) return fail(NVFP4_ERR_INVALID_ARG, "epilogue is NULL");
+    if (ep->y_dtype != NVFP4_OUT_F32 && ep->y_dtype != NVFP4_OUT_BF16)
+        return fail(NVFP4_ERR_INVALID_ARG, "unknown output dtype %d", ep->y_dtype);
+    if (ep->reserved != 0) return fail(NVFP4_ERR_INVALID_ARG, "epilogue.reserved must be 0");
+    nvfp4_status st = check_desc(w);
+    if (st != NVFP4_OK) return st;
+    if (ep->gates != nullptr) {
+        st = gate_params(ep->gates, w, out);
+        if (st != NVFP4_OK) return st;
+    }
+    out.out_bf16 = ep->y_dtype == NVFP4_OUT_BF16;
+    return NVFP4_OK;
+}
+
+nvfp4_status nvfp4_gemm_ex(int64_t M, const uint8_t* a_codes, const uint8_t* a_scales, const float* g_x,
+                           const nvfp4_weight_desc* w, const nvfp4_epilogue* ep, void* y, int64_t ld_y,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+    nvfp4::Epilogue e;
+    nvfp4_status st = epilogue(ep, w, e);
+    if (st != NVFP4_OK) return st;
+    return gemm_impl(M, a_codes, a_scales, g_x, w, e, y, ld_y, workspace, workspace_bytes, stream);
+}
+
+nvfp4_status nvfp4_linear_ex(const void* x, int in_dtype, int64_t M, int64_t ld_x, uint8_t* x_codes,
+                             uint8_t* x_scales, float* g_x, int g_mode, const nvfp4_weight_desc* w,
+                             const nvfp4_epilogue* ep, void* y, int64_t ld_y, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+    nvfp4::Epilogue e;
+    nvfp4_status st = epilogue(ep, w, e);
+    if (st != NVFP4_OK) return st;
+    return linear_impl(x, in_dtype, M, ld_x, x_codes, x_scales, g_x, g_mode, w, e, y, ld_y, workspace,
+                       workspace_bytes, stream);
 }
 
 nvfp4_status nvfp4_linear_gated(const void* x, int in_dtype, int64_t M, int64_t ld_x, uint8_t* x_codes,
@@ -423,7 +460,7 @@ nvfp4_status nvfp4_linear_gated(const void* x, int in_dtype, int64_t M, int64_t 
                                 size_t workspace_bytes, void* stream) {
     nvfp4_status st = check_desc(w);
     if (st != NVFP4_OK) return st;
-    nvfp4::GateParams gp;
+    nvfp4::Epilogue gp;
     st = gate_params(gates, w, gp);
     if (st != NVFP4_OK) return st;
     return linear_impl(x, in_dtype, M, ld_x, x_codes, x_scales, g_x, g_mode, w, gp, y, ld_y, workspace,

@@ -294,20 +294,37 @@ hipError_t launch_unpack(const nvfp4_weight_desc& d, uint8_t* codes, uint8_t* sc
 // decay exp(-exp(A) * softplus(y + bias)) of their head, columns
 // [b_col, b_col + n_b) the write strength sigmoid(y).  The kernels take it as a
 // compile-time option, so products without gates carry none of it.
-struct GateParams {
+struct Epilogue {
     int32_t a_col = 0, n_a = 0, b_col = 0, n_b = 0;   // columns fit 31 bits (the packed weight is <= 2 GiB)
     const float* a_log = nullptr;
     const float* dt_bias = nullptr;
+    int32_t out_bf16 = 0;                             // Y as bf16 (round to nearest even) instead of FP32
 };
 
+// FP32 -> bf16 bits, round to nearest with ties to even (NaN stays a quiet NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float v) {
+    const uint32_t u = __float_as_uint(v);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
+    return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+// One output element: FP32, or bf16 when the epilogue asks for it (y then
+// points at bf16 storage and idx counts bf16 elements).
+__device__ __forceinline__ void store_y(float* y, int64_t idx, float v, const Epilogue& ep) {
+    if (ep.out_bf16)
+        reinterpret_cast<uint16_t*>(y)[idx] = f32_to_bf16_rne(v);
+    else
+        y[idx] = v;
+}
+
 // Whether any column of [n0, n1) is a gate column (wave-uniform when n0, n1 are).
-__device__ __forceinline__ bool gates_touch(int64_t n0, int64_t n1, const GateParams& gp) {
+__device__ __forceinline__ bool gates_touch(int64_t n0, int64_t n1, const Epilogue& gp) {
     return (gp.n_a > 0 && n0 < gp.a_col + gp.n_a && gp.a_col < n1) ||
            (gp.n_b > 0 && n0 < gp.b_col + gp.n_b && gp.b_col < n1);
 }
 
 // FP32, with softplus and the sigmoid in forms that cannot overflow.
-__device__ __forceinline__ float gate(float y, int64_t n, const GateParams& gp) {
+__device__ __forceinline__ float gate(float y, int64_t n, const Epilogue& gp) {
     const uint32_t ha = (uint32_t)((int32_t)n - gp.a_col), hb = (uint32_t)((int32_t)n - gp.b_col);
     if (ha < (uint32_t)gp.n_a) {
         const float z = y + gp.dt_bias[ha];
@@ -324,7 +341,7 @@ __device__ __forceinline__ float gate(float y, int64_t n, const GateParams& gp) 
 size_t gemm_workspace_bytes(int64_t M, const nvfp4_weight_desc& d);
 hipError_t launch_gemm(int64_t M, const uint8_t* a_codes, const uint8_t* a_scales, const float* g_x,
                        const nvfp4_weight_desc& d, float* y, int64_t ld_y, void* ws, size_t ws_bytes,
-                       const GateParams& gp, hipStream_t stream);
+                       const Epilogue& gp, hipStream_t stream);
 
 // Few-token products (skinny.hip).  The workspace starts with one 32-bit counter
 // per 64-row weight group, which must be zero before first use (each call
@@ -333,6 +350,6 @@ bool skinny_applies(int64_t M, const nvfp4_weight_desc& d);
 size_t skinny_workspace_bytes(const nvfp4_weight_desc& d);
 hipError_t launch_skinny(int64_t M, const void* x, int in_dtype, int64_t ld_x, float* g_x, int g_mode,
                          uint8_t* x_codes, uint8_t* x_scales, bool quantize, const nvfp4_weight_desc& d, float* y,
-                         int64_t ld_y, void* ws, const GateParams& gp, hipStream_t stream);
+                         int64_t ld_y, void* ws, const Epilogue& gp, hipStream_t stream);
 
 }  // namespace nvfp4

@@ -398,10 +398,10 @@ __device__ __forceinline__ void tile_product(float16v (&acc)[TM][TN], uint8_t* c
     wait_vmem<0>();   // the zero loads past the end, before the stages are reused
 }
 
-template <int TM, int TN, bool GATED>
+template <int TM, int TN, bool GATED, bool EPI>
 __device__ __forceinline__ void store_tile_cols(const float16v (&acc)[TM][TN], int tm, int tn, int64_t M, int64_t N,
                                                 const float* __restrict__ g_x, const float* __restrict__ colscale,
-                                                float* __restrict__ y, int64_t ld_y, const GateParams& gp, int wm,
+                                                float* __restrict__ y, int64_t ld_y, const Epilogue& gp, int wm,
                                                 int wn, int lane) {
     using G = TileGeom<TM, TN>;
     const int l32 = lane & 31, h = lane >> 5;
@@ -420,29 +420,34 @@ __device__ __forceinline__ void store_tile_cols(const float16v (&acc)[TM][TN], i
                 if (m < M) {
                     float v = acc[i][j][r] * cs;
                     if constexpr (GATED) v = gate(v, n, gp);
-                    y[m * ld_y + n] = v;
+                    if constexpr (EPI)
+                        store_y(y, m * ld_y + n, v, gp);
+                    else
+                        y[m * ld_y + n] = v;
                 }
             }
         }
     }
 }
 
-// Y = acc * g_x * colscale for one tile (rows >= M and columns >= N skipped),
-// through the gate epilogue.
-template <int TM, int TN, bool GATED>
+// Y = acc * g_x * colscale for one tile (rows >= M and columns >= N skipped);
+// EPI: through the general epilogue (gates where the tile holds gate columns,
+// FP32 or bf16 output), else plain FP32 stores.
+template <int TM, int TN, bool EPI>
 __device__ __forceinline__ void store_tile(const float16v (&acc)[TM][TN], int tm, int tn, int64_t M, int64_t N,
                                            const float* __restrict__ g_x, const float* __restrict__ colscale,
-                                           float* __restrict__ y, int64_t ld_y, const GateParams& gp, int wm, int wn,
+                                           float* __restrict__ y, int64_t ld_y, const Epilogue& gp, int wm, int wn,
                                            int lane) {
     using G = TileGeom<TM, TN>;
-    if constexpr (GATED) {
+    if constexpr (EPI) {
         // only the tiles that hold gate columns take the gated stores
-        if (gates_touch((int64_t)tn * G::BN, (int64_t)(tn + 1) * G::BN, gp)) {
-            store_tile_cols<TM, TN, true>(acc, tm, tn, M, N, g_x, colscale, y, ld_y, gp, wm, wn, lane);
-            return;
-        }
+        if (gates_touch((int64_t)tn * G::BN, (int64_t)(tn + 1) * G::BN, gp))
+            store_tile_cols<TM, TN, true, true>(acc, tm, tn, M, N, g_x, colscale, y, ld_y, gp, wm, wn, lane);
+        else
+            store_tile_cols<TM, TN, false, true>(acc, tm, tn, M, N, g_x, colscale, y, ld_y, gp, wm, wn, lane);
+        return;
     }
-    store_tile_cols<TM, TN, false>(acc, tm, tn, M, N, g_x, colscale, y, ld_y, gp, wm, wn, lane);
+    store_tile_cols<TM, TN, false, false>(acc, tm, tn, M, N, g_x, colscale, y, ld_y, gp, wm, wn, lane);
 }
 
 #define NVFP4_TILE_KERNEL_ARGS                                                                                   \
@@ -452,8 +457,8 @@ __device__ __forceinline__ void store_tile(const float16v (&acc)[TM][TN], int tm
         int64_t ld_y
 
 // One whole tile per workgroup.
-template <int TM, int TN, bool GATED>
-__global__ __launch_bounds__(256) void gemm_tile_kernel(NVFP4_TILE_KERNEL_ARGS, GateParams gp, int tiles_m,
+template <int TM, int TN, bool EPI>
+__global__ __launch_bounds__(256) void gemm_tile_kernel(NVFP4_TILE_KERNEL_ARGS, Epilogue gp, int tiles_m,
                                                         int tiles_n) {
     using G = TileGeom<TM, TN>;
     // Four separate arrays rather than one: the compiler then tells the stages
@@ -472,7 +477,7 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(NVFP4_TILE_KERNEL_ARGS, 
     point_at<TM, TN>(s, tm, tn, 0);
     float16v acc[TM][TN];
     tile_product<TM, TN>(acc, stg, s, (uint32_t)(K / kPackK), wave, wm, wn, lane);
-    store_tile<TM, TN, GATED>(acc, tm, tn, M, N, g_x, colscale, y, ld_y, gp, wm, wn, lane);
+    store_tile<TM, TN, EPI>(acc, tm, tn, M, N, g_x, colscale, y, ld_y, gp, wm, wn, lane);
 }
 
 // Host side.  Time per round of workgroups, relative: a round of 128 x 128
@@ -494,7 +499,7 @@ size_t gemm_workspace_bytes(int64_t M, const nvfp4_weight_desc& d) {
 
 template <int TM, int TN>
 static hipError_t launch_tiles(int64_t M, const uint8_t* a_codes, const uint8_t* a_scales, const float* g_x,
-                               const nvfp4_weight_desc& d, float* y, int64_t ld_y, const GateParams& gp,
+                               const nvfp4_weight_desc& d, float* y, int64_t ld_y, const Epilogue& gp,
                                hipStream_t stream) {
     constexpr int BM = 64 * TM, BN = 64 * TN;
     const uint8_t* blob = static_cast<const uint8_t*>(d.blob);
@@ -502,14 +507,15 @@ static hipError_t launch_tiles(int64_t M, const uint8_t* a_codes, const uint8_t*
     const uint8_t* wsc = blob + d.scales_offset;
     const float* cs = reinterpret_cast<const float*>(blob + d.colscale_offset);
     const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)(d.n_padded / BN);
-    auto kern = (gp.n_a > 0 || gp.n_b > 0) ? gemm_tile_kernel<TM, TN, true> : gemm_tile_kernel<TM, TN, false>;
+    const bool epi = gp.n_a > 0 || gp.n_b > 0 || gp.out_bf16;
+    auto kern = epi ? gemm_tile_kernel<TM, TN, true> : gemm_tile_kernel<TM, TN, false>;
     hipLaunchKernelGGL(kern, dim3(tiles_m * tiles_n), dim3(256), 0, stream, M, a_codes,
                        a_scales, g_x, wc, wsc, cs, d.n, d.n_padded, d.k, y, ld_y, gp, tiles_m, tiles_n);
     return hipGetLastError();
 }
 
 hipError_t launch_gemm(int64_t M, const uint8_t* a_codes, const uint8_t* a_scales, const float* g_x,
-                       const nvfp4_weight_desc& d, float* y, int64_t ld_y, void* ws, size_t, const GateParams& gp,
+                       const nvfp4_weight_desc& d, float* y, int64_t ld_y, void* ws, size_t, const Epilogue& gp,
                        hipStream_t stream) {
     if (skinny_applies(M, d)) {
         return launch_skinny(M, nullptr, NVFP4_IN_BF16, 0, const_cast<float*>(g_x), NVFP4_G_GIVEN,

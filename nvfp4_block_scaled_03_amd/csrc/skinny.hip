@@ -74,13 +74,13 @@ __device__ __forceinline__ void put_block(uint8_t* lds, int kb, int m, bool vali
     *reinterpret_cast<half8*>(lds + o1) = hi;
 }
 
-template <typename T, int NKSL, int R, bool QUANT, bool PRE, bool GATED>
+template <typename T, int NKSL, int R, bool QUANT, bool PRE, bool EPI>
 __global__ __launch_bounds__(R * 64) void skinny_kernel(
     int M, int64_t K, const T* __restrict__ x, int64_t ld_x, float* __restrict__ g_x, int g_given,
     uint8_t* __restrict__ x_codes, uint8_t* __restrict__ x_scales, const uint8_t* __restrict__ w_codes,
     const uint8_t* __restrict__ w_scales, const float* __restrict__ colscale, int64_t N, int64_t n_pad,
     float* __restrict__ y, int64_t ld_y, uint32_t* __restrict__ counters, uint32_t* __restrict__ slots,
-    float* __restrict__ partials, int S, int amax_polls, GateParams gp) {
+    float* __restrict__ partials, int S, int amax_polls, Epilogue gp) {
     constexpr int kThreads = R * 64;
     constexpr int kXhatBytes = NKSL * 4 * 64 * 16;
     constexpr int kD = NKSL < kDepth ? NKSL : kDepth;
@@ -299,15 +299,18 @@ __global__ __launch_bounds__(R * 64) void skinny_kernel(
     // Lane holds rows 4*kg..4*kg+3 of block nb for token r16.
     const int64_t n_base = (int64_t)nb * 16 + kg * 4;
     bool gated = false;   // only the row blocks that hold gate columns take the gated stores
-    if constexpr (GATED) gated = gates_touch((int64_t)nb * 16, (int64_t)nb * 16 + 16, gp);
+    if constexpr (EPI) gated = gates_touch((int64_t)nb * 16, (int64_t)nb * 16 + 16, gp);
     if (S == 1) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int64_t n = n_base + r;
             if (r16 < M && n < N) {
                 float v = acc[r] * (gx * csv[r]);
-                if (GATED && gated) v = gate(v, n, gp);
-                y[(int64_t)r16 * ld_y + n] = v;
+                if (EPI && gated) v = gate(v, n, gp);
+                if constexpr (EPI)
+                    store_y(y, (int64_t)r16 * ld_y + n, v, gp);
+                else
+                    y[(int64_t)r16 * ld_y + n] = v;
             }
         }
         return;
@@ -376,8 +379,11 @@ __global__ __launch_bounds__(R * 64) void skinny_kernel(
         const int64_t n = n_base + r;
         if (r16 < M && n < N) {
             float v = sum[r] * (gx * csv[r]);
-            if (GATED && gated) v = gate(v, n, gp);
-            y[(int64_t)r16 * ld_y + n] = v;
+            if (EPI && gated) v = gate(v, n, gp);
+            if constexpr (EPI)
+                    store_y(y, (int64_t)r16 * ld_y + n, v, gp);
+                else
+                    y[(int64_t)r16 * ld_y + n] = v;
         }
     }
     const v4i zero = {0, 0, 0, 0};
@@ -456,14 +462,15 @@ struct SkinnyArgs {
     float* partials;
     int S;
     int amax_polls;
-    GateParams gp;
-    bool gated;
+    Epilogue gp;
+    bool epi;
 };
 
 template <typename T, int NKSL, int R, bool QUANT>
 void launch_one(dim3 grid, hipStream_t stream, const SkinnyArgs& a) {
     constexpr bool kPre = QUANT && NKSL <= kMaxPre / sizeof(T) * 2;
-    auto kern = a.gated ? skinny_kernel<T, NKSL, R, QUANT, kPre, true> : skinny_kernel<T, NKSL, R, QUANT, kPre, false>;
+    // the general epilogue (gates, bf16 output) only where asked for: the plain kernel keeps its registers
+    auto kern = a.epi ? skinny_kernel<T, NKSL, R, QUANT, kPre, true> : skinny_kernel<T, NKSL, R, QUANT, kPre, false>;
     hipLaunchKernelGGL(kern, grid, dim3(R * 64), 0, stream, a.M, a.K, static_cast<const T*>(a.x), a.ld_x, a.g_x, a.g_given, a.x_codes, a.x_scales,
                        a.wc, a.wsc, a.cs, a.N, a.n_pad, a.y, a.ld_y, a.counters, a.slots, a.partials, a.S,
                        a.amax_polls, a.gp);
@@ -514,7 +521,7 @@ size_t skinny_workspace_bytes(const nvfp4_weight_desc& d) {
 
 hipError_t launch_skinny(int64_t M, const void* x, int in_dtype, int64_t ld_x, float* g_x, int g_mode,
                          uint8_t* x_codes, uint8_t* x_scales, bool quantize, const nvfp4_weight_desc& d, float* y,
-                         int64_t ld_y, void* ws, const GateParams& gp, hipStream_t stream) {
+                         int64_t ld_y, void* ws, const Epilogue& gp, hipStream_t stream) {
     const SkinnyPlan p = plan_for(d);
     if (!p.ok()) return hipErrorInvalidValue;
     const uint8_t* blob = static_cast<const uint8_t*>(d.blob);
@@ -539,7 +546,7 @@ hipError_t launch_skinny(int64_t M, const void* x, int in_dtype, int64_t ld_x, f
     a.partials = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + counters_bytes(p));
     a.S = p.S;
     a.gp = gp;
-    a.gated = gp.n_a > 0 || gp.n_b > 0;
+    a.epi = gp.n_a > 0 || gp.n_b > 0 || gp.out_bf16;
     a.amax_polls = kAmaxSpin;
     if (const char* e = std::getenv("NVFP4_AMAX_POLLS")) a.amax_polls = std::atoi(e);   // testing the fallback
     if (!quantize) return launch_plan<uint16_t, false>(p, stream, a);

@@ -39,7 +39,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for required in ["nvfp4_quantize", "nvfp4_pack_weights", "nvfp4_gemm", "nvfp4_last_error",
                      "nvfp4_quantize_workspace_bytes", "nvfp4_packed_weight_bytes", "nvfp4_unpack_weights",
-                     "nvfp4_gemm_workspace_bytes", "nvfp4_abi_version", "nvfp4_device_check", "nvfp4_quantize_t", "nvfp4_quantize_rht", "nvfp4_quantize_t_rht"]:
+                     "nvfp4_gemm_workspace_bytes", "nvfp4_abi_version", "nvfp4_device_check", "nvfp4_quantize_t", "nvfp4_quantize_rht", "nvfp4_quantize_t_rht",
+                     "nvfp4_gemm_ex", "nvfp4_linear_ex"]:
         assert required in names
 
 
@@ -315,3 +316,28 @@ def test_gated_validation():
         assert gg() == nv.NVFP4_ERR_NO_DEVICE
         assert nv.lib.nvfp4_linear_gated(FAKE, nv.NVFP4_IN_BF16, 16, d.k, FAKE, FAKE, FAKE, 0, ctypes.byref(d),
                                          ctypes.byref(g), FAKE, d.n, FAKE, 1 << 30, None) == nv.NVFP4_ERR_NO_DEVICE
+
+
+def test_epilogue_validation():
+    """The output epilogue (y type, reserved field, gates) is checked on the host before any launch."""
+    d = make_desc()
+    g = nv.GdnGatesDesc(0, 4, 8, 4, FAKE, FAKE)
+
+    def ge(y_dtype=nv.NVFP4_OUT_BF16, reserved=0, gates=None, y=FAKE, ep=True):
+        e = nv.EpilogueDesc(y_dtype, reserved, ctypes.addressof(gates) if gates is not None else None)
+        return nv.lib.nvfp4_gemm_ex(32, FAKE, FAKE, FAKE, ctypes.byref(d), ctypes.byref(e) if ep else None, y, d.n,
+                                    None, 0, None)
+    assert ge(ep=False) == nv.NVFP4_ERR_INVALID_ARG
+    assert ge(y_dtype=2) == nv.NVFP4_ERR_INVALID_ARG
+    assert ge(reserved=1) == nv.NVFP4_ERR_INVALID_ARG
+    assert ge(gates=nv.GdnGatesDesc(0, 4, 2, 4, FAKE, FAKE)) == nv.NVFP4_ERR_SHAPE   # overlapping gate columns
+    assert ge(y=FAKE + 1) == nv.NVFP4_ERR_UNSUPPORTED                                 # bf16 y needs 2-byte alignment
+    assert ge(y_dtype=nv.NVFP4_OUT_F32, y=FAKE + 2) == nv.NVFP4_ERR_UNSUPPORTED       # FP32 y needs 4
+    e = nv.EpilogueDesc(nv.NVFP4_OUT_BF16, 0, None)
+    assert nv.lib.nvfp4_linear_ex(FAKE, nv.NVFP4_IN_BF16, 16, d.k, FAKE, FAKE, FAKE, 0, ctypes.byref(d), None,
+                                  FAKE, d.n, FAKE, 1 << 30, None) == nv.NVFP4_ERR_INVALID_ARG
+    if _no_gpu():
+        assert ge(y=FAKE + 2) == nv.NVFP4_ERR_NO_DEVICE
+        assert ge(gates=g) == nv.NVFP4_ERR_NO_DEVICE
+        assert nv.lib.nvfp4_linear_ex(FAKE, nv.NVFP4_IN_BF16, 16, d.k, FAKE, FAKE, FAKE, 0, ctypes.byref(d),
+                                      ctypes.byref(e), FAKE + 2, d.n, FAKE, 1 << 30, None) == nv.NVFP4_ERR_NO_DEVICE
