@@ -218,6 +218,14 @@ def main():
         def quant_rht_only(i):
             nv.nvfp4_quantize_rht(x, signs, codes_r, scales_r, g_r, nv.NVFP4_G_COMPUTE, ws)
 
+    # the same layer writing Y as bf16 (with the gates for the GDN projection, whose output feeds the recurrence)
+    y_b = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    codes_b, scales_b, g_b = nv.empty_quantized(M, K, dev)
+
+    def step_bf16(i):
+        nv.nvfp4_linear(x, codes_b, scales_b, g_b, weights[i % copies].desc, y_b, lin_ws, M=M, ld_x=K,
+                        in_dtype=in_dtype, ld_y=N, gates=gates if gate_p is not None else None)
+
     def gemm_only(i):
         nv.nvfp4_gemm(M, codes, scales, g, weights[i % copies].desc, y, N, gemm_ws)
 
@@ -275,6 +283,7 @@ def main():
     t_quant = timed(quant_only, k_steps, min(warmup, k_steps)) / k_steps
     t_given = timed(step_given, k_steps, min(warmup, k_steps)) / k_steps
     t_gated = timed(step_gated, k_steps, min(warmup, k_steps)) / k_steps if gate_p is not None else None
+    t_bf16 = timed(step_bf16, k_steps, min(warmup, k_steps)) / k_steps
     t_rht = timed(step_rht, k_steps, min(warmup, k_steps)) / k_steps if rht_on else None
     t_qrht = timed(quant_rht_only, k_steps, min(warmup, k_steps)) / k_steps if rht_on else None
     t_bwd = timed(bwd[0], k_steps, min(warmup, k_steps)) / k_steps if bwd else None
@@ -381,6 +390,9 @@ def main():
                           np.float32(a_dw[2].item()) == g_dy)
         bwd_parity = {"transposed_codes_scales_bit_exact": t_codes_ok, "dX_within_1e-5": bool(dx_ok),
                       "dX_worst_ratio": dx_worst, "dW_within_1e-5": bool(dw_ok), "dW_worst_ratio": dw_worst}
+    # bf16 Y: the round-to-nearest-even of the FP32 Y of the same step (the gated FP32 Y for GDN)
+    y32 = yg if gate_p is not None else y
+    bf16_ok = bool(torch.equal(y_b, y32.to(torch.bfloat16)))
     xq1 = ref.quantize(wl.x[rows], g_mode="given", g=1.0)
     given_ok = bool(np.array_equal(codes1[torch.from_numpy(rows).to(dev)].cpu().numpy(), xq1.codes) and
                     np.array_equal(scales1[torch.from_numpy(rows).to(dev)].cpu().numpy(), xq1.scales))
@@ -412,6 +424,7 @@ def main():
                               "step with g given (no amax pass)": t_given * 1e6,
                               "tflops with g given": flops / t_given / 1e12,
                               "step with GDN gates fused": t_gated * 1e6 if t_gated else None,
+                              "step with bf16 Y" + (" and GDN gates" if gate_p is not None else ""): t_bf16 * 1e6,
                               "step with RHT (both operands transformed, g computed)":
                                   t_rht * 1e6 if t_rht else None,
                               "quantize with RHT alone (g computed)": t_qrht * 1e6 if t_qrht else None,
@@ -425,7 +438,7 @@ def main():
         "parity": {"codes_scales_bit_exact": codes_ok, "gemm_within_1e-5": bool(y_ok), "worst_ratio": worst,
                    "g_given_codes_scales_bit_exact": given_ok,
                    "gdn_gates_within_bound": gated_ok, "gdn_gates_worst_ratio": gated_worst,
-                   "backward": bwd_parity, "rht": rht_parity,
+                   "backward": bwd_parity, "rht": rht_parity, "bf16_y_is_rne_of_f32_y": bf16_ok,
                    "rows_checked": int(len(rows)), "cols_checked": int(len(cols))},
     }
     print(json.dumps(out), flush=True)

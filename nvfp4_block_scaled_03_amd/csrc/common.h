@@ -301,12 +301,9 @@ struct Epilogue {
     int32_t out_bf16 = 0;                             // Y as bf16 (round to nearest even) instead of FP32
 };
 
-// FP32 -> bf16 bits, round to nearest with ties to even (NaN stays a quiet NaN).
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float v) {
-    const uint32_t u = __float_as_uint(v);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
-    return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
-}
+// FP32 -> bf16 bits, round to nearest with ties to even: gfx950's conversion
+// instruction (v_cvt_pk_bf16_f32) under the default rounding mode, one operation.
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float v) { return __builtin_bit_cast(uint16_t, (__bf16)v); }
 
 // One output element: FP32, or bf16 when the epilogue asks for it (y then
 // points at bf16 storage and idx counts bf16 elements).

@@ -398,7 +398,7 @@ __device__ __forceinline__ void tile_product(float16v (&acc)[TM][TN], uint8_t* c
     wait_vmem<0>();   // the zero loads past the end, before the stages are reused
 }
 
-template <int TM, int TN, bool GATED, bool EPI>
+template <int TM, int TN, bool GATED, bool BF16>
 __device__ __forceinline__ void store_tile_cols(const float16v (&acc)[TM][TN], int tm, int tn, int64_t M, int64_t N,
                                                 const float* __restrict__ g_x, const float* __restrict__ colscale,
                                                 float* __restrict__ y, int64_t ld_y, const Epilogue& gp, int wm,
@@ -420,8 +420,8 @@ __device__ __forceinline__ void store_tile_cols(const float16v (&acc)[TM][TN], i
                 if (m < M) {
                     float v = acc[i][j][r] * cs;
                     if constexpr (GATED) v = gate(v, n, gp);
-                    if constexpr (EPI)
-                        store_y(y, m * ld_y + n, v, gp);
+                    if constexpr (BF16)
+                        reinterpret_cast<uint16_t*>(y)[m * ld_y + n] = f32_to_bf16_rne(v);
                     else
                         y[m * ld_y + n] = v;
                 }
@@ -430,24 +430,27 @@ __device__ __forceinline__ void store_tile_cols(const float16v (&acc)[TM][TN], i
     }
 }
 
-// Y = acc * g_x * colscale for one tile (rows >= M and columns >= N skipped);
-// EPI: through the general epilogue (gates where the tile holds gate columns,
-// FP32 or bf16 output), else plain FP32 stores.
-template <int TM, int TN, bool EPI>
+// Y = acc * g_x * colscale for one tile (rows >= M and columns >= N skipped).
+// EPI bit 0: gates, evaluated only in the tiles that hold gate columns;
+// EPI bit 1: bf16 output.  Each combination is its own kernel, so the store
+// loops stay straight-line code over the accumulator registers and the plain
+// kernel carries nothing of the others.
+constexpr int kEpiGates = 1, kEpiBf16 = 2;
+
+template <int TM, int TN, int EPI>
 __device__ __forceinline__ void store_tile(const float16v (&acc)[TM][TN], int tm, int tn, int64_t M, int64_t N,
                                            const float* __restrict__ g_x, const float* __restrict__ colscale,
                                            float* __restrict__ y, int64_t ld_y, const Epilogue& gp, int wm, int wn,
                                            int lane) {
     using G = TileGeom<TM, TN>;
-    if constexpr (EPI) {
-        // only the tiles that hold gate columns take the gated stores
-        if (gates_touch((int64_t)tn * G::BN, (int64_t)(tn + 1) * G::BN, gp))
-            store_tile_cols<TM, TN, true, true>(acc, tm, tn, M, N, g_x, colscale, y, ld_y, gp, wm, wn, lane);
-        else
-            store_tile_cols<TM, TN, false, true>(acc, tm, tn, M, N, g_x, colscale, y, ld_y, gp, wm, wn, lane);
-        return;
+    constexpr bool BF16 = (EPI & kEpiBf16) != 0;
+    if constexpr ((EPI & kEpiGates) != 0) {
+        if (gates_touch((int64_t)tn * G::BN, (int64_t)(tn + 1) * G::BN, gp)) {
+            store_tile_cols<TM, TN, true, BF16>(acc, tm, tn, M, N, g_x, colscale, y, ld_y, gp, wm, wn, lane);
+            return;
+        }
     }
-    store_tile_cols<TM, TN, false, false>(acc, tm, tn, M, N, g_x, colscale, y, ld_y, gp, wm, wn, lane);
+    store_tile_cols<TM, TN, false, BF16>(acc, tm, tn, M, N, g_x, colscale, y, ld_y, gp, wm, wn, lane);
 }
 
 #define NVFP4_TILE_KERNEL_ARGS                                                                                   \
@@ -457,7 +460,7 @@ __device__ __forceinline__ void store_tile(const float16v (&acc)[TM][TN], int tm
         int64_t ld_y
 
 // One whole tile per workgroup.
-template <int TM, int TN, bool EPI>
+template <int TM, int TN, int EPI>
 __global__ __launch_bounds__(256) void gemm_tile_kernel(NVFP4_TILE_KERNEL_ARGS, Epilogue gp, int tiles_m,
                                                         int tiles_n) {
     using G = TileGeom<TM, TN>;
@@ -507,8 +510,11 @@ static hipError_t launch_tiles(int64_t M, const uint8_t* a_codes, const uint8_t*
     const uint8_t* wsc = blob + d.scales_offset;
     const float* cs = reinterpret_cast<const float*>(blob + d.colscale_offset);
     const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)(d.n_padded / BN);
-    const bool epi = gp.n_a > 0 || gp.n_b > 0 || gp.out_bf16;
-    auto kern = epi ? gemm_tile_kernel<TM, TN, true> : gemm_tile_kernel<TM, TN, false>;
+    const int epi = (gp.n_a > 0 || gp.n_b > 0 ? kEpiGates : 0) | (gp.out_bf16 ? kEpiBf16 : 0);
+    auto kern = epi == 0 ? gemm_tile_kernel<TM, TN, 0>
+              : epi == kEpiGates ? gemm_tile_kernel<TM, TN, kEpiGates>
+              : epi == kEpiBf16 ? gemm_tile_kernel<TM, TN, kEpiBf16>
+                                : gemm_tile_kernel<TM, TN, kEpiGates | kEpiBf16>;
     hipLaunchKernelGGL(kern, dim3(tiles_m * tiles_n), dim3(256), 0, stream, M, a_codes,
                        a_scales, g_x, wc, wsc, cs, d.n, d.n_padded, d.k, y, ld_y, gp, tiles_m, tiles_n);
     return hipGetLastError();
