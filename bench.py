@@ -45,6 +45,8 @@ def parse():
     p.add_argument("--config", default="decode", choices=sorted(CONFIG_NAMES))
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
+    p.add_argument("--minimal", action="store_true",
+                   help="time only the step, the product and the quantizer (profiler runs: one shape per kernel)")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                    help="only run a plain device-to-device copy of MIB MiB 20 times (calibrates HBM byte counters)")
     return p.parse_args()
@@ -123,7 +125,8 @@ def main():
     weights = [packed] + [packed.clone() for _ in range(copies - 1)]
     # the standard transformer's NVFP4 recipe (randomized Hadamard transform before quantization, g computed),
     # which nGPT does without: both operands transformed with the same signs, weights packed once
-    rht_on = name in ("ngpt", "gdn")
+    extra = not args.minimal        # the variants below: g given, gates, bf16 Y, RHT, backward
+    rht_on = extra and name in ("ngpt", "gdn")
     if rht_on:
         signs = workloads.rht_signs()
         packed_rht = nv.PackedWeight([nv.quantize_rht(w, signs) for w in w_dev], K)
@@ -162,7 +165,7 @@ def main():
                         in_dtype=in_dtype, ld_y=N)
 
     # the GDN projection with its gate epilogue fused (decay and write-strength columns)
-    gate_p = workloads.gdn_gate_params() if name == "gdn" else None
+    gate_p = workloads.gdn_gate_params() if extra and name == "gdn" else None
     if gate_p is not None:
         gates = nv.GdnGates(gate_p.a_col, gate_p.n_a, gate_p.b_col, gate_p.n_b,
                             torch.from_numpy(gate_p.a_log).to(dev), torch.from_numpy(gate_p.dt_bias).to(dev))
@@ -177,7 +180,7 @@ def main():
     # every operand quantized along its contraction axis inside the step (dY along N for dX; W, dY and X
     # along their rows, i.e. transposed), the two transposed weights packed, then the two products
     bwd = None
-    if name == "ngpt":
+    if extra and name == "ngpt":
         dy_np = workloads.random_matrix(workloads.SEEDS["ngpt"] + 7, M, N, 1e-3, "bf16")
         dy = torch.from_numpy(dy_np).to(dev).to(torch.bfloat16)
         w_full = w_first
@@ -281,9 +284,9 @@ def main():
     k_steps = max(steps, rot)
     t_gemm = timed(gemm_only, k_steps, min(warmup, k_steps)) / k_steps
     t_quant = timed(quant_only, k_steps, min(warmup, k_steps)) / k_steps
-    t_given = timed(step_given, k_steps, min(warmup, k_steps)) / k_steps
+    t_given = timed(step_given, k_steps, min(warmup, k_steps)) / k_steps if extra else None
     t_gated = timed(step_gated, k_steps, min(warmup, k_steps)) / k_steps if gate_p is not None else None
-    t_bf16 = timed(step_bf16, k_steps, min(warmup, k_steps)) / k_steps
+    t_bf16 = timed(step_bf16, k_steps, min(warmup, k_steps)) / k_steps if extra else None
     t_rht = timed(step_rht, k_steps, min(warmup, k_steps)) / k_steps if rht_on else None
     t_qrht = timed(quant_rht_only, k_steps, min(warmup, k_steps)) / k_steps if rht_on else None
     t_bwd = timed(bwd[0], k_steps, min(warmup, k_steps)) / k_steps if bwd else None
@@ -391,11 +394,13 @@ def main():
         bwd_parity = {"transposed_codes_scales_bit_exact": t_codes_ok, "dX_within_1e-5": bool(dx_ok),
                       "dX_worst_ratio": dx_worst, "dW_within_1e-5": bool(dw_ok), "dW_worst_ratio": dw_worst}
     # bf16 Y: the round-to-nearest-even of the FP32 Y of the same step (the gated FP32 Y for GDN)
-    y32 = yg if gate_p is not None else y
-    bf16_ok = bool(torch.equal(y_b, y32.to(torch.bfloat16)))
-    xq1 = ref.quantize(wl.x[rows], g_mode="given", g=1.0)
-    given_ok = bool(np.array_equal(codes1[torch.from_numpy(rows).to(dev)].cpu().numpy(), xq1.codes) and
-                    np.array_equal(scales1[torch.from_numpy(rows).to(dev)].cpu().numpy(), xq1.scales))
+    bf16_ok, given_ok = None, None
+    if extra:
+        y32 = yg if gate_p is not None else y
+        bf16_ok = bool(torch.equal(y_b, y32.to(torch.bfloat16)))
+        xq1 = ref.quantize(wl.x[rows], g_mode="given", g=1.0)
+        given_ok = bool(np.array_equal(codes1[torch.from_numpy(rows).to(dev)].cpu().numpy(), xq1.codes) and
+                        np.array_equal(scales1[torch.from_numpy(rows).to(dev)].cpu().numpy(), xq1.scales))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -416,15 +421,16 @@ def main():
         "data": "synthetic (seeded; distributions of the pages' workloads)",
         "config": {"workload": CONFIG_NAMES[name], "M": M, "K": K, "N": N,
                    "modules": [int(w.shape[0]) for w in wl.w], "x_dtype": wl.x_dtype,
-                   "weight_copies": copies, "graph": not args.no_graph},
+                   "weight_copies": copies, "graph": not args.no_graph, "variants_timed": extra},
         "roofline": roof,
         "cpu_baseline": cpu,
         "step_breakdown_us": {"step (nvfp4_linear)": t_step * 1e6, "launches_per_step": 1 if skinny else 3,
                               "quantize alone": t_quant * 1e6, "gemm alone": t_gemm * 1e6,
-                              "step with g given (no amax pass)": t_given * 1e6,
-                              "tflops with g given": flops / t_given / 1e12,
+                              "step with g given (no amax pass)": t_given * 1e6 if t_given else None,
+                              "tflops with g given": flops / t_given / 1e12 if t_given else None,
                               "step with GDN gates fused": t_gated * 1e6 if t_gated else None,
-                              "step with bf16 Y" + (" and GDN gates" if gate_p is not None else ""): t_bf16 * 1e6,
+                              "step with bf16 Y" + (" and GDN gates" if gate_p is not None else ""):
+                                  t_bf16 * 1e6 if t_bf16 else None,
                               "step with RHT (both operands transformed, g computed)":
                                   t_rht * 1e6 if t_rht else None,
                               "quantize with RHT alone (g computed)": t_qrht * 1e6 if t_qrht else None,
