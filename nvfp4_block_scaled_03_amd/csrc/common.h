@@ -320,20 +320,39 @@ __device__ __forceinline__ bool gates_touch(int64_t n0, int64_t n1, const Epilog
            (gp.n_b > 0 && n0 < gp.b_col + gp.n_b && gp.b_col < n1);
 }
 
-// FP32, with softplus and the sigmoid in forms that cannot overflow.
-__device__ __forceinline__ float gate(float y, int64_t n, const Epilogue& gp) {
+// The gate of one output column: what it is and its per-head parameters, read
+// once per column (the store loops then run without loads): kind 1 = decay
+// with bias and c = exp(A), kind 2 = write strength, 0 = no gate.
+struct GateCol {
+    int kind;
+    float bias, c;
+};
+
+__device__ __forceinline__ GateCol gate_col(int64_t n, const Epilogue& gp) {
     const uint32_t ha = (uint32_t)((int32_t)n - gp.a_col), hb = (uint32_t)((int32_t)n - gp.b_col);
-    if (ha < (uint32_t)gp.n_a) {
-        const float z = y + gp.dt_bias[ha];
-        const float sp = z > 0.0f ? z + log1pf(expf(-z)) : log1pf(expf(z));
-        return expf(-(expf(gp.a_log[ha]) * sp));
+    if (ha < (uint32_t)gp.n_a) return GateCol{1, gp.dt_bias[ha], expf(gp.a_log[ha])};
+    if (hb < (uint32_t)gp.n_b) return GateCol{2, 0.0f, 0.0f};
+    return GateCol{0, 0.0f, 0.0f};
+}
+
+// FP32, with softplus and the sigmoid in forms that cannot overflow and without
+// divergent branches (a lane's rows mix signs, so branches would run both sides):
+// softplus(z) = max(z, 0) + log1p(exp(-|z|)) and sigmoid(y) = (y >= 0 ? 1 : e) / (1 + e)
+// with e = exp(-|y|), each the same operations as the two-sided forms.
+__device__ __forceinline__ float gate_apply(float y, const GateCol& g) {
+    if (g.kind == 1) {
+        const float z = y + g.bias;
+        const float sp = (z > 0.0f ? z : 0.0f) + log1pf(expf(-__builtin_fabsf(z)));
+        return expf(-(g.c * sp));
     }
-    if (hb < (uint32_t)gp.n_b) {
+    if (g.kind == 2) {
         const float e = expf(-__builtin_fabsf(y));
-        return y >= 0.0f ? 1.0f / (1.0f + e) : e / (1.0f + e);
+        return (y >= 0.0f ? 1.0f : e) / (1.0f + e);
     }
     return y;
 }
+
+__device__ __forceinline__ float gate(float y, int64_t n, const Epilogue& gp) { return gate_apply(y, gate_col(n, gp)); }
 
 size_t gemm_workspace_bytes(int64_t M, const nvfp4_weight_desc& d);
 hipError_t launch_gemm(int64_t M, const uint8_t* a_codes, const uint8_t* a_scales, const float* g_x,

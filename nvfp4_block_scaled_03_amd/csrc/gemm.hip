@@ -412,6 +412,8 @@ __device__ __forceinline__ void store_tile_cols(const float16v (&acc)[TM][TN], i
         const int64_t n = n0 + j * 32;
         if (n >= N) continue;
         const float cs = gx * colscale[n];
+        GateCol gc{0, 0.0f, 0.0f};
+        if constexpr (GATED) gc = gate_col(n, gp);
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -419,7 +421,7 @@ __device__ __forceinline__ void store_tile_cols(const float16v (&acc)[TM][TN], i
                 const int64_t m = (int64_t)tm * G::BM + wm * (TM * 32) + i * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
                 if (m < M) {
                     float v = acc[i][j][r] * cs;
-                    if constexpr (GATED) v = gate(v, n, gp);
+                    if constexpr (GATED) v = gate_apply(v, gc);
                     if constexpr (BF16)
                         reinterpret_cast<uint16_t*>(y)[m * ld_y + n] = f32_to_bf16_rne(v);
                     else
@@ -488,35 +490,64 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(NVFP4_TILE_KERNEL_ARGS, 
 // (measured on MI355X over K = 4096; the ratio barely moves with K).
 constexpr int kTileRoundsSmall = 53, kTileRoundsLarge = 100;
 
-static bool small_tiles(int64_t M, const nvfp4_weight_desc& d) {
-    if (M <= 128) return true;
-    const int64_t big = ((M + 255) / 256) * (d.n_padded / 256), small = ((M + 127) / 128) * (d.n_padded / 128);
-    const int64_t rounds_big = (big + kComputeUnits - 1) / kComputeUnits;
-    const int64_t rounds_small = (small + 2 * kComputeUnits - 1) / (2 * kComputeUnits);
-    return rounds_small * kTileRoundsSmall < rounds_big * kTileRoundsLarge;
+// Time of a launch in those units: whole rounds of 256x256 tiles (one per
+// compute unit) or of 128x128 tiles (two per compute unit).
+static int64_t cost_large(int64_t M, int64_t cols_pad) {
+    const int64_t tiles = ((M + 255) / 256) * (cols_pad / 256);
+    return (tiles + kComputeUnits - 1) / kComputeUnits * kTileRoundsLarge;
+}
+static int64_t cost_small(int64_t M, int64_t cols_pad) {
+    const int64_t tiles = ((M + 127) / 128) * (cols_pad / 128);
+    return (tiles + 2 * kComputeUnits - 1) / (2 * kComputeUnits) * kTileRoundsSmall;
+}
+
+// Columns [0, split) on 256x256 tiles and [split, n_padded) on 128x128 tiles:
+// split = n_padded (all large), 0 (all small), or the last multiple of 256 at
+// or below n when a ragged column edge (e.g. the 96 gate columns past 16384 of
+// a fused GDN projection) would otherwise cost a whole extra round of large
+// tiles.  Every output element is the same sum whichever tile computes it.
+static int64_t column_split(int64_t M, const nvfp4_weight_desc& d) {
+    if (M <= 128) return 0;
+    const int64_t all_large = cost_large(M, d.n_padded), all_small = cost_small(M, d.n_padded);
+    const int64_t edge = d.n / 256 * 256;
+    const int64_t mixed = (edge > 0 && edge < d.n_padded) ? cost_large(M, edge) + cost_small(M, d.n_padded - edge)
+                                                           : INT64_MAX;
+    if (mixed < all_large && mixed < all_small) return edge;
+    return all_small < all_large ? 0 : d.n_padded;
 }
 
 size_t gemm_workspace_bytes(int64_t M, const nvfp4_weight_desc& d) {
     return skinny_applies(M, d) ? skinny_workspace_bytes(d) : 0;
 }
 
+// One launch over the weight's columns [c0, c1) (multiples of the tile width;
+// c1 <= n_padded): operand, column-scale and output pointers move to column
+// c0, the gate columns shift with them.
 template <int TM, int TN>
 static hipError_t launch_tiles(int64_t M, const uint8_t* a_codes, const uint8_t* a_scales, const float* g_x,
-                               const nvfp4_weight_desc& d, float* y, int64_t ld_y, const Epilogue& gp,
-                               hipStream_t stream) {
+                               const nvfp4_weight_desc& d, int64_t c0, int64_t c1, float* y, int64_t ld_y,
+                               const Epilogue& gp_all, hipStream_t stream) {
     constexpr int BM = 64 * TM, BN = 64 * TN;
     const uint8_t* blob = static_cast<const uint8_t*>(d.blob);
-    const uint8_t* wc = blob + d.codes_offset;
-    const uint8_t* wsc = blob + d.scales_offset;
-    const float* cs = reinterpret_cast<const float*>(blob + d.colscale_offset);
-    const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)(d.n_padded / BN);
-    const int epi = (gp.n_a > 0 || gp.n_b > 0 ? kEpiGates : 0) | (gp.out_bf16 ? kEpiBf16 : 0);
+    const uint8_t* wc = blob + d.codes_offset + c0 * d.k / 2;
+    const uint8_t* wsc = blob + d.scales_offset + c0 * d.k / 16;
+    const float* cs = reinterpret_cast<const float*>(blob + d.colscale_offset) + c0;
+    float* yc = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(y) + c0 * (gp_all.out_bf16 ? 2 : 4));
+    const int64_t n = (d.n < c1 ? d.n : c1) - c0, n_pad = c1 - c0;
+    Epilogue gp = gp_all;
+    gp.a_col -= (int32_t)c0;
+    gp.b_col -= (int32_t)c0;
+    // gates only where a gate column falls inside this launch
+    const bool gated = (gp.n_a > 0 && 0 < gp.a_col + gp.n_a && gp.a_col < n) ||
+                       (gp.n_b > 0 && 0 < gp.b_col + gp.n_b && gp.b_col < n);
+    const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)(n_pad / BN);
+    const int epi = (gated ? kEpiGates : 0) | (gp.out_bf16 ? kEpiBf16 : 0);
     auto kern = epi == 0 ? gemm_tile_kernel<TM, TN, 0>
               : epi == kEpiGates ? gemm_tile_kernel<TM, TN, kEpiGates>
               : epi == kEpiBf16 ? gemm_tile_kernel<TM, TN, kEpiBf16>
                                 : gemm_tile_kernel<TM, TN, kEpiGates | kEpiBf16>;
     hipLaunchKernelGGL(kern, dim3(tiles_m * tiles_n), dim3(256), 0, stream, M, a_codes,
-                       a_scales, g_x, wc, wsc, cs, d.n, d.n_padded, d.k, y, ld_y, gp, tiles_m, tiles_n);
+                       a_scales, g_x, wc, wsc, cs, n, n_pad, d.k, yc, ld_y, gp, tiles_m, tiles_n);
     return hipGetLastError();
 }
 
@@ -528,8 +559,12 @@ hipError_t launch_gemm(int64_t M, const uint8_t* a_codes, const uint8_t* a_scale
                              const_cast<uint8_t*>(a_codes), const_cast<uint8_t*>(a_scales), false, d, y, ld_y, ws,
                              gp, stream);
     }
-    return small_tiles(M, d) ? launch_tiles<2, 2>(M, a_codes, a_scales, g_x, d, y, ld_y, gp, stream)
-                             : launch_tiles<4, 4>(M, a_codes, a_scales, g_x, d, y, ld_y, gp, stream);
+    const int64_t split = column_split(M, d);
+    if (split > 0) {
+        const hipError_t e = launch_tiles<4, 4>(M, a_codes, a_scales, g_x, d, 0, split, y, ld_y, gp, stream);
+        if (e != hipSuccess || split == d.n_padded) return e;
+    }
+    return launch_tiles<2, 2>(M, a_codes, a_scales, g_x, d, split, d.n_padded, y, ld_y, gp, stream);
 }
 
 }  // namespace nvfp4

@@ -183,6 +183,21 @@ def test_tile_shape_does_not_change_results():
     assert torch.equal(y_all[:256], y_top)
 
 
+def test_mixed_tile_split():
+    """A ragged column edge (16384 + 96 columns, as the fused GDN projection's gate modules leave) at 1024
+    tokens runs its first 16384 columns on 256 x 256 tiles and the last 96 on 128 x 128 tiles in a second
+    launch: every output within the oracle's bound, and bit for bit what 128 x 128 tiles alone give."""
+    x = workloads.random_matrix(1301, 1024, 512, dtype="bf16")
+    ws = [workloads.random_matrix(1302, 16384, 512, 0.05, dtype="bf16"),
+          workloads.random_matrix(1303, 96, 512, 2.0, dtype="bf16")]
+    y = check_dense(x, "bf16", ws, "bf16", "mixed tiles")
+    xc, xs, gx = nv.quantize(to_dev(x, "bf16"))
+    pw = nv.PackedWeight([nv.quantize(to_dev(w, "bf16")) for w in ws], 512)
+    y_top = nv.gemm(xc[:128].contiguous(), xs[:128].contiguous(), gx, pw)     # 128 rows: small tiles only
+    torch.cuda.synchronize()
+    assert torch.equal(y[:128], y_top)
+
+
 def test_shared_scale_pitfall_is_detected():
     """Negative control: packing module a's codes with module q's global scale (one scale for a
     fused kernel) corrupts exactly the a columns, and the parity check catches it."""
