@@ -229,6 +229,25 @@ def main():
         nv.nvfp4_linear(x, codes_b, scales_b, g_b, weights[i % copies].desc, y_b, lin_ws, M=M, ld_x=K,
                         in_dtype=in_dtype, ld_y=N, gates=gates if gate_p is not None else None)
 
+    # the FP8 KV-cache quantizer (the page's calibrated FP8 scales), on a K-cache-shaped tensor of the GDN model
+    kv = None
+    if extra and name == "gdn":
+        kv_np = workloads.kv_cache()
+        kv_x = torch.from_numpy(kv_np).to(dev).to(torch.bfloat16)
+        kv_codes = torch.empty(kv_np.shape, dtype=torch.uint8, device=dev)
+        kv_s = torch.empty((1,), dtype=torch.float32, device=dev)
+        kv_ws = torch.empty((max(nv.nvfp4_quantize_workspace_bytes(*kv_np.shape), 256),), dtype=torch.uint8,
+                            device=dev)
+        kv_codes_g = torch.empty_like(kv_codes)
+        kv_sg = torch.full((1,), 0.05, dtype=torch.float32, device=dev)
+
+        def kv_calibrated(i):
+            nv.nvfp4_kv_quantize_fp8(kv_x, kv_codes, kv_s, nv.NVFP4_G_COMPUTE, kv_ws)
+
+        def kv_given(i):
+            nv.nvfp4_kv_quantize_fp8(kv_x, kv_codes_g, kv_sg, nv.NVFP4_G_GIVEN, None)
+        kv = (kv_calibrated, kv_given)
+
     def gemm_only(i):
         nv.nvfp4_gemm(M, codes, scales, g, weights[i % copies].desc, y, N, gemm_ws)
 
@@ -289,6 +308,8 @@ def main():
     t_bf16 = timed(step_bf16, k_steps, min(warmup, k_steps)) / k_steps if extra else None
     t_rht = timed(step_rht, k_steps, min(warmup, k_steps)) / k_steps if rht_on else None
     t_qrht = timed(quant_rht_only, k_steps, min(warmup, k_steps)) / k_steps if rht_on else None
+    t_kv = timed(kv[0], k_steps, min(warmup, k_steps)) / k_steps if kv else None
+    t_kvg = timed(kv[1], k_steps, min(warmup, k_steps)) / k_steps if kv else None
     t_bwd = timed(bwd[0], k_steps, min(warmup, k_steps)) / k_steps if bwd else None
     t_qt = timed(bwd[1], k_steps, min(warmup, k_steps)) / k_steps if bwd else None
 
@@ -369,6 +390,14 @@ def main():
         yr = y_r[rsel][:, torch.from_numpy(cols).to(dev)].cpu().numpy()
         r_ok, r_worst = ref.gemm_within_tolerance(yr, yr_ref, ar_ref)
         rht_parity = {"codes_scales_bit_exact": r_codes_ok, "gemm_within_1e-5": bool(r_ok), "worst_ratio": r_worst}
+    kv_parity = None
+    if kv:   # every byte and the calibrated scale against the oracle
+        from oracle import fp8_kv
+        oc, os_ = fp8_kv.quantize_kv(kv_np)
+        ocg, _ = fp8_kv.quantize_kv(kv_np, "given", 0.05)
+        kv_parity = {"bytes_and_scale_bit_exact": bool(np.array_equal(kv_codes.cpu().numpy(), oc) and
+                                                       np.float32(kv_s.item()) == os_),
+                     "given_scale_bytes_bit_exact": bool(np.array_equal(kv_codes_g.cpu().numpy(), ocg))}
     bwd_parity = None
     if bwd:   # sampled entries of dX and dW, and sampled rows of the transposed encodings, against the oracle
         rsel = torch.from_numpy(rows).to(dev)
@@ -434,6 +463,10 @@ def main():
                               "step with RHT (both operands transformed, g computed)":
                                   t_rht * 1e6 if t_rht else None,
                               "quantize with RHT alone (g computed)": t_qrht * 1e6 if t_qrht else None,
+                              "kv fp8 quantize 4096x1024 bf16 (scale calibrated)": t_kv * 1e6 if t_kv else None,
+                              "kv fp8 quantize (scale given)": t_kvg * 1e6 if t_kvg else None,
+                              "kv fp8 GB/s (scale given; read x, write bytes)":
+                                  4096 * 1024 * 3 / t_kvg / 1e9 if t_kvg else None,
                               "backward step (dX and dW, operands quantized and packed in the step)":
                                   t_bwd * 1e6 if t_bwd else None,
                               "backward tflops": 2.0 * flops / t_bwd / 1e12 if t_bwd else None,
@@ -444,7 +477,7 @@ def main():
         "parity": {"codes_scales_bit_exact": codes_ok, "gemm_within_1e-5": bool(y_ok), "worst_ratio": worst,
                    "g_given_codes_scales_bit_exact": given_ok,
                    "gdn_gates_within_bound": gated_ok, "gdn_gates_worst_ratio": gated_worst,
-                   "backward": bwd_parity, "rht": rht_parity, "bf16_y_is_rne_of_f32_y": bf16_ok,
+                   "backward": bwd_parity, "rht": rht_parity, "kv_fp8": kv_parity, "bf16_y_is_rne_of_f32_y": bf16_ok,
                    "rows_checked": int(len(rows)), "cols_checked": int(len(cols))},
     }
     print(json.dumps(out), flush=True)

@@ -185,6 +185,32 @@ nvfp4_status nvfp4_quantize_t_rht(const void* x, int in_dtype, int64_t rows, int
                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * FP8 KV cache: E4M3 bytes with one calibrated FP32 scale per tensor.
+ *
+ * The Gated DeltaNet page's summary credits calibrated FP8 scales on the KV
+ * cache with recovering most of the long-context loss.  Per tensor (a layer's
+ * K or V cache, [rows][cols] = [tokens][heads * head_dim]): s given (a
+ * calibrated value, s_mode NVFP4_G_GIVEN) or calibrated on the tensor itself
+ * (NVFP4_G_COMPUTE: s = fl32(amax / 448), 1 for an all-zero tensor, floored at
+ * 2^-100, written to *scale).  Per element: q = fl32(x * fl32(1/s)), byte =
+ * sign of q (bit 7) | E4M3 "FN" magnitude nearest to |q| (bias 7, ties to the
+ * even byte, saturating at 448; the sign is kept when the magnitude is 0);
+ * a NaN gives 0x7F with its sign.  The dequantized value is e4m3(byte) * s.
+ *
+ * x        : device, rows x cols elements of in_dtype, row r at x + r*ld_x,
+ *            aligned to the element size
+ * rows,cols: >= 0 (either 0: empty; s = 1 in COMPUTE mode)
+ * codes    : device, rows * cols bytes, written dense ([rows][cols])
+ * scale    : device, one float; written in COMPUTE mode, read in GIVEN mode
+ *            (finite and positive)
+ * workspace: COMPUTE mode only, >= nvfp4_quantize_workspace_bytes(rows, cols)
+ * Errors as for nvfp4_quantize; nothing is launched on an error.
+ * ------------------------------------------------------------------------- */
+nvfp4_status nvfp4_kv_quantize_fp8(const void* x, int in_dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                                   uint8_t* codes, float* scale, int s_mode, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Packed weights.
  *
  * A projection is a stack of n_modules sub-modules (e.g. q,k,v,z,a,b of a

@@ -121,6 +121,7 @@ def _load():
         "nvfp4_quantize_workspace_bytes": (c_sz, [c_i64, c_i64]),
         "nvfp4_quantize": (c_int, [c_vp, c_int, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_int, c_vp, c_sz, c_vp]),
         "nvfp4_quantize_t": (c_int, [c_vp, c_int, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_int, c_vp, c_sz, c_vp]),
+        "nvfp4_kv_quantize_fp8": (c_int, [c_vp, c_int, c_i64, c_i64, c_i64, c_vp, c_vp, c_int, c_vp, c_sz, c_vp]),
         "nvfp4_quantize_rht": (c_int, [c_vp, c_int, c_i64, c_i64, c_i64, ctypes.c_uint32, c_vp, c_vp, c_vp, c_int,
                                        c_vp, c_sz, c_vp]),
         "nvfp4_quantize_t_rht": (c_int, [c_vp, c_int, c_i64, c_i64, c_i64, ctypes.c_uint32, c_vp, c_vp, c_vp, c_int,
@@ -250,6 +251,14 @@ def nvfp4_quantize_t_rht(x, signs: int, codes, scales, g, g_mode=NVFP4_G_COMPUTE
     ws_bytes = workspace.numel() * workspace.element_size() if isinstance(workspace, torch.Tensor) else 0
     _check(_lib.nvfp4_quantize_t_rht(_ptr(x), in_dtype, rows, cols, ld_x, int(signs), _ptr(codes), _ptr(scales),
                                      _ptr(g), g_mode, _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def nvfp4_kv_quantize_fp8(x, codes, scale, s_mode=NVFP4_G_COMPUTE, workspace=None, stream=None):
+    """FP8 (E4M3) bytes of x [rows, cols] with one per-tensor scale (calibrated here, or given in scale)."""
+    rows, cols, ld_x, in_dtype = _layout(x, "x must have unit stride along its columns")
+    ws_bytes = workspace.numel() * workspace.element_size() if isinstance(workspace, torch.Tensor) else 0
+    _check(_lib.nvfp4_kv_quantize_fp8(_ptr(x), in_dtype, rows, cols, ld_x, _ptr(codes), _ptr(scale), s_mode,
+                                      _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def nvfp4_packed_weight_bytes(module_rows: Sequence[int], K: int) -> int:
@@ -395,6 +404,23 @@ def quantize_rht(x: torch.Tensor, signs: int, g=None, stream=None):
 def quantize_t_rht(x: torch.Tensor, signs: int, g=None, stream=None):
     """The same for x^T: codes [cols, rows/2], scales [cols, rows/16]."""
     return _quantize_with(nvfp4_quantize_t_rht, x, signs, x.shape[1], x.shape[0], g, stream)
+
+
+def kv_quantize_fp8(x: torch.Tensor, scale=None, stream=None):
+    """(codes uint8 [rows, cols], scale [1]) of x in FP8 E4M3; scale=None calibrates on x."""
+    rows, cols = x.shape
+    codes = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    st = torch.empty((1,), dtype=torch.float32, device=x.device)
+    if scale is None:
+        ws = torch.empty((max(nvfp4_quantize_workspace_bytes(rows, cols), 1),), dtype=torch.uint8, device=x.device)
+        nvfp4_kv_quantize_fp8(x, codes, st, NVFP4_G_COMPUTE, ws, stream)
+    else:
+        if isinstance(scale, torch.Tensor):
+            st.copy_(scale.reshape(1))
+        else:
+            st.fill_(float(scale))
+        nvfp4_kv_quantize_fp8(x, codes, st, NVFP4_G_GIVEN, None, stream)
+    return codes, st
 
 
 class PackedWeight:

@@ -131,6 +131,68 @@ __global__ __launch_bounds__(kQThreads) void encode_kernel(const T* __restrict__
 __global__ void write_unit_g_kernel(float* g) { g[0] = 1.0f; }
 
 // ---------------------------------------------------------------------------
+// FP8 (E4M3) KV-cache quantizer with one FP32 scale s per tensor (calibrated
+// and given, or calibrated on the tensor: s = fl32(amax / 448), 1 for an
+// all-zero tensor, floored at 2^-100).  Per element, like the NVFP4 element
+// step: q = fl32(x * fl32(1/s)), byte = sign of q | nearest E4M3 magnitude
+// (ties to even, saturating at 448); NaN gives 0x7F with its sign.  Each
+// thread converts runs of 8 elements of a row (one 16-byte or two 16-byte
+// loads, one 8-byte store); ragged or unaligned runs go element by element.
+// ---------------------------------------------------------------------------
+constexpr float kKvRange = 448.0f;
+
+__device__ __forceinline__ uint32_t kv_byte(float v, float r) {
+    const float q = v * r;
+    const float a = __builtin_fabsf(q);
+    const uint32_t mag = a != a ? 0x7Fu : e4m3_rne_sat(a);
+    return ((__float_as_uint(q) >> 24) & 0x80u) | mag;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kQThreads) void kv_fp8_kernel(const T* __restrict__ x, int64_t rows, int64_t cols,
+                                                           int64_t ld, uint8_t* __restrict__ codes,
+                                                           float* __restrict__ s_io, int s_given,
+                                                           const float* __restrict__ partials, int n_partials,
+                                                           int vec) {
+    __shared__ float s_r;
+    if (s_given) {
+        if (threadIdx.x == 0) s_r = 1.0f / s_io[0];
+    } else {
+        float m = 0.0f;
+        for (int i = threadIdx.x; i < n_partials; i += kQThreads) m = fmaxf(m, partials[i]);
+        m = block_max<kQThreads>(m);
+        if (threadIdx.x == 0) {
+            float sc = m / kKvRange;
+            sc = m == 0.0f ? 1.0f : (sc < kGFloor ? kGFloor : sc);
+            s_r = 1.0f / sc;
+            if (blockIdx.x == 0) s_io[0] = sc;
+        }
+    }
+    __syncthreads();
+    const float r = s_r;
+    const int64_t runs_per_row = (cols + 7) / 8, nruns = rows * runs_per_row;
+    for (int64_t u = (int64_t)blockIdx.x * kQThreads + threadIdx.x; u < nruns; u += (int64_t)gridDim.x * kQThreads) {
+        const int64_t row = u / runs_per_row, col = (u - row * runs_per_row) * 8;
+        const T* src = x + row * ld + col;
+        uint8_t* dst = codes + row * cols + col;
+        if (vec && col + 8 <= cols) {
+            float v[8];
+            load8(src, v);
+            uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                w0 |= kv_byte(v[i], r) << (8 * i);
+                w1 |= kv_byte(v[4 + i], r) << (8 * i);
+            }
+            *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
+        } else {
+            const int64_t e = col + 8 <= cols ? 8 : cols - col;
+            for (int64_t i = 0; i < e; ++i) dst[i] = (uint8_t)kv_byte(elem_f32(src[i]), r);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // The encoding of x^T (blocks of 16 consecutive rows of x, one output row per
 // column of x): the other operand orientation of the training GEMMs
 // (dX = dY.W needs W quantized along its rows, dW = dY^T.X needs dY and X
@@ -397,6 +459,40 @@ static void launch_rows(const T* xp, int64_t rows, int64_t K, int64_t ld_x, uint
     else
         hipLaunchKernelGGL((encode_kernel<T, false>), dim3(grid), dim3(kQThreads), 0, stream, xp, rows, K, ld_x,
                            codes, scales, g, given, partials, n_partials, 0u);
+}
+
+hipError_t launch_kv_fp8(const void* x, int in_dtype, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* codes,
+                         float* scale, int s_mode, float* partials, int n_partials, hipStream_t stream) {
+    const int given = (s_mode == NVFP4_G_GIVEN);
+    if (rows == 0 || cols == 0) {
+        if (!given) hipLaunchKernelGGL(write_unit_g_kernel, dim3(1), dim3(1), 0, stream, scale);
+        return hipGetLastError();
+    }
+    const int esize = in_dtype == NVFP4_IN_BF16 ? 2 : 4;
+    const bool x16 = reinterpret_cast<uintptr_t>(x) % 16 == 0;
+    // vector runs: 16-byte aligned input rows (or a dense tensor) and 8-byte aligned output runs
+    const int vec_in = x16 && (ld_x == cols || (ld_x * esize) % 16 == 0);
+    const int vec = vec_in && (reinterpret_cast<uintptr_t>(codes) % 8 == 0) && cols % 8 == 0 &&
+                    (ld_x * esize) % 16 == 0;
+    const int64_t runs = rows * ((cols + 7) / 8);
+    int64_t wg = (runs + kQThreads - 1) / kQThreads;
+    if (wg > 256 * 16) wg = 256 * 16;
+    if (in_dtype == NVFP4_IN_BF16) {
+        const uint16_t* xp = static_cast<const uint16_t*>(x);
+        if (!given)
+            hipLaunchKernelGGL(amax_partials_kernel<uint16_t>, dim3(n_partials), dim3(kQThreads), 0, stream, xp,
+                               rows, cols, ld_x, partials, vec_in);
+        hipLaunchKernelGGL(kv_fp8_kernel<uint16_t>, dim3((int)wg), dim3(kQThreads), 0, stream, xp, rows, cols, ld_x,
+                           codes, scale, given, partials, n_partials, vec);
+    } else {
+        const float* xp = static_cast<const float*>(x);
+        if (!given)
+            hipLaunchKernelGGL(amax_partials_kernel<float>, dim3(n_partials), dim3(kQThreads), 0, stream, xp, rows,
+                               cols, ld_x, partials, vec_in);
+        hipLaunchKernelGGL(kv_fp8_kernel<float>, dim3((int)wg), dim3(kQThreads), 0, stream, xp, rows, cols, ld_x,
+                           codes, scale, given, partials, n_partials, vec);
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_quantize(const void* x, int in_dtype, int64_t rows, int64_t K, int64_t ld_x,

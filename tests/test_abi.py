@@ -40,7 +40,7 @@ def test_header_declares_the_boundary():
     for required in ["nvfp4_quantize", "nvfp4_pack_weights", "nvfp4_gemm", "nvfp4_last_error",
                      "nvfp4_quantize_workspace_bytes", "nvfp4_packed_weight_bytes", "nvfp4_unpack_weights",
                      "nvfp4_gemm_workspace_bytes", "nvfp4_abi_version", "nvfp4_device_check", "nvfp4_quantize_t", "nvfp4_quantize_rht", "nvfp4_quantize_t_rht",
-                     "nvfp4_gemm_ex", "nvfp4_linear_ex"]:
+                     "nvfp4_gemm_ex", "nvfp4_linear_ex", "nvfp4_kv_quantize_fp8"]:
         assert required in names
 
 
@@ -341,3 +341,24 @@ def test_epilogue_validation():
         assert ge(gates=g) == nv.NVFP4_ERR_NO_DEVICE
         assert nv.lib.nvfp4_linear_ex(FAKE, nv.NVFP4_IN_BF16, 16, d.k, FAKE, FAKE, FAKE, 0, ctypes.byref(d),
                                       ctypes.byref(e), FAKE + 2, d.n, FAKE, 1 << 30, None) == nv.NVFP4_ERR_NO_DEVICE
+
+
+def test_kv_fp8_validation():
+    def kv(**kw):
+        a = dict(x=FAKE, in_dtype=nv.NVFP4_IN_BF16, rows=16, cols=40, ld_x=40, codes=FAKE, scale=FAKE,
+                 s_mode=nv.NVFP4_G_COMPUTE, ws=FAKE, ws_bytes=1 << 16)
+        a.update(kw)
+        return nv.lib.nvfp4_kv_quantize_fp8(a["x"], a["in_dtype"], a["rows"], a["cols"], a["ld_x"], a["codes"],
+                                            a["scale"], a["s_mode"], a["ws"], a["ws_bytes"], None)
+    assert kv(in_dtype=9) == nv.NVFP4_ERR_INVALID_ARG
+    assert kv(s_mode=5) == nv.NVFP4_ERR_INVALID_ARG
+    assert kv(scale=None) == nv.NVFP4_ERR_INVALID_ARG
+    assert kv(codes=None) == nv.NVFP4_ERR_INVALID_ARG
+    assert kv(rows=-1) == nv.NVFP4_ERR_SHAPE
+    assert kv(ld_x=39) == nv.NVFP4_ERR_SHAPE
+    assert kv(x=FAKE + 1) == nv.NVFP4_ERR_UNSUPPORTED
+    assert kv(ws=None) == nv.NVFP4_ERR_WORKSPACE
+    if _no_gpu():
+        assert kv() == nv.NVFP4_ERR_NO_DEVICE
+        assert kv(ws=None, ws_bytes=0, s_mode=nv.NVFP4_G_GIVEN, cols=7, ld_x=9, x=FAKE + 2) == nv.NVFP4_ERR_NO_DEVICE
+        assert kv(rows=0, x=None, codes=None) == nv.NVFP4_ERR_NO_DEVICE

@@ -192,6 +192,17 @@ def make(name: str, **kw) -> Workload:
     return MAKERS[name](**kw)
 
 
+def kv_cache(seed: int = 707, tokens: int = 4096, width: int = 1024) -> np.ndarray:
+    """A K-cache-shaped bf16 tensor [tokens x heads*head_dim]: N(0,1) per channel times a per-channel
+    scale exp(U(-1, 1)), with 1% of the channels x20 (the outlier channels of keys)."""
+    c = np.random.SeedSequence(seed).spawn(3)
+    x = _rng(c[0]).standard_normal((tokens, width), dtype=np.float32)
+    scale = np.exp(_rng(c[1]).uniform(-1.0, 1.0, width)).astype(np.float32)
+    out = _rng(c[2]).choice(width, size=max(1, width // 100), replace=False)
+    scale[out] *= np.float32(20.0)
+    return to_bf16_values(x * scale)
+
+
 def rht_signs(seed: int = 606) -> int:
     """A seeded random 16-bit sign mask for the randomized Hadamard transform (the method's random draw,
     passed to both sides as an input)."""
