@@ -196,15 +196,14 @@ def main():
         dw = torch.empty((N, K), dtype=torch.float32, device=dev)
 
         def step_backward(i):
-            nv.nvfp4_quantize(dy, *a_dx[:3], nv.NVFP4_G_COMPUTE, a_dx[3], rows=M, K=N, ld_x=N,
-                              in_dtype=nv.NVFP4_IN_BF16)
+            # dY in both orientations from one read (one g), W and X transposed
+            nv.nvfp4_quantize_both(dy, a_dx[0], a_dx[1], a_dw[0], a_dw[1], a_dx[2], nv.NVFP4_G_COMPUTE, a_dx[3])
             nv.nvfp4_quantize_t(w_full, *wt[:3], nv.NVFP4_G_COMPUTE, wt[3])
             d_wt = nv.nvfp4_pack_weights([wt[:3]], N, blob_wt)
             nv.nvfp4_gemm(M, a_dx[0], a_dx[1], a_dx[2], d_wt, dx, K, None)
-            nv.nvfp4_quantize_t(dy, *a_dw[:3], nv.NVFP4_G_COMPUTE, a_dw[3])
             nv.nvfp4_quantize_t(x, *xt[:3], nv.NVFP4_G_COMPUTE, xt[3])
             d_xt = nv.nvfp4_pack_weights([xt[:3]], M, blob_xt)
-            nv.nvfp4_gemm(N, a_dw[0], a_dw[1], a_dw[2], d_xt, dw, K, None)
+            nv.nvfp4_gemm(N, a_dw[0], a_dw[1], a_dx[2], d_xt, dw, K, None)
 
         def quant_t_only(i):
             nv.nvfp4_quantize_t(x, *xt[:3], nv.NVFP4_G_COMPUTE, xt[3])
@@ -419,7 +418,7 @@ def main():
         nsel_t = torch.from_numpy(nsel).to(dev)
         t_codes_ok = bool(np.array_equal(a_dw[0][nsel_t].cpu().numpy(), dytq.codes) and
                           np.array_equal(a_dw[1][nsel_t].cpu().numpy(), dytq.scales) and
-                          np.float32(a_dw[2].item()) == g_dy)
+                          np.float32(a_dx[2].item()) == g_dy)
         bwd_parity = {"transposed_codes_scales_bit_exact": t_codes_ok, "dX_within_1e-5": bool(dx_ok),
                       "dX_worst_ratio": dx_worst, "dW_within_1e-5": bool(dw_ok), "dW_worst_ratio": dw_worst}
     # bf16 Y: the round-to-nearest-even of the FP32 Y of the same step (the gated FP32 Y for GDN)
@@ -467,7 +466,7 @@ def main():
                               "kv fp8 quantize (scale given)": t_kvg * 1e6 if t_kvg else None,
                               "kv fp8 GB/s (scale given; read x, write bytes)":
                                   4096 * 1024 * 3 / t_kvg / 1e9 if t_kvg else None,
-                              "backward step (dX and dW, operands quantized and packed in the step)":
+                              "backward step (dX and dW; dY both ways in one pass, W and X transposed, packed)":
                                   t_bwd * 1e6 if t_bwd else None,
                               "backward tflops": 2.0 * flops / t_bwd / 1e12 if t_bwd else None,
                               "quantize_t alone (X^T, g computed)": t_qt * 1e6 if t_qt else None,

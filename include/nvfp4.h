@@ -158,6 +158,23 @@ nvfp4_status nvfp4_quantize_t(const void* x, int in_dtype, int64_t rows, int64_t
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Both orientations from one read: nvfp4_quantize of x and nvfp4_quantize_t
+ * of x with one g, bit for bit, reading x once (a training step needs dY
+ * along N for dX = dY . W and along the tokens for dW = dY^T . X; the
+ * "Normalized Architectures are Natively 4-Bit" page trains end to end in
+ * NVFP4, abstract and section "Approach").
+ *
+ * x        : as for nvfp4_quantize_t (aligned to the element size)
+ * rows,cols: >= 0, both multiples of 16
+ * codes    : [rows][cols/2], 4-byte aligned; scales [rows][cols/16]
+ * codes_t  : [cols][rows/2], 8-byte aligned; scales_t [cols][rows/16]
+ * g, g_mode, workspace: as for nvfp4_quantize (nvfp4_quantize_workspace_bytes(rows, cols))
+ * ------------------------------------------------------------------------- */
+nvfp4_status nvfp4_quantize_both(const void* x, int in_dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                                 uint8_t* codes, uint8_t* scales, uint8_t* codes_t, uint8_t* scales_t,
+                                 float* g, int g_mode, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Quantize behind a randomized Hadamard transform (RHT).
  *
  * Standard transformers trained in NVFP4 apply random Hadamard transforms

@@ -121,6 +121,8 @@ def _load():
         "nvfp4_quantize_workspace_bytes": (c_sz, [c_i64, c_i64]),
         "nvfp4_quantize": (c_int, [c_vp, c_int, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_int, c_vp, c_sz, c_vp]),
         "nvfp4_quantize_t": (c_int, [c_vp, c_int, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_int, c_vp, c_sz, c_vp]),
+        "nvfp4_quantize_both": (c_int, [c_vp, c_int, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_vp,
+                                        c_sz, c_vp]),
         "nvfp4_kv_quantize_fp8": (c_int, [c_vp, c_int, c_i64, c_i64, c_i64, c_vp, c_vp, c_int, c_vp, c_sz, c_vp]),
         "nvfp4_quantize_rht": (c_int, [c_vp, c_int, c_i64, c_i64, c_i64, ctypes.c_uint32, c_vp, c_vp, c_vp, c_int,
                                        c_vp, c_sz, c_vp]),
@@ -251,6 +253,15 @@ def nvfp4_quantize_t_rht(x, signs: int, codes, scales, g, g_mode=NVFP4_G_COMPUTE
     ws_bytes = workspace.numel() * workspace.element_size() if isinstance(workspace, torch.Tensor) else 0
     _check(_lib.nvfp4_quantize_t_rht(_ptr(x), in_dtype, rows, cols, ld_x, int(signs), _ptr(codes), _ptr(scales),
                                      _ptr(g), g_mode, _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def nvfp4_quantize_both(x, codes, scales, codes_t, scales_t, g, g_mode=NVFP4_G_COMPUTE, workspace=None,
+                        stream=None):
+    """Row and column encodings of x [rows, cols] (both multiples of 16) from one read, one g."""
+    rows, cols, ld_x, in_dtype = _layout(x, "x must have unit stride along its columns")
+    ws_bytes = workspace.numel() * workspace.element_size() if isinstance(workspace, torch.Tensor) else 0
+    _check(_lib.nvfp4_quantize_both(_ptr(x), in_dtype, rows, cols, ld_x, _ptr(codes), _ptr(scales), _ptr(codes_t),
+                                    _ptr(scales_t), _ptr(g), g_mode, _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def nvfp4_kv_quantize_fp8(x, codes, scale, s_mode=NVFP4_G_COMPUTE, workspace=None, stream=None):
@@ -404,6 +415,24 @@ def quantize_rht(x: torch.Tensor, signs: int, g=None, stream=None):
 def quantize_t_rht(x: torch.Tensor, signs: int, g=None, stream=None):
     """The same for x^T: codes [cols, rows/2], scales [cols, rows/16]."""
     return _quantize_with(nvfp4_quantize_t_rht, x, signs, x.shape[1], x.shape[0], g, stream)
+
+
+def quantize_both(x: torch.Tensor, g=None, stream=None):
+    """((codes, scales, g), (codes_t, scales_t, g)) of x [rows, cols]: the encodings of x and of x^T, sharing
+    one g tensor."""
+    rows, cols = x.shape
+    codes, scales, gt = empty_quantized(rows, cols, x.device)
+    codes_t, scales_t, _ = empty_quantized(cols, rows, x.device)
+    if g is None:
+        ws = torch.empty((max(nvfp4_quantize_workspace_bytes(rows, cols), 1),), dtype=torch.uint8, device=x.device)
+        nvfp4_quantize_both(x, codes, scales, codes_t, scales_t, gt, NVFP4_G_COMPUTE, ws, stream)
+    else:
+        if isinstance(g, torch.Tensor):
+            gt.copy_(g.reshape(1))
+        else:
+            gt.fill_(float(g))
+        nvfp4_quantize_both(x, codes, scales, codes_t, scales_t, gt, NVFP4_G_GIVEN, None, stream)
+    return (codes, scales, gt), (codes_t, scales_t, gt)
 
 
 def kv_quantize_fp8(x: torch.Tensor, scale=None, stream=None):

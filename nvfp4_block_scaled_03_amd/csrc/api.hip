@@ -225,6 +225,41 @@ nvfp4_status nvfp4_quantize_t_rht(const void* x, int in_dtype, int64_t rows, int
                            stream, 1, signs);
 }
 
+nvfp4_status nvfp4_quantize_both(const void* x, int in_dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                                 uint8_t* codes, uint8_t* scales, uint8_t* codes_t, uint8_t* scales_t, float* g,
+                                 int g_mode, void* workspace, size_t workspace_bytes, void* stream) {
+    if (in_dtype != NVFP4_IN_F32 && in_dtype != NVFP4_IN_BF16)
+        return fail(NVFP4_ERR_INVALID_ARG, "unknown input dtype %d", in_dtype);
+    if (g_mode != NVFP4_G_COMPUTE && g_mode != NVFP4_G_GIVEN)
+        return fail(NVFP4_ERR_INVALID_ARG, "unknown g mode %d", g_mode);
+    if (g == nullptr) return fail(NVFP4_ERR_INVALID_ARG, "g is NULL");
+    if (rows < 0 || cols < 0 || rows % 16 != 0 || cols % 16 != 0)
+        return fail(NVFP4_ERR_SHAPE, "need rows and cols >= 0, multiples of 16 (rows=%lld cols=%lld)",
+                    (long long)rows, (long long)cols);
+    if (ld_x < cols) return fail(NVFP4_ERR_SHAPE, "ld_x (%lld) < cols (%lld)", (long long)ld_x, (long long)cols);
+    if (rows > 0 && ld_x > INT64_MAX / rows) return fail(NVFP4_ERR_SHAPE, "tensor too large");
+    const int esize = in_dtype == NVFP4_IN_BF16 ? 2 : 4;
+    if (rows > 0 && cols > 0) {
+        if (x == nullptr || codes == nullptr || scales == nullptr || codes_t == nullptr || scales_t == nullptr)
+            return fail(NVFP4_ERR_INVALID_ARG, "x and the four outputs must be non-NULL");
+        if (!aligned(x, esize)) return fail(NVFP4_ERR_UNSUPPORTED, "x must be aligned to its element size");
+        if (!aligned(codes, 4) || !aligned(codes_t, 8))
+            return fail(NVFP4_ERR_UNSUPPORTED, "codes must be 4-byte and codes_t 8-byte aligned");
+    }
+    const int n_partials = nvfp4::quantize_partials_count(rows, cols);
+    if (g_mode == NVFP4_G_COMPUTE && rows > 0 && cols > 0) {
+        const size_t need = nvfp4_quantize_workspace_bytes(rows, cols);
+        if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 4))
+            return fail(NVFP4_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+    }
+    nvfp4_status st = check_device();
+    if (st != NVFP4_OK) return st;
+    return launched(nvfp4::launch_quantize_both(x, in_dtype, rows, cols, ld_x, codes, scales, codes_t, scales_t, g,
+                                                g_mode, static_cast<float*>(workspace), n_partials,
+                                                static_cast<hipStream_t>(stream)),
+                    "quantize_both launch");
+}
+
 nvfp4_status nvfp4_kv_quantize_fp8(const void* x, int in_dtype, int64_t rows, int64_t cols, int64_t ld_x,
                                    uint8_t* codes, float* scale, int s_mode, void* workspace, size_t workspace_bytes,
                                    void* stream) {

@@ -274,6 +274,9 @@ __device__ __forceinline__ void skinny_step(float4v& acc, const uint4& wv, uint3
 
 int quantize_partials_count(int64_t rows, int64_t K);
 // Per-workgroup partial maxima of |x| (n_partials workgroups), as the first kernel of the quantizer.
+hipError_t launch_quantize_both(const void* x, int in_dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                                uint8_t* codes, uint8_t* scales, uint8_t* codes_t, uint8_t* scales_t, float* g,
+                                int g_mode, float* partials, int n_partials, hipStream_t stream);
 hipError_t launch_kv_fp8(const void* x, int in_dtype, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* codes,
                          float* scale, int s_mode, float* partials, int n_partials, hipStream_t stream);
 

@@ -213,8 +213,29 @@ constexpr int kTRows = 4 * (64 / kTLanesC) * 16;   // rows per workgroup tile (5
 
 // MODE: kTEncode (plain), kTEncodeRht (transformed blocks), kTAmaxRht (no
 // encoding: max |v| of the transformed blocks, one partial per workgroup into
-// amax_out, tiles by grid stride).
-enum { kTEncode = 0, kTEncodeRht = 1, kTAmaxRht = 2 };
+// amax_out, tiles by grid stride), kTBoth (plain, and from the same registers
+// the row encoding too: a row block of 16 columns spans 16/kVec neighbouring
+// lanes, which combine their maxima by lane exchange and each encode their own
+// kVec elements; needs cols % 16 == 0).
+enum { kTEncode = 0, kTEncodeRht = 1, kTAmaxRht = 2, kTBoth = 3 };
+
+// The row-block part of a lane's patch: NE (8 or 4) elements of one row whose
+// 16-element block has max |v| = bamax; the same operations as encode_block.
+template <int NE>
+__device__ __forceinline__ uint32_t encode_part(const float* v, float bamax, float s_enc, const float* rtab,
+                                                uint32_t& scale) {
+    const uint32_t S = e4m3_rne_sat(div6(bamax * s_enc));
+    const float r = rtab[S];
+    uint32_t a = 0;
+    a = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(a, v[0] * r, v[1] * r, 1.0f, 0);
+    a = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(a, v[2] * r, v[3] * r, 1.0f, 1);
+    if constexpr (NE == 8) {
+        a = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(a, v[4] * r, v[5] * r, 1.0f, 2);
+        a = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(a, v[6] * r, v[7] * r, 1.0f, 3);
+    }
+    scale = S;
+    return a;
+}
 
 template <typename T, int MODE>
 __global__ __launch_bounds__(kQThreads) void encode_t_kernel(const T* __restrict__ x, int64_t rows, int64_t cols,
@@ -222,7 +243,9 @@ __global__ __launch_bounds__(kQThreads) void encode_t_kernel(const T* __restrict
                                                              uint8_t* __restrict__ scales, float* __restrict__ g_io,
                                                              int g_given, const float* __restrict__ partials,
                                                              int n_partials, int vec, uint32_t signs,
-                                                             float* __restrict__ amax_out) {
+                                                             float* __restrict__ amax_out,
+                                                             uint8_t* __restrict__ codes_r = nullptr,
+                                                             uint8_t* __restrict__ scales_r = nullptr) {
     __shared__ float s_senc;
     __shared__ float rtab[128];
     float s_enc = 0.0f, m = 0.0f;
@@ -269,13 +292,36 @@ __global__ __launch_bounds__(kQThreads) void encode_t_kernel(const T* __restrict
 #pragma unroll
                 for (int k = 0; k < kVec; ++k) e[i][k] = c0 + k < cols ? src[i * ld + k] : T(0);
         }
+        if constexpr (MODE == kTBoth) {
+            // row blocks: lanes cl, cl ^ 1 (and cl ^ 2 for FP32) hold one 16-column block of each row
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                float v[kVec];
+                float pm = 0.0f;
+#pragma unroll
+                for (int k = 0; k < kVec; ++k) {
+                    v[k] = elem_f32(e[i][k]);
+                    pm = fmaxf(pm, __builtin_fabsf(v[k]));
+                }
+                pm = fmaxf(pm, __shfl_xor(pm, 1, 64));
+                if constexpr (kVec == 4) pm = fmaxf(pm, __shfl_xor(pm, 2, 64));
+                uint32_t sc;
+                const uint32_t w = encode_part<kVec>(v, pm, s_enc, rtab, sc);
+                uint8_t* crow = codes_r + (r0 + i) * (cols / 2) + c0 / 2;
+                if constexpr (kVec == 8)
+                    *reinterpret_cast<uint32_t*>(crow) = w;
+                else
+                    *reinterpret_cast<uint16_t*>(crow) = (uint16_t)w;
+                if ((c0 & 15) == 0) scales_r[(r0 + i) * (cols / 16) + c0 / 16] = (uint8_t)sc;
+            }
+        }
 #pragma unroll
         for (int k = 0; k < kVec; ++k) {
             if (c0 + k >= cols) break;
             float v[16];
 #pragma unroll
             for (int i = 0; i < 16; ++i) v[i] = elem_f32(e[i][k]);
-            if (MODE != kTEncode) rht16(v, signs);
+            if (MODE == kTEncodeRht || MODE == kTAmaxRht) rht16(v, signs);
             if (MODE == kTAmaxRht) {
                 m = fmaxf(m, block_amax(v));
                 continue;
@@ -459,6 +505,40 @@ static void launch_rows(const T* xp, int64_t rows, int64_t K, int64_t ld_x, uint
     else
         hipLaunchKernelGGL((encode_kernel<T, false>), dim3(grid), dim3(kQThreads), 0, stream, xp, rows, K, ld_x,
                            codes, scales, g, given, partials, n_partials, 0u);
+}
+
+hipError_t launch_quantize_both(const void* x, int in_dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                                uint8_t* codes, uint8_t* scales, uint8_t* codes_t, uint8_t* scales_t, float* g,
+                                int g_mode, float* partials, int n_partials, hipStream_t stream) {
+    const int given = (g_mode == NVFP4_G_GIVEN);
+    if (rows == 0 || cols == 0) {
+        if (!given) hipLaunchKernelGGL(write_unit_g_kernel, dim3(1), dim3(1), 0, stream, g);
+        return hipGetLastError();
+    }
+    const int esize = in_dtype == NVFP4_IN_BF16 ? 2 : 4;
+    const int vec = (reinterpret_cast<uintptr_t>(x) % 16 == 0) && (ld_x == cols || (ld_x * esize) % 16 == 0);
+    const int vec_rows = (reinterpret_cast<uintptr_t>(x) % 16 == 0) && (ld_x * esize) % 16 == 0;
+    const int64_t tcols = kTLanesC * (16 / esize);
+    const int64_t tiles = ((rows + kTRows - 1) / kTRows) * ((cols + tcols - 1) / tcols);
+    const int grid = (int)(tiles < (1 << 24) ? tiles : (1 << 24));
+    if (in_dtype == NVFP4_IN_BF16) {
+        const uint16_t* xp = static_cast<const uint16_t*>(x);
+        if (!given)
+            hipLaunchKernelGGL(amax_partials_kernel<uint16_t>, dim3(n_partials), dim3(kQThreads), 0, stream, xp,
+                               rows, cols, ld_x, partials, vec);
+        hipLaunchKernelGGL((encode_t_kernel<uint16_t, kTBoth>), dim3(grid), dim3(kQThreads), 0, stream, xp, rows,
+                           cols, ld_x, codes_t, scales_t, g, given, partials, n_partials, vec_rows, 0u, nullptr,
+                           codes, scales);
+    } else {
+        const float* xp = static_cast<const float*>(x);
+        if (!given)
+            hipLaunchKernelGGL(amax_partials_kernel<float>, dim3(n_partials), dim3(kQThreads), 0, stream, xp, rows,
+                               cols, ld_x, partials, vec);
+        hipLaunchKernelGGL((encode_t_kernel<float, kTBoth>), dim3(grid), dim3(kQThreads), 0, stream, xp, rows, cols,
+                           ld_x, codes_t, scales_t, g, given, partials, n_partials, vec_rows, 0u, nullptr, codes,
+                           scales);
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_kv_fp8(const void* x, int in_dtype, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* codes,

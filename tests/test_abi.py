@@ -40,7 +40,7 @@ def test_header_declares_the_boundary():
     for required in ["nvfp4_quantize", "nvfp4_pack_weights", "nvfp4_gemm", "nvfp4_last_error",
                      "nvfp4_quantize_workspace_bytes", "nvfp4_packed_weight_bytes", "nvfp4_unpack_weights",
                      "nvfp4_gemm_workspace_bytes", "nvfp4_abi_version", "nvfp4_device_check", "nvfp4_quantize_t", "nvfp4_quantize_rht", "nvfp4_quantize_t_rht",
-                     "nvfp4_gemm_ex", "nvfp4_linear_ex", "nvfp4_kv_quantize_fp8"]:
+                     "nvfp4_gemm_ex", "nvfp4_linear_ex", "nvfp4_kv_quantize_fp8", "nvfp4_quantize_both"]:
         assert required in names
 
 
@@ -362,3 +362,24 @@ def test_kv_fp8_validation():
         assert kv() == nv.NVFP4_ERR_NO_DEVICE
         assert kv(ws=None, ws_bytes=0, s_mode=nv.NVFP4_G_GIVEN, cols=7, ld_x=9, x=FAKE + 2) == nv.NVFP4_ERR_NO_DEVICE
         assert kv(rows=0, x=None, codes=None) == nv.NVFP4_ERR_NO_DEVICE
+
+
+def test_quantize_both_validation():
+    def qb(**kw):
+        a = dict(x=FAKE, in_dtype=nv.NVFP4_IN_BF16, rows=32, cols=48, ld_x=48, c=FAKE, s=FAKE, ct=FAKE, st=FAKE,
+                 g=FAKE, g_mode=nv.NVFP4_G_COMPUTE, ws=FAKE, ws_bytes=1 << 16)
+        a.update(kw)
+        return nv.lib.nvfp4_quantize_both(a["x"], a["in_dtype"], a["rows"], a["cols"], a["ld_x"], a["c"], a["s"],
+                                          a["ct"], a["st"], a["g"], a["g_mode"], a["ws"], a["ws_bytes"], None)
+    assert qb(in_dtype=3) == nv.NVFP4_ERR_INVALID_ARG
+    assert qb(g=None) == nv.NVFP4_ERR_INVALID_ARG
+    assert qb(ct=None) == nv.NVFP4_ERR_INVALID_ARG
+    assert qb(rows=24) == nv.NVFP4_ERR_SHAPE
+    assert qb(cols=40, ld_x=40) == nv.NVFP4_ERR_SHAPE
+    assert qb(ld_x=32) == nv.NVFP4_ERR_SHAPE
+    assert qb(c=FAKE + 2) == nv.NVFP4_ERR_UNSUPPORTED
+    assert qb(ct=FAKE + 4) == nv.NVFP4_ERR_UNSUPPORTED
+    assert qb(ws_bytes=0) == nv.NVFP4_ERR_WORKSPACE
+    if _no_gpu():
+        assert qb() == nv.NVFP4_ERR_NO_DEVICE
+        assert qb(ld_x=50, x=FAKE + 2, ws=None, ws_bytes=0, g_mode=nv.NVFP4_G_GIVEN) == nv.NVFP4_ERR_NO_DEVICE

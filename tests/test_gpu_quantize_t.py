@@ -155,3 +155,43 @@ def test_repeat_deterministic():
         again = nv.quantize_t(xd)
         torch.cuda.synchronize()
         assert all(torch.equal(p, q) for p, q in zip(first, again))
+
+
+@pytest.mark.parametrize("rows,cols", [(16, 16), (48, 80), (272, 144), (1024, 1040)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_both_orientations(rows, cols, dtype):
+    """nvfp4_quantize_both: the row and the column encodings from one read, each bit for bit the oracle's
+    (and the GPU's separate calls')."""
+    x = workloads.random_matrix(1400 + rows + cols, rows, cols, dtype=dtype)
+    x[rows // 3, cols // 5] = F32(29.0)
+    xd = to_dev(x, dtype)
+    say(f"quantize both orientations {dtype} {rows}x{cols}")
+    (c, s, g), (ct, st, gt) = nv.quantize_both(xd)
+    torch.cuda.synchronize()
+    assert_quant_equal(c, s, g, ref.quantize(x), what=f"rows {dtype} {rows}x{cols}")
+    assert_quant_equal(ct, st, gt, ref.quantize_t(x), what=f"cols {dtype} {rows}x{cols}")
+    sep_t = nv.quantize_t(xd)
+    torch.cuda.synchronize()
+    assert torch.equal(ct, sep_t[0]) and torch.equal(st, sep_t[1])
+    (c, s, g), (ct, st, _) = nv.quantize_both(xd, g=0.25)
+    torch.cuda.synchronize()
+    assert_quant_equal(c, s, g, ref.quantize(x, "given", 0.25), what=f"rows given {dtype}")
+    assert_quant_equal(ct, st, g, ref.quantize_t(x, "given", 0.25), what=f"cols given {dtype}")
+
+
+def test_both_orientations_strided_workload():
+    """The nGPT gradient-shaped tensor [8192 x 4096] bf16 viewed with a padded row stride: sampled rows of
+    both encodings against the oracle."""
+    x = workloads.random_matrix(1450, 8192, 4096, 1e-3, "bf16")
+    big = torch.zeros((8192, 4096 + 64), dtype=torch.bfloat16, device=DEV)
+    big[:, :4096] = to_dev(x, "bf16")
+    say("quantize both orientations 8192x4096 bf16, ld = 4160")
+    (c, s, g), (ct, st, _) = nv.quantize_both(big[:, :4096])
+    torch.cuda.synchronize()
+    g_ref = ref.global_scale(F32(np.max(np.abs(x))))
+    rows = _sampled(8192, 11, 24)
+    assert_quant_equal(c, s, g, ref.quantize(x[rows], "given", g_ref), rows=torch.from_numpy(rows).to(DEV),
+                       what="rows")
+    cols = _sampled(4096, 12, 24)
+    assert_quant_equal(ct, st, g, ref.quantize_t(x[:, cols], "given", g_ref), rows=torch.from_numpy(cols).to(DEV),
+                       what="cols")
