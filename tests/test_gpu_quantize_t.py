@@ -195,3 +195,45 @@ def test_both_orientations_strided_workload():
     cols = _sampled(4096, 12, 24)
     assert_quant_equal(ct, st, g, ref.quantize_t(x[:, cols], "given", g_ref), rows=torch.from_numpy(cols).to(DEV),
                        what="cols")
+
+
+def test_graph_replays_of_the_training_quantizers():
+    """quantize_t, quantize_both, the RHT variants and the FP8 KV quantizer (g or the scale computed, so
+    the amax pass runs too) captured in one HIP graph: every replay equals the eager calls."""
+    x = workloads.random_matrix(1500, 512, 384, 0.5, "bf16")
+    xd = to_dev(x, "bf16")
+    rows, cols = x.shape
+    ws = torch.empty((max(nv.nvfp4_quantize_workspace_bytes(rows, cols), 256),), dtype=torch.uint8, device=DEV)
+    outs_t = nv.empty_quantized(cols, rows, DEV)
+    outs_b = nv.empty_quantized(rows, cols, DEV) + nv.empty_quantized(cols, rows, DEV)[:2]
+    outs_r = nv.empty_quantized(rows, cols, DEV)
+    outs_rt = nv.empty_quantized(cols, rows, DEV)
+    kv_c = torch.empty((rows, cols), dtype=torch.uint8, device=DEV)
+    kv_s = torch.empty((1,), dtype=torch.float32, device=DEV)
+    ws2, ws3, ws4, ws5 = (torch.empty_like(ws) for _ in range(4))
+
+    def run(s):
+        nv.nvfp4_quantize_t(xd, *outs_t, nv.NVFP4_G_COMPUTE, ws, stream=s)
+        c, sc, g, ct, st = outs_b
+        nv.nvfp4_quantize_both(xd, c, sc, ct, st, g, nv.NVFP4_G_COMPUTE, ws2, stream=s)
+        nv.nvfp4_quantize_rht(xd, 0x5A5A, *outs_r, nv.NVFP4_G_COMPUTE, ws3, stream=s)
+        nv.nvfp4_quantize_t_rht(xd, 0x0F0F, *outs_rt, nv.NVFP4_G_COMPUTE, ws4, stream=s)
+        nv.nvfp4_kv_quantize_fp8(xd, kv_c, kv_s, nv.NVFP4_G_COMPUTE, ws5, stream=s)
+
+    tensors = list(outs_t) + list(outs_b) + list(outs_r) + list(outs_rt) + [kv_c, kv_s]
+    say("training quantizers: graph replays")
+    strm = torch.cuda.Stream()
+    with torch.cuda.stream(strm):
+        run(strm)
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in tensors]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=strm):
+        run(strm)
+    for _ in range(3):
+        for t in tensors:
+            t.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert all(torch.equal(a, b) for a, b in zip(tensors, eager))
