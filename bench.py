@@ -207,7 +207,16 @@ def main():
 
         def quant_t_only(i):
             nv.nvfp4_quantize_t(x, *xt[:3], nv.NVFP4_G_COMPUTE, xt[3])
-        bwd = (step_backward, quant_t_only)
+
+        # weight re-quantization per training step (W changes after every optimizer step): W along K, packed
+        wq = qbufs(N, K)
+        blob_w = torch.empty((nv.nvfp4_packed_weight_bytes([N], K),), dtype=torch.uint8, device=dev)
+
+        def requant_w(i):
+            nv.nvfp4_quantize(w_full, *wq[:3], nv.NVFP4_G_COMPUTE, wq[3], rows=N, K=K, ld_x=K,
+                              in_dtype=nv.NVFP4_IN_BF16)
+            nv.nvfp4_pack_weights([wq[:3]], K, blob_w)
+        bwd = (step_backward, quant_t_only, requant_w)
 
     if rht_on:
         codes_r, scales_r, g_r = nv.empty_quantized(M, K, dev)
@@ -311,6 +320,7 @@ def main():
     t_kvg = timed(kv[1], k_steps, min(warmup, k_steps)) / k_steps if kv else None
     t_bwd = timed(bwd[0], k_steps, min(warmup, k_steps)) / k_steps if bwd else None
     t_qt = timed(bwd[1], k_steps, min(warmup, k_steps)) / k_steps if bwd else None
+    t_rq = timed(bwd[2], k_steps, min(warmup, k_steps)) / k_steps if bwd else None
 
     flops = 2.0 * M * N * K
     tflops = flops / t_step / 1e12
@@ -470,6 +480,7 @@ def main():
                                   t_bwd * 1e6 if t_bwd else None,
                               "backward tflops": 2.0 * flops / t_bwd / 1e12 if t_bwd else None,
                               "quantize_t alone (X^T, g computed)": t_qt * 1e6 if t_qt else None,
+                              "weight re-quantization per step (W quantized and packed)": t_rq * 1e6 if t_rq else None,
                               "quantize_t GB/s (read x once, write codes and scales)":
                                   (x_in_bytes + x_q_bytes) / t_qt / 1e9 if t_qt else None},
         "step_gbs": (x_in_bytes + w_bytes + x_q_bytes + M * N * 4) / t_step / 1e9,
