@@ -146,13 +146,15 @@ def main():
         wq_bufs = [nv.empty_quantized(w.shape[0], K, dev) for w in w_dev]
         wq_ws = [torch.empty((max(nv.nvfp4_quantize_workspace_bytes(w.shape[0], K), 256),), dtype=torch.uint8,
                              device=dev) for w in w_dev]
+        blob_step = torch.empty_like(packed.blob)
 
     def step(i):
-        if wl.quantize_w_in_step:   # tiny case: both operands quantized inside the step
+        desc = weights[i % copies].desc
+        if wl.quantize_w_in_step:   # tiny case: both operands quantized inside the step, the weights packed
             for w, (c, s, gg), wsb in zip(w_dev, wq_bufs, wq_ws):
                 nv.nvfp4_quantize(w, c, s, gg, nv.NVFP4_G_COMPUTE, wsb)
-        nv.nvfp4_linear(x, codes, scales, g, weights[i % copies].desc, y, lin_ws, M=M, ld_x=K, in_dtype=in_dtype,
-                        ld_y=N)
+            desc = nv.nvfp4_pack_weights(wq_bufs, K, blob_step)
+        nv.nvfp4_linear(x, codes, scales, g, desc, y, lin_ws, M=M, ld_x=K, in_dtype=in_dtype, ld_y=N)
 
     # the same layer without per-tensor scaling (the nGPT recipe): g given as 1, no amax pass
     codes1, scales1, g1 = nv.empty_quantized(M, K, dev)
@@ -462,7 +464,11 @@ def main():
                    "weight_copies": copies, "graph": not args.no_graph, "variants_timed": extra},
         "roofline": roof,
         "cpu_baseline": cpu,
-        "step_breakdown_us": {"step (nvfp4_linear)": t_step * 1e6, "launches_per_step": 1 if skinny else 3,
+        # launches: few tokens one kernel; otherwise amax + encode + product (two product launches when the
+        # weight has a ragged column edge, as the GDN projection); tiny adds the weights' quantize and pack
+        "step_breakdown_us": {"step (nvfp4_linear)": t_step * 1e6,
+                              "launches_per_step": 1 if skinny else (5 if wl.quantize_w_in_step else
+                                                                     (4 if N % 256 else 3)),
                               "quantize alone": t_quant * 1e6, "gemm alone": t_gemm * 1e6,
                               "step with g given (no amax pass)": t_given * 1e6 if t_given else None,
                               "tflops with g given": flops / t_given / 1e12 if t_given else None,
