@@ -218,7 +218,19 @@ def main():
             nv.nvfp4_quantize(w_full, *wq[:3], nv.NVFP4_G_COMPUTE, wq[3], rows=N, K=K, ld_x=K,
                               in_dtype=nv.NVFP4_IN_BF16)
             nv.nvfp4_pack_weights([wq[:3]], K, blob_w)
-        bwd = (step_backward, quant_t_only, requant_w)
+
+        # both packed operands of W per step (forward along K, backward transposed), separately and fused
+        blob_wt2 = torch.empty_like(blob_wt)
+        g_tr = torch.empty((1,), dtype=torch.float32, device=dev)
+
+        def requant_both_separate(i):
+            requant_w(i)
+            nv.nvfp4_quantize_t(w_full, *wt[:3], nv.NVFP4_G_COMPUTE, wt[3])
+            nv.nvfp4_pack_weights([wt[:3]], N, blob_wt)
+
+        def requant_both_fused(i):
+            nv.nvfp4_pack_weights_train(w_full, g_tr, blob_w, blob_wt2, nv.NVFP4_G_COMPUTE, wq[3])
+        bwd = (step_backward, quant_t_only, requant_w, requant_both_separate, requant_both_fused)
 
     if rht_on:
         codes_r, scales_r, g_r = nv.empty_quantized(M, K, dev)
@@ -323,6 +335,8 @@ def main():
     t_bwd = timed(bwd[0], k_steps, min(warmup, k_steps)) / k_steps if bwd else None
     t_qt = timed(bwd[1], k_steps, min(warmup, k_steps)) / k_steps if bwd else None
     t_rq = timed(bwd[2], k_steps, min(warmup, k_steps)) / k_steps if bwd else None
+    t_rq2 = timed(bwd[3], k_steps, min(warmup, k_steps)) / k_steps if bwd else None
+    t_rqf = timed(bwd[4], k_steps, min(warmup, k_steps)) / k_steps if bwd else None
 
     flops = 2.0 * M * N * K
     tflops = flops / t_step / 1e12
@@ -487,6 +501,10 @@ def main():
                               "backward tflops": 2.0 * flops / t_bwd / 1e12 if t_bwd else None,
                               "quantize_t alone (X^T, g computed)": t_qt * 1e6 if t_qt else None,
                               "weight re-quantization per step (W quantized and packed)": t_rq * 1e6 if t_rq else None,
+                              "W and W^T packed per step (quantize, quantize_t, two packs)":
+                                  t_rq2 * 1e6 if t_rq2 else None,
+                              "W and W^T packed per step (nvfp4_pack_weights_train, one read)":
+                                  t_rqf * 1e6 if t_rqf else None,
                               "quantize_t GB/s (read x once, write codes and scales)":
                                   (x_in_bytes + x_q_bytes) / t_qt / 1e9 if t_qt else None},
         "step_gbs": (x_in_bytes + w_bytes + x_q_bytes + M * N * 4) / t_step / 1e9,

@@ -287,6 +287,32 @@ nvfp4_status nvfp4_pack_weights(int n_modules, const int64_t* module_rows, int64
                                 const float* const* g_w, void* blob, size_t blob_bytes,
                                 nvfp4_weight_desc* desc_out, void* stream);
 
+/* Weight re-quantization for a training step ("Normalized Architectures are
+ * Natively 4-Bit": nGPT trains end to end in NVFP4, abstract and section
+ * "Approach"; the weight changes after every optimizer step).  One weight
+ * W [n][k] (a single module, one g) is read once and written as both packed
+ * operands: blob_fwd holds W quantized along k (for Y = X . W^T, as
+ * nvfp4_pack_weights of nvfp4_quantize(W) would), blob_bwd holds W^T
+ * quantized along n (for dX = dY . W, as nvfp4_pack_weights of
+ * nvfp4_quantize_t(W) would); both bit for bit, including padding rows,
+ * column scales and the header fields.
+ *
+ * w            : device, n x k elements of in_dtype, row r at w + r*ld_w,
+ *                aligned to the element size
+ * n, k         : positive multiples of 128 (each is the other blob's K)
+ * g, g_mode    : as for nvfp4_quantize (one g for both blobs)
+ * blob_fwd     : device, 256-byte aligned, >= nvfp4_packed_weight_bytes({n}, k)
+ * blob_bwd     : device, 256-byte aligned, >= nvfp4_packed_weight_bytes({k}, n)
+ * desc_fwd/bwd : host, filled in on success (blob pointers set)
+ * workspace    : COMPUTE mode, >= nvfp4_quantize_workspace_bytes(n, k)
+ * Errors: NVFP4_ERR_SHAPE for n or k not a positive multiple of 128 or too
+ * large, NVFP4_ERR_WORKSPACE for short blobs or workspace, the rest as for
+ * nvfp4_quantize; nothing is launched then. */
+nvfp4_status nvfp4_pack_weights_train(const void* w, int in_dtype, int64_t n, int64_t k, int64_t ld_w, float* g,
+                                      int g_mode, void* blob_fwd, size_t blob_fwd_bytes, nvfp4_weight_desc* desc_fwd,
+                                      void* blob_bwd, size_t blob_bwd_bytes, nvfp4_weight_desc* desc_bwd,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
 /*
  * Inverse of the packing, for checking and for saving weights: writes the
  * canonical codes [n][K/2], scales [n][K/16] and per-row column scale [n]

@@ -121,6 +121,9 @@ def _load():
         "nvfp4_quantize_workspace_bytes": (c_sz, [c_i64, c_i64]),
         "nvfp4_quantize": (c_int, [c_vp, c_int, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_int, c_vp, c_sz, c_vp]),
         "nvfp4_quantize_t": (c_int, [c_vp, c_int, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_int, c_vp, c_sz, c_vp]),
+        "nvfp4_pack_weights_train": (c_int, [c_vp, c_int, c_i64, c_i64, c_i64, c_vp, c_int, c_vp, c_sz,
+                                             ctypes.POINTER(WeightDesc), c_vp, c_sz, ctypes.POINTER(WeightDesc), c_vp,
+                                             c_sz, c_vp]),
         "nvfp4_quantize_both": (c_int, [c_vp, c_int, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_vp,
                                         c_sz, c_vp]),
         "nvfp4_kv_quantize_fp8": (c_int, [c_vp, c_int, c_i64, c_i64, c_i64, c_vp, c_vp, c_int, c_vp, c_sz, c_vp]),
@@ -262,6 +265,17 @@ def nvfp4_quantize_both(x, codes, scales, codes_t, scales_t, g, g_mode=NVFP4_G_C
     ws_bytes = workspace.numel() * workspace.element_size() if isinstance(workspace, torch.Tensor) else 0
     _check(_lib.nvfp4_quantize_both(_ptr(x), in_dtype, rows, cols, ld_x, _ptr(codes), _ptr(scales), _ptr(codes_t),
                                     _ptr(scales_t), _ptr(g), g_mode, _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def nvfp4_pack_weights_train(w, g, blob_fwd, blob_bwd, g_mode=NVFP4_G_COMPUTE, workspace=None, stream=None):
+    """Both packed operands of a training weight w [n, k] from one read; returns (desc_fwd, desc_bwd)."""
+    n, k, ld_w, in_dtype = _layout(w, "w must have unit stride along k")
+    ws_bytes = workspace.numel() * workspace.element_size() if isinstance(workspace, torch.Tensor) else 0
+    df, db = WeightDesc(), WeightDesc()
+    _check(_lib.nvfp4_pack_weights_train(_ptr(w), in_dtype, n, k, ld_w, _ptr(g), g_mode, _ptr(blob_fwd),
+                                         blob_fwd.numel(), ctypes.byref(df), _ptr(blob_bwd), blob_bwd.numel(),
+                                         ctypes.byref(db), _ptr(workspace), ws_bytes, _stream(stream)))
+    return df, db
 
 
 def nvfp4_kv_quantize_fp8(x, codes, scale, s_mode=NVFP4_G_COMPUTE, workspace=None, stream=None):
@@ -486,6 +500,25 @@ class PackedWeight:
         colscale = torch.empty((n,), dtype=torch.float32, device=self.blob.device)
         nvfp4_unpack_weights(self.desc, codes, scales, colscale, stream)
         return codes, scales, colscale
+
+
+def pack_weights_train(w: torch.Tensor, g=None, stream=None):
+    """(forward PackedWeight of w along k, backward PackedWeight of w^T along n, g) for a training weight
+    w [n, k], from one read of w (g computed when None)."""
+    n, k = w.shape
+    fwd, bwd = PackedWeight.__new__(PackedWeight), PackedWeight.__new__(PackedWeight)
+    fwd.blob = torch.empty((nvfp4_packed_weight_bytes([n], k),), dtype=torch.uint8, device=w.device)
+    bwd.blob = torch.empty((nvfp4_packed_weight_bytes([k], n),), dtype=torch.uint8, device=w.device)
+    gt = torch.empty((1,), dtype=torch.float32, device=w.device)
+    if g is None:
+        ws = torch.empty((max(nvfp4_quantize_workspace_bytes(n, k), 1),), dtype=torch.uint8, device=w.device)
+        fwd.desc, bwd.desc = nvfp4_pack_weights_train(w, gt, fwd.blob, bwd.blob, NVFP4_G_COMPUTE, ws, stream)
+    else:
+        gt.fill_(float(g)) if not isinstance(g, torch.Tensor) else gt.copy_(g.reshape(1))
+        fwd.desc, bwd.desc = nvfp4_pack_weights_train(w, gt, fwd.blob, bwd.blob, NVFP4_G_GIVEN, None, stream)
+    fwd.module_rows, fwd.K = [n], k
+    bwd.module_rows, bwd.K = [k], n
+    return fwd, bwd, gt
 
 
 def linear_workspace(M: int, x_dtype, w: "PackedWeight", device="cuda") -> torch.Tensor:

@@ -331,6 +331,47 @@ nvfp4_status nvfp4_pack_weights(int n_modules, const int64_t* module_rows, int64
     return ok();
 }
 
+nvfp4_status nvfp4_pack_weights_train(const void* w, int in_dtype, int64_t n, int64_t k, int64_t ld_w, float* g,
+                                      int g_mode, void* blob_fwd, size_t blob_fwd_bytes, nvfp4_weight_desc* desc_fwd,
+                                      void* blob_bwd, size_t blob_bwd_bytes, nvfp4_weight_desc* desc_bwd,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+    if (in_dtype != NVFP4_IN_F32 && in_dtype != NVFP4_IN_BF16)
+        return fail(NVFP4_ERR_INVALID_ARG, "unknown input dtype %d", in_dtype);
+    if (g_mode != NVFP4_G_COMPUTE && g_mode != NVFP4_G_GIVEN)
+        return fail(NVFP4_ERR_INVALID_ARG, "unknown g mode %d", g_mode);
+    if (w == nullptr || g == nullptr || desc_fwd == nullptr || desc_bwd == nullptr)
+        return fail(NVFP4_ERR_INVALID_ARG, "w, g and both descriptors must be non-NULL");
+    if (n <= 0 || k <= 0 || n % nvfp4::kPackK != 0 || k % nvfp4::kPackK != 0)
+        return fail(NVFP4_ERR_SHAPE, "n and k must be positive multiples of %d (n=%lld k=%lld)", nvfp4::kPackK,
+                    (long long)n, (long long)k);
+    if (ld_w < k || ld_w > INT64_MAX / n) return fail(NVFP4_ERR_SHAPE, "bad ld_w (%lld)", (long long)ld_w);
+    const int esize = in_dtype == NVFP4_IN_BF16 ? 2 : 4;
+    if (!aligned(w, esize)) return fail(NVFP4_ERR_UNSUPPORTED, "w must be aligned to its element size");
+    nvfp4_weight_desc df, db;
+    if (!blob_layout(1, &n, k, &df) || !blob_layout(1, &k, n, &db)) return fail(NVFP4_ERR_SHAPE, "weight too large");
+    if (blob_fwd == nullptr || blob_bwd == nullptr || !aligned(blob_fwd, 256) || !aligned(blob_bwd, 256))
+        return fail(NVFP4_ERR_INVALID_ARG, "blobs must be non-NULL and 256-byte aligned");
+    if (blob_fwd_bytes < df.blob_bytes || blob_bwd_bytes < db.blob_bytes)
+        return fail(NVFP4_ERR_WORKSPACE, "blobs need %zu and %zu bytes (got %zu and %zu)", df.blob_bytes,
+                    db.blob_bytes, blob_fwd_bytes, blob_bwd_bytes);
+    const int n_partials = nvfp4::quantize_partials_count(n, k);
+    if (g_mode == NVFP4_G_COMPUTE) {
+        const size_t need = nvfp4_quantize_workspace_bytes(n, k);
+        if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 4))
+            return fail(NVFP4_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+    }
+    nvfp4_status st = check_device();
+    if (st != NVFP4_OK) return st;
+    df.blob = blob_fwd;
+    db.blob = blob_bwd;
+    hipError_t e = nvfp4::launch_pack_train(w, in_dtype, n, k, ld_w, g, g_mode, static_cast<float*>(workspace),
+                                            n_partials, df, db, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(NVFP4_ERR_HIP, "pack_train launch: %s", hipGetErrorString(e));
+    *desc_fwd = df;
+    *desc_bwd = db;
+    return ok();
+}
+
 nvfp4_status nvfp4_unpack_weights(const nvfp4_weight_desc* w, uint8_t* codes, uint8_t* scales, float* colscale,
                                   void* stream) {
     nvfp4_status st = check_desc(w);

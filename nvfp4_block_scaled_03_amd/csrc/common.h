@@ -277,6 +277,11 @@ int quantize_partials_count(int64_t rows, int64_t K);
 hipError_t launch_quantize_both(const void* x, int in_dtype, int64_t rows, int64_t cols, int64_t ld_x,
                                 uint8_t* codes, uint8_t* scales, uint8_t* codes_t, uint8_t* scales_t, float* g,
                                 int g_mode, float* partials, int n_partials, hipStream_t stream);
+// Both packed operands of one training weight (forward: rows x cols along cols;
+// backward: its transpose), from one read; the descriptors are filled in.
+hipError_t launch_pack_train(const void* x, int in_dtype, int64_t rows, int64_t cols, int64_t ld_x, float* g,
+                             int g_mode, float* partials, int n_partials, const nvfp4_weight_desc& df,
+                             const nvfp4_weight_desc& db, hipStream_t stream);
 hipError_t launch_kv_fp8(const void* x, int in_dtype, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* codes,
                          float* scale, int s_mode, float* partials, int n_partials, hipStream_t stream);
 

@@ -507,6 +507,186 @@ static void launch_rows(const T* xp, int64_t rows, int64_t K, int64_t ld_x, uint
                            codes, scales, g, given, partials, n_partials, 0u);
 }
 
+// ---------------------------------------------------------------------------
+// Weight re-quantization for a training step: one weight W [n][k] read once,
+// both packed operands written (the forward product's W along k, the backward
+// dX = dY . W product's W^T along n), with one g.  The same lane patches as the
+// x^T encoder (row blocks across neighbouring lanes, column blocks inside a
+// lane), with the stores going straight to the packed blob order; the tiles
+// also cover the padding rows of both blobs (zero input encodes to zero codes
+// and zero scales), and the column scales and headers are written here too.
+// ---------------------------------------------------------------------------
+struct PackedOut {
+    uint8_t *fwd, *bwd;                 // blob bases
+    size_t f_codes, f_scales, f_cs;     // offsets inside the forward blob
+    size_t b_codes, b_scales, b_cs;     // and the backward one
+    int64_t ksf, ksb;                   // k-steps per row of each blob (k / 128, n / 128)
+    int64_t n_pad, k_pad;               // padded row counts of the forward and backward blobs
+};
+
+__device__ __forceinline__ size_t code_unit(int64_t row, int64_t kb, int64_t ks_per_row) {
+    return ((size_t)((row >> 4) * ks_per_row + (kb >> 3)) * 64 + (size_t)(((kb & 7) >> 1) * 16) + (size_t)(row & 15));
+}
+__device__ __forceinline__ size_t scale_unit(int64_t row, int64_t kb, int64_t ks_per_row) {
+    return (size_t)((row >> 4) * ks_per_row + (kb >> 3)) * 16 + (size_t)(row & 15);
+}
+
+template <typename T>
+__global__ __launch_bounds__(kQThreads) void pack_train_kernel(const T* __restrict__ x, int64_t rows, int64_t cols,
+                                                               int64_t ld, float* __restrict__ g_io, int g_given,
+                                                               const float* __restrict__ partials, int n_partials,
+                                                               int vec, PackedOut o) {
+    __shared__ float s_senc, s_g;
+    __shared__ float rtab[128];
+    if (g_given) {
+        if (threadIdx.x == 0) {
+            s_g = g_io[0];
+            s_senc = 1.0f / s_g;
+        }
+    } else {
+        float pm = 0.0f;
+        for (int i = threadIdx.x; i < n_partials; i += kQThreads) pm = fmaxf(pm, partials[i]);
+        pm = block_max<kQThreads>(pm);
+        if (threadIdx.x == 0) {
+            const float g = global_scale_from_amax(pm);
+            s_g = g;
+            s_senc = 1.0f / g;
+            if (blockIdx.x == 0) g_io[0] = g;
+        }
+    }
+    __syncthreads();
+    const float s_enc = s_senc, g = s_g;
+    fill_recip_table(rtab, s_enc, threadIdx.x, kQThreads);
+    __syncthreads();
+
+    // column scales (g for real rows, 0 for padding) and the two headers
+    for (int64_t i = (int64_t)blockIdx.x * kQThreads + threadIdx.x; i < o.n_pad + o.k_pad;
+         i += (int64_t)gridDim.x * kQThreads) {
+        if (i < o.n_pad)
+            reinterpret_cast<float*>(o.fwd + o.f_cs)[i] = i < rows ? g : 0.0f;
+        else
+            reinterpret_cast<float*>(o.bwd + o.b_cs)[i - o.n_pad] = i - o.n_pad < cols ? g : 0.0f;
+    }
+    if (blockIdx.x == 0 && threadIdx.x < 2) {
+        uint8_t* blob = threadIdx.x == 0 ? o.fwd : o.bwd;
+        uint32_t* h32 = reinterpret_cast<uint32_t*>(blob);
+        int64_t* h64 = reinterpret_cast<int64_t*>(blob + 8);
+        h32[0] = NVFP4_WEIGHT_MAGIC;
+        h32[1] = NVFP4_WEIGHT_VERSION;
+        h64[0] = threadIdx.x == 0 ? rows : cols;
+        h64[1] = threadIdx.x == 0 ? cols : rows;
+        h64[2] = threadIdx.x == 0 ? o.n_pad : o.k_pad;
+        h64[3] = 1;
+    }
+
+    constexpr int kVec = 16 / (int)sizeof(T);
+    constexpr int kRG = 64 / kTLanesC;
+    constexpr int kTCols = kTLanesC * kVec;
+    const int64_t tiles_r = (o.n_pad + kTRows - 1) / kTRows, tiles_c = (o.k_pad + kTCols - 1) / kTCols;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int cl = lane % kTLanesC, rg = lane / kTLanesC;
+    uint8_t* const fc = o.fwd + o.f_codes;
+    uint8_t* const fs = o.fwd + o.f_scales;
+    uint8_t* const bc = o.bwd + o.b_codes;
+    uint8_t* const bs = o.bwd + o.b_scales;
+    for (int64_t tile_id = blockIdx.x; tile_id < tiles_r * tiles_c; tile_id += gridDim.x) {
+        const int64_t tr = tile_id % tiles_r, tc = tile_id / tiles_r;
+        const int64_t r0 = tr * kTRows + (w * kRG + rg) * 16;
+        const int64_t c0 = tc * kTCols + (int64_t)kVec * cl;
+        if (r0 >= o.n_pad || c0 >= o.k_pad) continue;   // whole 16-row groups and 16-column blocks
+        const T* src = x + r0 * ld + c0;
+        T e[16][kVec];
+        if (vec && r0 + 16 <= rows && c0 + kVec <= cols) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) *reinterpret_cast<uint4*>(e[i]) = *reinterpret_cast<const uint4*>(src + i * ld);
+        } else {                           // padding, ragged edges or unaligned rows: element by element
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+#pragma unroll
+                for (int k = 0; k < kVec; ++k)
+                    e[i][k] = (r0 + i < rows && c0 + k < cols) ? src[i * ld + k] : T(0);
+        }
+        // row blocks (the forward operand, k = cols columns; its padding rows up to n_pad are written too):
+        // 16/kVec neighbouring lanes share a block
+        const int64_t kb = c0 >> 4;
+        const int part = (int)((c0 >> (kVec == 8 ? 3 : 2)) & (16 / kVec - 1));   // which kVec-slice of the block
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            if (c0 >= cols) break;                  // (the lanes of a block agree: cols % 16 == 0)
+            float v[kVec];
+            float pm = 0.0f;
+#pragma unroll
+            for (int k = 0; k < kVec; ++k) {
+                v[k] = elem_f32(e[i][k]);
+                pm = fmaxf(pm, __builtin_fabsf(v[k]));
+            }
+            pm = fmaxf(pm, __shfl_xor(pm, 1, 64));
+            if constexpr (kVec == 4) pm = fmaxf(pm, __shfl_xor(pm, 2, 64));
+            uint32_t sc;
+            const uint32_t wd = encode_part<kVec>(v, pm, s_enc, rtab, sc);
+            const int64_t row = r0 + i;
+            uint8_t* dst = fc + code_unit(row, kb, o.ksf) * 16 + (kb & 1) * 8 + part * (kVec / 2);
+            if constexpr (kVec == 8)
+                *reinterpret_cast<uint32_t*>(dst) = wd;
+            else
+                *reinterpret_cast<uint16_t*>(dst) = (uint16_t)wd;
+            if (part == 0) fs[scale_unit(row, kb, o.ksf) * 8 + (kb & 7)] = (uint8_t)sc;
+        }
+        // column blocks (the backward operand, k = rows; its padding rows up to k_pad are written too):
+        // output row c0 + k, block r0 / 16 along n
+        const int64_t kbt = r0 >> 4;
+#pragma unroll
+        for (int k = 0; k < kVec; ++k) {
+            if (r0 >= rows) break;
+            float v[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) v[i] = elem_f32(e[i][k]);
+            uint32_t lo, hi, sc;
+            encode_block(v, block_amax(v), s_enc, rtab, lo, hi, sc);
+            const int64_t c = c0 + k;
+            *reinterpret_cast<uint2*>(bc + code_unit(c, kbt, o.ksb) * 16 + (kbt & 1) * 8) = make_uint2(lo, hi);
+            bs[scale_unit(c, kbt, o.ksb) * 8 + (kbt & 7)] = (uint8_t)sc;
+        }
+    }
+}
+
+hipError_t launch_pack_train(const void* x, int in_dtype, int64_t rows, int64_t cols, int64_t ld_x, float* g,
+                             int g_mode, float* partials, int n_partials, const nvfp4_weight_desc& df,
+                             const nvfp4_weight_desc& db, hipStream_t stream) {
+    const int given = (g_mode == NVFP4_G_GIVEN);
+    const int esize = in_dtype == NVFP4_IN_BF16 ? 2 : 4;
+    const int vec = (reinterpret_cast<uintptr_t>(x) % 16 == 0) && (ld_x * esize) % 16 == 0;
+    const int vec_amax = (reinterpret_cast<uintptr_t>(x) % 16 == 0) && (ld_x == cols || (ld_x * esize) % 16 == 0);
+    PackedOut o;
+    o.fwd = static_cast<uint8_t*>(const_cast<void*>(df.blob));   // the blobs being written
+    o.bwd = static_cast<uint8_t*>(const_cast<void*>(db.blob));
+    o.f_codes = df.codes_offset; o.f_scales = df.scales_offset; o.f_cs = df.colscale_offset;
+    o.b_codes = db.codes_offset; o.b_scales = db.scales_offset; o.b_cs = db.colscale_offset;
+    o.ksf = df.k / kPackK;
+    o.ksb = db.k / kPackK;
+    o.n_pad = df.n_padded;
+    o.k_pad = db.n_padded;
+    const int64_t tcols = kTLanesC * (16 / esize);
+    const int64_t tiles = ((o.n_pad + kTRows - 1) / kTRows) * ((o.k_pad + tcols - 1) / tcols);
+    const int grid = (int)(tiles < (1 << 24) ? tiles : (1 << 24));
+    if (in_dtype == NVFP4_IN_BF16) {
+        const uint16_t* xp = static_cast<const uint16_t*>(x);
+        if (!given)
+            hipLaunchKernelGGL(amax_partials_kernel<uint16_t>, dim3(n_partials), dim3(kQThreads), 0, stream, xp,
+                               rows, cols, ld_x, partials, vec_amax);
+        hipLaunchKernelGGL(pack_train_kernel<uint16_t>, dim3(grid), dim3(kQThreads), 0, stream, xp, rows, cols, ld_x,
+                           g, given, partials, n_partials, vec, o);
+    } else {
+        const float* xp = static_cast<const float*>(x);
+        if (!given)
+            hipLaunchKernelGGL(amax_partials_kernel<float>, dim3(n_partials), dim3(kQThreads), 0, stream, xp, rows,
+                               cols, ld_x, partials, vec_amax);
+        hipLaunchKernelGGL(pack_train_kernel<float>, dim3(grid), dim3(kQThreads), 0, stream, xp, rows, cols, ld_x, g,
+                           given, partials, n_partials, vec, o);
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_quantize_both(const void* x, int in_dtype, int64_t rows, int64_t cols, int64_t ld_x,
                                 uint8_t* codes, uint8_t* scales, uint8_t* codes_t, uint8_t* scales_t, float* g,
                                 int g_mode, float* partials, int n_partials, hipStream_t stream) {

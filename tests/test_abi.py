@@ -40,7 +40,8 @@ def test_header_declares_the_boundary():
     for required in ["nvfp4_quantize", "nvfp4_pack_weights", "nvfp4_gemm", "nvfp4_last_error",
                      "nvfp4_quantize_workspace_bytes", "nvfp4_packed_weight_bytes", "nvfp4_unpack_weights",
                      "nvfp4_gemm_workspace_bytes", "nvfp4_abi_version", "nvfp4_device_check", "nvfp4_quantize_t", "nvfp4_quantize_rht", "nvfp4_quantize_t_rht",
-                     "nvfp4_gemm_ex", "nvfp4_linear_ex", "nvfp4_kv_quantize_fp8", "nvfp4_quantize_both"]:
+                     "nvfp4_gemm_ex", "nvfp4_linear_ex", "nvfp4_kv_quantize_fp8", "nvfp4_quantize_both",
+                     "nvfp4_pack_weights_train"]:
         assert required in names
 
 
@@ -383,3 +384,30 @@ def test_quantize_both_validation():
     if _no_gpu():
         assert qb() == nv.NVFP4_ERR_NO_DEVICE
         assert qb(ld_x=50, x=FAKE + 2, ws=None, ws_bytes=0, g_mode=nv.NVFP4_G_GIVEN) == nv.NVFP4_ERR_NO_DEVICE
+
+
+def test_pack_weights_train_validation():
+    df, db = nv.WeightDesc(), nv.WeightDesc()
+
+    def pt(**kw):
+        a = dict(w=FAKE, in_dtype=nv.NVFP4_IN_BF16, n=256, k=384, ld=384, g=FAKE, g_mode=nv.NVFP4_G_COMPUTE,
+                 bf=FAKE, bfb=1 << 30, df=ctypes.byref(df), bb=FAKE, bbb=1 << 30, db=ctypes.byref(db), ws=FAKE,
+                 wsb=1 << 16)
+        a.update(kw)
+        return nv.lib.nvfp4_pack_weights_train(a["w"], a["in_dtype"], a["n"], a["k"], a["ld"], a["g"], a["g_mode"],
+                                               a["bf"], a["bfb"], a["df"], a["bb"], a["bbb"], a["db"], a["ws"],
+                                               a["wsb"], None)
+    assert pt(in_dtype=5) == nv.NVFP4_ERR_INVALID_ARG
+    assert pt(g=None) == nv.NVFP4_ERR_INVALID_ARG
+    assert pt(df=None) == nv.NVFP4_ERR_INVALID_ARG
+    assert pt(n=200) == nv.NVFP4_ERR_SHAPE                  # the backward blob's K must be a multiple of 128
+    assert pt(k=400, ld=400) == nv.NVFP4_ERR_SHAPE
+    assert pt(ld=300) == nv.NVFP4_ERR_SHAPE
+    assert pt(w=FAKE + 1) == nv.NVFP4_ERR_UNSUPPORTED
+    assert pt(bf=FAKE + 16) == nv.NVFP4_ERR_INVALID_ARG     # blobs 256-byte aligned
+    assert pt(bfb=1024) == nv.NVFP4_ERR_WORKSPACE
+    assert pt(bbb=1024) == nv.NVFP4_ERR_WORKSPACE
+    assert pt(ws=None) == nv.NVFP4_ERR_WORKSPACE
+    if _no_gpu():
+        assert pt() == nv.NVFP4_ERR_NO_DEVICE
+        assert pt(ws=None, wsb=0, g_mode=nv.NVFP4_G_GIVEN, ld=390, w=FAKE + 2) == nv.NVFP4_ERR_NO_DEVICE

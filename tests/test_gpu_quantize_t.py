@@ -237,3 +237,49 @@ def test_graph_replays_of_the_training_quantizers():
         graph.replay()
         torch.cuda.synchronize()
         assert all(torch.equal(a, b) for a, b in zip(tensors, eager))
+
+
+def _blob_regions(pw: "nv.PackedWeight"):
+    """The written parts of a packed blob: header fields, codes, scales and column scales (the bytes between
+    them are alignment padding that no one writes)."""
+    d, b = pw.desc, host(pw.blob)
+    n_pad, k = d.n_padded, d.k
+    return (b[:40], b[d.codes_offset:d.codes_offset + n_pad * k // 2],
+            b[d.scales_offset:d.scales_offset + n_pad * k // 16], b[d.colscale_offset:d.colscale_offset + 4 * n_pad])
+
+
+@pytest.mark.parametrize("n,k,dtype,ld_pad", [(128, 128, "bf16", 0), (384, 256, "bf16", 0), (640, 384, "f32", 0),
+                                              (256, 640, "bf16", 24), (4096, 4096, "bf16", 0)])
+def test_pack_weights_train(n, k, dtype, ld_pad):
+    """Both packed operands from one read equal, byte for byte, quantize + pack and quantize_t + pack (whose
+    codes the oracle checks), padding rows, column scales and header fields included; so do their products."""
+    wt = workloads.random_matrix(1600 + n + k, n, k, 0.05, dtype)
+    wt[n // 3, k // 7] = F32(3.5)
+    if ld_pad:
+        big = np.zeros((n, k + ld_pad), F32)
+        big[:, :k] = wt
+        wd = to_dev(big, dtype)[:, :k]
+    else:
+        wd = to_dev(wt, dtype)
+    say(f"pack_weights_train {dtype} n={n} k={k} ld_pad={ld_pad}")
+    fwd, bwd, g = nv.pack_weights_train(wd)
+    ref_fwd = nv.PackedWeight([nv.quantize(wd)], k)
+    ref_bwd = nv.PackedWeight([nv.quantize_t(wd)], n)
+    torch.cuda.synchronize()
+    for got, want, what in [(fwd, ref_fwd, "forward"), (bwd, ref_bwd, "backward")]:
+        for part, (a, b) in zip(["header", "codes", "scales", "colscale"], zip(_blob_regions(got), _blob_regions(want))):
+            assert np.array_equal(a, b), f"{what} {part} differs"
+    assert np.float32(host(g)[0]) == ref.global_scale(F32(np.max(np.abs(wt))))
+    x = to_dev(workloads.random_matrix(1700 + n, 64, k, 1.0, "bf16"), "bf16")
+    xq = nv.quantize(x)
+    assert torch.equal(nv.gemm(*xq, fwd), nv.gemm(*xq, ref_fwd))
+    dy = to_dev(workloads.random_matrix(1800 + k, 64, n, 0.01, "bf16"), "bf16")
+    dq = nv.quantize(dy)
+    torch.cuda.synchronize()
+    assert torch.equal(nv.gemm(*dq, bwd), nv.gemm(*dq, ref_bwd))
+    fwd_g, bwd_g, _ = nv.pack_weights_train(wd, g=0.125)
+    ref_fwd_g = nv.PackedWeight([nv.quantize(wd, g=0.125)], k)
+    ref_bwd_g = nv.PackedWeight([nv.quantize_t(wd, g=0.125)], n)
+    torch.cuda.synchronize()
+    for got, want in [(fwd_g, ref_fwd_g), (bwd_g, ref_bwd_g)]:
+        assert all(np.array_equal(a, b) for a, b in zip(_blob_regions(got), _blob_regions(want)))
