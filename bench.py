@@ -156,6 +156,17 @@ def main():
             desc = nv.nvfp4_pack_weights(wq_bufs, K, blob_step)
         nv.nvfp4_linear(x, codes, scales, g, desc, y, lin_ws, M=M, ld_x=K, in_dtype=in_dtype, ld_y=N)
 
+    # the decode step with one weight copy, which stays in the Infinity Cache (labelled hot-cache figure)
+    step_hot = None
+    if extra and copies > 1:
+        codes_h, scales_h, g_h = nv.empty_quantized(M, K, dev)
+        y_h = torch.empty((M, N), dtype=torch.float32, device=dev)
+        lin_ws_h = nv.linear_workspace(M, xdt, packed, dev)
+
+        def step_hot(i):
+            nv.nvfp4_linear(x, codes_h, scales_h, g_h, packed.desc, y_h, lin_ws_h, M=M, ld_x=K, in_dtype=in_dtype,
+                            ld_y=N)
+
     # the same layer without per-tensor scaling (the nGPT recipe): g given as 1, no amax pass
     codes1, scales1, g1 = nv.empty_quantized(M, K, dev)
     g1.fill_(1.0)
@@ -326,6 +337,8 @@ def main():
     t_gemm = timed(gemm_only, k_steps, min(warmup, k_steps)) / k_steps
     t_quant = timed(quant_only, k_steps, min(warmup, k_steps)) / k_steps
     t_given = timed(step_given, k_steps, min(warmup, k_steps)) / k_steps if extra else None
+    t_hot = timed(step_hot, k_steps, min(warmup, k_steps)) / k_steps if step_hot else None
+    clock = observed_gfx_clock(make_runner(step, rot)) if extra else None
     t_gated = timed(step_gated, k_steps, min(warmup, k_steps)) / k_steps if gate_p is not None else None
     t_bf16 = timed(step_bf16, k_steps, min(warmup, k_steps)) / k_steps if extra else None
     t_rht = timed(step_rht, k_steps, min(warmup, k_steps)) / k_steps if rht_on else None
@@ -485,6 +498,8 @@ def main():
                                                                      (4 if N % 256 else 3)),
                               "quantize alone": t_quant * 1e6, "gemm alone": t_gemm * 1e6,
                               "step with g given (no amax pass)": t_given * 1e6 if t_given else None,
+                              "hot-cache step (one weight copy, resident in the Infinity Cache)":
+                                  t_hot * 1e6 if t_hot else None,
                               "tflops with g given": flops / t_given / 1e12 if t_given else None,
                               "step with GDN gates fused": t_gated * 1e6 if t_gated else None,
                               "step with bf16 Y" + (" and GDN gates" if gate_p is not None else ""):
@@ -508,6 +523,7 @@ def main():
                               "quantize_t GB/s (read x once, write codes and scales)":
                                   (x_in_bytes + x_q_bytes) / t_qt / 1e9 if t_qt else None},
         "step_gbs": (x_in_bytes + w_bytes + x_q_bytes + M * N * 4) / t_step / 1e9,
+        "shader_clock_mhz_right_after_step": clock,
         "parity": {"codes_scales_bit_exact": codes_ok, "gemm_within_1e-5": bool(y_ok), "worst_ratio": worst,
                    "g_given_codes_scales_bit_exact": given_ok,
                    "gdn_gates_within_bound": gated_ok, "gdn_gates_worst_ratio": gated_worst,
@@ -515,6 +531,32 @@ def main():
                    "rows_checked": int(len(rows)), "cols_checked": int(len(cols))},
     }
     print(json.dumps(out), flush=True)
+
+
+def observed_gfx_clock(run, cycles=200_000, rounds=20):
+    """The shader clock right after the step has run: after each of `rounds` replays of `run`, a
+    one-wave spin of `cycles` shader-clock cycles (torch.cuda._sleep, which counts the core clock)
+    is timed with events on the same stream; its cycles over its time is the clock, in MHz, before
+    the power management can react to the lighter load.  Untimed, after the timed region."""
+    import torch
+    if not hasattr(torch.cuda, "_sleep"):
+        return {"error": "torch.cuda._sleep not available"}
+    cur = torch.cuda.current_stream()
+    mhz = []
+    for _ in range(rounds):
+        run()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(cur)
+        torch.cuda._sleep(cycles)
+        e1.record(cur)
+        e1.synchronize()
+        ms = e0.elapsed_time(e1)
+        if ms > 0:
+            mhz.append(cycles / (ms * 1e3))
+    if not mhz:
+        return {"error": "no timing"}
+    mhz.sort()
+    return {"median": mhz[len(mhz) // 2], "min": mhz[0], "max": mhz[-1], "spins": len(mhz), "cycles": cycles}
 
 
 def cpu_baseline(wl, ref, budget_s=12.0):
