@@ -62,9 +62,13 @@ struct TileGeom {
     static constexpr int A_CODES = RB * 2 * 1024;
     static constexpr int B_CODES = CB * 2 * 1024;
     static constexpr int A_SC = RB * 256, B_SC = CB * 256;
-    static constexpr int STAGE = A_CODES + B_CODES + A_SC + B_SC;
+    // scale slabs (256 B each) per wavefront, rounded up: with fewer than four
+    // row or column blocks some wavefronts load into a spare slab instead
+    static constexpr int SPARE = (RB % 4 != 0 || CB % 4 != 0) ? 256 : 0;
+    static constexpr int STAGE = A_CODES + B_CODES + A_SC + B_SC + SPARE;
     static constexpr int A_CHUNKS = A_CODES / 16 / 256, B_CHUNKS = B_CODES / 16 / 256;   // per thread
-    static constexpr int AS_WORDS = A_SC / 4 / 256, BS_WORDS = B_SC / 4 / 256;
+    static constexpr int AS_WORDS = (RB + 3) / 4, BS_WORDS = (CB + 3) / 4;
+    static_assert(A_CHUNKS * 16 * 256 == A_CODES && B_CHUNKS * 16 * 256 == B_CODES, "whole code slabs per wave");
 };
 
 struct TileSrc {
@@ -113,16 +117,19 @@ __device__ __forceinline__ void dma_one(uint8_t* stage, const TileSrc& s, uint32
         return;
     }
     idx -= G::B_CHUNKS;
+    uint8_t* const spare = stage + G::A_CODES + G::B_CODES + G::A_SC + G::B_SC;
     if (idx < G::AS_WORDS) {
         const int slab = wave + 4 * idx;
-        dma4(s.as, stage + G::A_CODES + G::B_CODES + slab * 256, s.as_lane,
-             live ? s.as_tile + slab * s.as_blk + ks * 8 : kDeadOffset);
+        const bool own = slab < G::RB;   // (wave-uniform)
+        dma4(s.as, own ? stage + G::A_CODES + G::B_CODES + slab * 256 : spare, s.as_lane,
+             live && own ? s.as_tile + slab * s.as_blk + ks * 8 : kDeadOffset);
         return;
     }
     idx -= G::AS_WORDS;
     const int slab = wave + 4 * idx;
-    dma4(s.bs, stage + G::A_CODES + G::B_CODES + G::A_SC + slab * 256, s.bs_lane,
-         live ? s.bs_tile + slab * s.bs_blk + ks * 128 : kDeadOffset);
+    const bool own = slab < G::CB;
+    dma4(s.bs, own ? stage + G::A_CODES + G::B_CODES + G::A_SC + slab * 256 : spare, s.bs_lane,
+         live && own ? s.bs_tile + slab * s.bs_blk + ks * 128 : kDeadOffset);
 }
 template <int TM, int TN>
 __device__ __forceinline__ void stage_dma(uint8_t* stage, const TileSrc& s, uint32_t ks, bool live, int wave) {
@@ -274,9 +281,12 @@ __device__ __forceinline__ void kstep(float16v (&acc)[TM][TN], Frags<TM, TN> (&f
             const int i = m / TN, j = m % TN;
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(d[q & 1].a[i], d[q & 1].b[j], acc[i][j], 0, 0, 0);
             if (q * kMma + m < kLoads) dma_one<TM, TN>(dma_stage, src, dma_ks, dma_live, wave, q * kMma + m);
-            if (q == 5 && m < kOps) {
-                if (m < TM) nsc.a[m] = split_scales(raw.a[m]);
-                else nsc.b[m - TM] = split_scales(raw.b[m - TM]);
+            if (q == 5) {
+#pragma unroll
+                for (int o = m; o < kOps; o += kMma) {
+                    if (o < TM) nsc.a[o] = split_scales(raw.a[o]);
+                    else nsc.b[o - TM] = split_scales(raw.b[o - TM]);
+                }
             }
 #pragma unroll
             for (int k = m * kPieces / kMma; k < (m + 1) * kPieces / kMma; ++k)
@@ -540,7 +550,8 @@ static hipError_t launch_tiles(int64_t M, const uint8_t* a_codes, const uint8_t*
     // gates only where a gate column falls inside this launch
     const bool gated = (gp.n_a > 0 && 0 < gp.a_col + gp.n_a && gp.a_col < n) ||
                        (gp.n_b > 0 && 0 < gp.b_col + gp.n_b && gp.b_col < n);
-    const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)(n_pad / BN);
+    // tiles up to the last real column (the padding columns past it are never stored)
+    const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((n + BN - 1) / BN);
     const int epi = (gated ? kEpiGates : 0) | (gp.out_bf16 ? kEpiBf16 : 0);
     auto kern = epi == 0 ? gemm_tile_kernel<TM, TN, 0>
               : epi == kEpiGates ? gemm_tile_kernel<TM, TN, kEpiGates>
@@ -564,6 +575,11 @@ hipError_t launch_gemm(int64_t M, const uint8_t* a_codes, const uint8_t* a_scale
         const hipError_t e = launch_tiles<4, 4>(M, a_codes, a_scales, g_x, d, 0, split, y, ld_y, gp, stream);
         if (e != hipSuccess || split == d.n_padded) return e;
     }
+    // a narrow remainder (the ragged column edge of a fused projection) that 128 x 128 tiles would spread
+    // over few compute units goes on 64 x 64 tiles: four times the workgroups, each a quarter of the work
+    const int64_t rest_cols = (d.n < d.n_padded ? d.n : d.n_padded) - split;
+    if (split > 0 && ((M + 127) / 128) * ((rest_cols + 127) / 128) < kComputeUnits)
+        return launch_tiles<1, 1>(M, a_codes, a_scales, g_x, d, split, d.n_padded, y, ld_y, gp, stream);
     return launch_tiles<2, 2>(M, a_codes, a_scales, g_x, d, split, d.n_padded, y, ld_y, gp, stream);
 }
 
