@@ -575,10 +575,15 @@ hipError_t launch_gemm(int64_t M, const uint8_t* a_codes, const uint8_t* a_scale
         const hipError_t e = launch_tiles<4, 4>(M, a_codes, a_scales, g_x, d, 0, split, y, ld_y, gp, stream);
         if (e != hipSuccess || split == d.n_padded) return e;
     }
-    // a narrow remainder (the ragged column edge of a fused projection) that 128 x 128 tiles would spread
-    // over few compute units goes on 64 x 64 tiles: four times the workgroups, each a quarter of the work
+    // 64 x 64 tiles (four times the workgroups, each a quarter of the work) where 128 x 128 tiles would
+    // leave units idle: a few hundred tokens, or the ragged column edge of a fused projection after the
+    // large tiles.  Taken when the narrow tiles fit one per unit, or when the small ones would leave more
+    // than half of the units idle (measured, N = K = 5120: 32-192 tokens 36-38 -> 22-25 us, 256 tokens
+    // 38.9 -> 35.1 us, 512 tokens 42.9 -> 51.3 us, so 512 stays on 128 x 128)
     const int64_t rest_cols = (d.n < d.n_padded ? d.n : d.n_padded) - split;
-    if (split > 0 && ((M + 127) / 128) * ((rest_cols + 127) / 128) < kComputeUnits)
+    const int64_t small_tiles = ((M + 127) / 128) * ((rest_cols + 127) / 128);
+    const int64_t narrow_tiles = ((M + 63) / 64) * ((rest_cols + 63) / 64);
+    if (narrow_tiles <= kComputeUnits || 2 * small_tiles < kComputeUnits)
         return launch_tiles<1, 1>(M, a_codes, a_scales, g_x, d, split, d.n_padded, y, ld_y, gp, stream);
     return launch_tiles<2, 2>(M, a_codes, a_scales, g_x, d, split, d.n_padded, y, ld_y, gp, stream);
 }

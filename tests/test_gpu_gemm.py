@@ -183,17 +183,33 @@ def test_tile_shape_does_not_change_results():
     assert torch.equal(y_all[:256], y_top)
 
 
-def test_mixed_tile_split():
-    """A ragged column edge (16384 + 96 columns, as the fused GDN projection's gate modules leave) at 1024
-    tokens runs its first 16384 columns on 256 x 256 tiles and the last 96 on 128 x 128 tiles in a second
-    launch: every output within the oracle's bound, and bit for bit what 128 x 128 tiles alone give."""
-    x = workloads.random_matrix(1301, 1024, 512, dtype="bf16")
+@pytest.mark.parametrize("M", [1024, 1000])
+def test_mixed_tile_split(M):
+    """A ragged column edge (16384 + 96 columns, as the fused GDN projection's gate modules leave) at about
+    a thousand tokens runs its first 16384 columns on 256 x 256 tiles and the last 96 in a second launch on
+    64 x 64 tiles (128 x 128 tiles would occupy only 8 units); 1000 rows also leave ragged row tiles in
+    both launches: every output within the oracle's bound, and bit for bit what 128 x 128 tiles alone give."""
+    x = workloads.random_matrix(1301, M, 512, dtype="bf16")
     ws = [workloads.random_matrix(1302, 16384, 512, 0.05, dtype="bf16"),
           workloads.random_matrix(1303, 96, 512, 2.0, dtype="bf16")]
     y = check_dense(x, "bf16", ws, "bf16", "mixed tiles")
     xc, xs, gx = nv.quantize(to_dev(x, "bf16"))
     pw = nv.PackedWeight([nv.quantize(to_dev(w, "bf16")) for w in ws], 512)
     y_top = nv.gemm(xc[:128].contiguous(), xs[:128].contiguous(), gx, pw)     # 128 rows: small tiles only
+    torch.cuda.synchronize()
+    assert torch.equal(y[:128], y_top)
+
+
+def test_small_tile_shapes_agree():
+    """1024 tokens x 4096 columns run on 128 x 128 tiles (256 of them, one round at two per unit); the
+    first 128 rows alone make only 32 such tiles and run on 64 x 64 tiles instead: the same sums, bit for
+    bit, and every output within the oracle's bound."""
+    x = workloads.random_matrix(1311, 1024, 512, dtype="bf16")
+    ws = [workloads.random_matrix(1312, 4096, 512, 0.05, dtype="bf16")]
+    y = check_dense(x, "bf16", ws, "bf16", "128x128 tiles")
+    xc, xs, gx = nv.quantize(to_dev(x, "bf16"))
+    pw = nv.PackedWeight([nv.quantize(to_dev(w, "bf16")) for w in ws], 512)
+    y_top = nv.gemm(xc[:128].contiguous(), xs[:128].contiguous(), gx, pw)
     torch.cuda.synchronize()
     assert torch.equal(y[:128], y_top)
 
