@@ -299,12 +299,12 @@ __device__ __forceinline__ void kstep(float16v (&acc)[TM][TN], Frags<TM, TN> (&f
 
 // ---------------------------------------------------------------------------
 // Work split: one workgroup per output tile, 256 x 256 (one workgroup per
-// compute unit: 147 KB of LDS, all 512 registers of each SIMD) or 128 x 128
-// (two per compute unit).  The host picks the shape that finishes first,
-// counting rounds of workgroups over the compute units: small products get
-// the small tiles, so that more compute units have work.  Every output element
-// sums its k-steps in the same order with either shape, so the choice never
-// changes a result.
+// compute unit: 147 KB of LDS, all 512 registers of each SIMD), 128 x 128
+// (two per compute unit) or 64 x 64 (four per compute unit).  The host picks
+// the shape that finishes first, counting rounds of workgroups over the
+// compute units: small products get the small tiles, so that more compute
+// units have work.  Every output element sums its k-steps in the same order
+// with any shape, so the choice never changes a result.
 // ---------------------------------------------------------------------------
 // logical workgroup id: the workgroups of one XCD (hardware ids go round-robin
 // over the XCDs) get consecutive logical ids
