@@ -87,7 +87,7 @@ def log(msg):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (collectives are not part of it); "
+        print("bench.py measures one GPU: the library has no multi-GPU path (no collectives); "
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
