@@ -417,26 +417,37 @@ __device__ __forceinline__ void store_tile_cols(const float16v (&acc)[TM][TN], i
     const int l32 = lane & 31, h = lane >> 5;
     const float gx = g_x[0];
     const int64_t n0 = (int64_t)tn * G::BN + wn * (TN * 32) + l32;
+    // per column block: its scale (and gate parameters); the stores then walk the rows with the column
+    // blocks innermost, so the pieces of one output row's line are written back to back
+    float cs[TN];
+    GateCol gc[TN];
+    bool live[TN];
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
         const int64_t n = n0 + j * 32;
-        if (n >= N) continue;
-        const float cs = gx * colscale[n];
-        GateCol gc{0, 0.0f, 0.0f};
-        if constexpr (GATED) gc = gate_col(n, gp);
+        live[j] = n < N;
+        cs[j] = live[j] ? gx * colscale[n] : 0.0f;
+        gc[j] = GateCol{0, 0.0f, 0.0f};
+        if constexpr (GATED) {
+            if (live[j]) gc[j] = gate_col(n, gp);
+        }
+    }
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
+    for (int i = 0; i < TM; ++i) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t m = (int64_t)tm * G::BM + wm * (TM * 32) + i * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
-                if (m < M) {
-                    float v = acc[i][j][r] * cs;
-                    if constexpr (GATED) v = gate_apply(v, gc);
-                    if constexpr (BF16)
-                        reinterpret_cast<uint16_t*>(y)[m * ld_y + n] = f32_to_bf16_rne(v);
-                    else
-                        y[m * ld_y + n] = v;
-                }
+        for (int r = 0; r < 16; ++r) {
+            const int64_t m = (int64_t)tm * G::BM + wm * (TM * 32) + i * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
+            if (m >= M) continue;
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                if (!live[j]) continue;
+                const int64_t n = n0 + j * 32;
+                float v = acc[i][j][r] * cs[j];
+                if constexpr (GATED) v = gate_apply(v, gc[j]);
+                if constexpr (BF16)
+                    reinterpret_cast<uint16_t*>(y)[m * ld_y + n] = f32_to_bf16_rne(v);
+                else
+                    y[m * ld_y + n] = v;
             }
         }
     }
