@@ -204,8 +204,9 @@ nvfp4_status nvfp4_quantize_t_rht(const void* x, int in_dtype, int64_t rows, int
 /* ---------------------------------------------------------------------------
  * FP8 KV cache: E4M3 bytes with one calibrated FP32 scale per tensor.
  *
- * The Gated DeltaNet page's summary credits calibrated FP8 scales on the KV
- * cache with recovering most of the long-context loss.  Per tensor (a layer's
+ * The Gated DeltaNet page ("Why Gated DeltaNet Survives 4-Bit Quantization",
+ * section "Critical Lessons for Model Serving") credits calibrated FP8 scales
+ * on the KV cache with recovering most of the long-context loss.  Per tensor (a layer's
  * K or V cache, [rows][cols] = [tokens][heads * head_dim]): s given (a
  * calibrated value, s_mode NVFP4_G_GIVEN) or calibrated on the tensor itself
  * (NVFP4_G_COMPUTE: s = fl32(amax / 448), 1 for an all-zero tensor, floored at
@@ -324,6 +325,15 @@ nvfp4_status nvfp4_unpack_weights(const nvfp4_weight_desc* w, uint8_t* codes, ui
 /* ---------------------------------------------------------------------------
  * Block-scaled GEMM: Y[m][n] = sum_k xhat[m][k] * what[n][k], FP32 out.
  *
+ * The product every linear layer runs with both operands in NVFP4 ("Why
+ * Gated DeltaNet Survives 4-Bit Quantization", section "Performance and
+ * Efficiency Gains": weights and activations in NVFP4 on all 496 linear
+ * layers), the dot products of "Normalized Architectures are Natively 4-Bit"
+ * (section "Approach"); blocks of 16 along K carry their own scales (the
+ * Gated DeltaNet page, section "Why the 'Fragile' Recurrence is Actually
+ * Robust") and a fused projection keeps each module's global scale (its
+ * section "Critical Lessons for Model Serving").
+ *
  * xhat = e2m1(a_code) * e4m3(a_scale) * g_x, what = e2m1(w_code) * e4m3(w_scale)
  * * g_w[module(n)].  The products of decoded codes and block scales are exact in
  * FP16 and are multiplied and summed on the matrix cores in FP32; the two
@@ -381,10 +391,10 @@ nvfp4_status nvfp4_linear(const void* x, int in_dtype, int64_t M, int64_t ld_x, 
                           int64_t ld_y, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
- * Gate epilogue of a fused Gated DeltaNet input projection ("Why Gated
- * DeltaNet Survives 4-Bit Quantization", section "The gates are shielded by
- * their parameterization": the state decay is exp(-exp(A) * softplus(a + b))
- * and the write strength a sigmoid).  The two small gate projections sit in
+ * Gate epilogue of a fused Gated DeltaNet input projection (anthology-of-the-
+ * sota record theory-128, Kozyrev and Maiboroda 2026, section "The account",
+ * its paragraph on the gates' parameterization: the state decay is
+ * exp(-exp(A) * softplus(a + b)) and the write strength a sigmoid).  The two small gate projections sit in
  * the same fused weight as q, k, v, z; the epilogue turns their output columns
  * into the gates as Y is written, so no second pass over Y is needed:
  *
@@ -418,8 +428,9 @@ nvfp4_status nvfp4_linear_gated(const void* x, int in_dtype, int64_t M, int64_t 
 
 /* ---------------------------------------------------------------------------
  * Product with an output epilogue: the output type and, optionally, the GDN
- * gates (section "The gates are shielded by their parameterization" of the
- * Gated DeltaNet page; the projection's output feeds the recurrence).
+ * gates (anthology-of-the-sota record theory-128, section "The account", the
+ * paragraph on the gates' parameterization; the projection's output feeds
+ * the recurrence).
  *
  * y_dtype : NVFP4_OUT_F32 or NVFP4_OUT_BF16 (else NVFP4_ERR_INVALID_ARG)
  * reserved: must be 0

@@ -184,6 +184,32 @@ def _stream(stream):
     return stream.cuda_stream
 
 
+def _on_stream(stream):
+    """Context for the conveniences below when the caller names a stream: the stream first waits for the
+    current stream (whose work produced the inputs), and every allocation and fill inside runs on it, so
+    temporaries (workspaces, g) are ordered with the launches that use them and are only reused by the
+    caching allocator after that stream's work.  No stream: the current one, nothing to do."""
+    import contextlib
+    if stream is None:
+        return contextlib.nullcontext()
+    s = torch.cuda.ExternalStream(stream) if isinstance(stream, int) else stream
+    s.wait_stream(torch.cuda.current_stream())
+    return torch.cuda.stream(s)
+
+
+def _stream_ordered(fn):
+    """Runs a convenience under _on_stream of its ``stream`` argument."""
+    import functools
+    import inspect
+    sig = inspect.signature(fn)
+
+    @functools.wraps(fn)
+    def wrapper(*args, **kwargs):
+        with _on_stream(sig.bind(*args, **kwargs).arguments.get("stream")):
+            return fn(*args, **kwargs)
+    return wrapper
+
+
 def last_error() -> str:
     return _lib.nvfp4_last_error().decode(errors="replace")
 
@@ -374,6 +400,7 @@ def empty_quantized(rows: int, K: int, device="cuda"):
     return codes, scales, g
 
 
+@_stream_ordered
 def quantize(x: torch.Tensor, g=None, stream=None):
     """NVFP4-quantize x [rows, K]; g=None computes the global scale, otherwise uses the given value."""
     rows, K = x.shape
@@ -390,6 +417,7 @@ def quantize(x: torch.Tensor, g=None, stream=None):
     return codes, scales, gt
 
 
+@_stream_ordered
 def quantize_t(x: torch.Tensor, g=None, stream=None):
     """NVFP4 encoding of x^T for x [rows, cols]: codes [cols, rows/2], scales [cols, rows/16] and g
     (computed from x's amax when g is None, otherwise the given value)."""
@@ -421,16 +449,19 @@ def _quantize_with(fn, x, signs, out_rows, out_k, g, stream):
     return codes, scales, gt
 
 
+@_stream_ordered
 def quantize_rht(x: torch.Tensor, signs: int, g=None, stream=None):
     """NVFP4 codes, scales and g of the randomized Hadamard transform of x [rows, K]."""
     return _quantize_with(nvfp4_quantize_rht, x, signs, x.shape[0], x.shape[1], g, stream)
 
 
+@_stream_ordered
 def quantize_t_rht(x: torch.Tensor, signs: int, g=None, stream=None):
     """The same for x^T: codes [cols, rows/2], scales [cols, rows/16]."""
     return _quantize_with(nvfp4_quantize_t_rht, x, signs, x.shape[1], x.shape[0], g, stream)
 
 
+@_stream_ordered
 def quantize_both(x: torch.Tensor, g=None, stream=None):
     """((codes, scales, g), (codes_t, scales_t, g)) of x [rows, cols]: the encodings of x and of x^T, sharing
     one g tensor."""
@@ -449,6 +480,7 @@ def quantize_both(x: torch.Tensor, g=None, stream=None):
     return (codes, scales, gt), (codes_t, scales_t, gt)
 
 
+@_stream_ordered
 def kv_quantize_fp8(x: torch.Tensor, scale=None, stream=None):
     """(codes uint8 [rows, cols], scale [1]) of x in FP8 E4M3; scale=None calibrates on x."""
     rows, cols = x.shape
@@ -469,6 +501,7 @@ def kv_quantize_fp8(x: torch.Tensor, scale=None, stream=None):
 class PackedWeight:
     """A packed (possibly fused multi-module) weight: the device blob plus its descriptor."""
 
+    @_stream_ordered
     def __init__(self, modules, K: int, stream=None):
         rows = [int(m[0].shape[0]) for m in modules]
         nbytes = nvfp4_packed_weight_bytes(rows, K)
@@ -493,6 +526,7 @@ class PackedWeight:
         other.module_rows, other.K = self.module_rows, self.K
         return other
 
+    @_stream_ordered
     def unpack(self, stream=None):
         n, K = self.n, self.K
         codes = torch.empty((n, K // 2), dtype=torch.uint8, device=self.blob.device)
@@ -502,6 +536,7 @@ class PackedWeight:
         return codes, scales, colscale
 
 
+@_stream_ordered
 def pack_weights_train(w: torch.Tensor, g=None, stream=None):
     """(forward PackedWeight of w along k, backward PackedWeight of w^T along n, g) for a training weight
     w [n, k], from one read of w (g computed when None)."""
@@ -527,6 +562,7 @@ def linear_workspace(M: int, x_dtype, w: "PackedWeight", device="cuda") -> torch
     return torch.zeros((nvfp4_linear_workspace_bytes(M, in_dtype, w.desc),), dtype=torch.uint8, device=device)
 
 
+@_stream_ordered
 def linear(x: torch.Tensor, w: "PackedWeight", workspace=None, g=None, stream=None, gates=None,
            out_dtype=torch.float32):
     """Y = NVFP4(x) . W^T in one call (through the GDN gate epilogue when gates are given; Y in float32 or
@@ -543,6 +579,7 @@ def linear(x: torch.Tensor, w: "PackedWeight", workspace=None, g=None, stream=No
     return y, codes, scales, gt
 
 
+@_stream_ordered
 def gemm(a_codes, a_scales, g_x, w: PackedWeight, y=None, stream=None, gates=None, out_dtype=torch.float32):
     M = a_codes.shape[0]
     if y is None:

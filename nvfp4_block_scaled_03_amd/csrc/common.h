@@ -299,9 +299,9 @@ hipError_t launch_pack(const nvfp4_weight_desc& d, const uint8_t* const* codes,
 hipError_t launch_unpack(const nvfp4_weight_desc& d, uint8_t* codes, uint8_t* scales, float* colscale,
                          hipStream_t stream);
 
-// Gate epilogue of a fused Gated DeltaNet projection ("Why Gated DeltaNet
-// Survives 4-Bit Quantization", section "The gates are shielded by their
-// parameterization"): output columns [a_col, a_col + n_a) become the state
+// Gate epilogue of a fused Gated DeltaNet projection (anthology-of-the-sota
+// record theory-128, Kozyrev and Maiboroda 2026, section "The account", the
+// paragraph on the gates' parameterization): output columns [a_col, a_col + n_a) become the state
 // decay exp(-exp(A) * softplus(y + bias)) of their head, columns
 // [b_col, b_col + n_b) the write strength sigmoid(y).  The kernels take it as a
 // compile-time option, so products without gates carry none of it.

@@ -4,10 +4,9 @@ TEST INFRASTRUCTURE ONLY.  Like ``nvfp4_ref``, only ``tests/``, ``__graft_entry_
 and the ``cpu_baseline`` leg of ``bench.py`` may import this module; the product path never
 does, and this module imports nothing from the product package.
 
-What it follows: "Why Gated DeltaNet Survives 4-Bit Quantization: NVFP4 W4A4 for the
-Recurrent Half of a Hybrid 27B LLM", section "The gates are shielded by their
-parameterization": the state decay is exp(-exp(A) * softplus(a + b)) and the write
-strength is a sigmoid.  The a and b of that section are the outputs of two small
+What it follows: the anthology-of-the-sota record theory-128 (Kozyrev and Maiboroda,
+2026), section "The account", its paragraph on how the gates are parameterized: the
+state decay is exp(-exp(A) * softplus(a + b)) and the write strength is a sigmoid.  The a and b of that section are the outputs of two small
 projections that sit in the same fused input projection as q, k, v and z (section
 "Critical Lessons for Model Serving": fused modules, each with its own global scale).
 

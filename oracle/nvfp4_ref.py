@@ -271,10 +271,6 @@ def dequantize(qt: Quantized) -> np.ndarray:
     return (vals * sc).reshape(rows, K) * np.float64(qt.g)
 
 
-def dequantize_parts(codes, scales, g) -> np.ndarray:
-    return dequantize(Quantized(np.asarray(codes, np.uint8), np.asarray(scales, np.uint8), g))
-
-
 # ---------------------------------------------------------------------------
 # GEMM
 # ---------------------------------------------------------------------------
@@ -304,13 +300,6 @@ def gemm(xq: Quantized, w_modules: list[Quantized]) -> tuple[np.ndarray, np.ndar
 def gemm_dequantized(xh: np.ndarray, wh: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     """Same as ``gemm`` on already dequantized FP64 operands [M,K] and [N,K]."""
     return xh @ wh.T, np.abs(xh) @ np.abs(wh).T
-
-
-def gemm_entries(xh: np.ndarray, wh: np.ndarray, rows: np.ndarray, cols: np.ndarray):
-    """Selected entries Y[rows[i], cols[i]] (and their |term| sums) by direct FP64 dot products."""
-    xr = xh[rows]
-    wc = wh[cols]
-    return np.einsum("ik,ik->i", xr, wc), np.einsum("ik,ik->i", np.abs(xr), np.abs(wc))
 
 
 #: Tolerance of a GEMM output against the FP64 oracle, relative to the sum of

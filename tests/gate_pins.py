@@ -86,4 +86,16 @@ def check_tolerance(g):
     assert np.all(tight[:, 4:12] <= 1e-5 * (1.0 + np.abs(out[:, 4:12]) * 60.0) + 1e-30)
 
 
-ALL_CHECKS = [check_softplus, check_sigmoid, check_decay, check_apply_gates, check_tolerance]
+def check_within(g):
+    """The comparison the GPU gate tests call: inside the bound passes, beyond it fails, and the worst
+    ratio is |diff| / tol (dyadic values, so every difference is exact)."""
+    e = 2.0 ** -20
+    ref_out = np.array([[0.5, 0.25, 1.0]])
+    tol = np.array([[e, 2 * e, 4 * e]])
+    ok, worst = g.within(ref_out + [[e, -e, 0.0]], ref_out, tol)
+    assert ok and worst == 1.0
+    assert not g.within(ref_out + [[0.0, 0.0, 8 * e]], ref_out, tol)[0]
+    ok, worst = g.within(ref_out, ref_out, tol)
+    assert ok and worst == 0.0
+
+ALL_CHECKS = [check_softplus, check_sigmoid, check_decay, check_apply_gates, check_tolerance, check_within]

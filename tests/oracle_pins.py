@@ -375,6 +375,25 @@ def check_gemm_bruteforce(ref):
             assert abs(a[m, n] - float(absum)) <= 1e-13 * float(absum)
 
 
+def check_gemm_dequantized_bruteforce(ref):
+    """The product on already dequantized operands (what the full-size parity checks call) against the exact
+    rational triple loop, on non-square operands with mixed signs and module scales."""
+    rng = np.random.default_rng(25)
+    x = (rng.standard_normal((5, 64)) * np.exp(rng.uniform(-2, 2, (5, 64)))).astype(F32)
+    w = (rng.standard_normal((3, 64)) * 0.05).astype(F32)
+    xq, wq = ref.quantize(x), ref.quantize(w)
+    y, a = ref.gemm_dequantized(ref.dequantize(xq), ref.dequantize(wq))
+    assert y.shape == (5, 3) and a.shape == (5, 3)
+    X = _exact_dequant(xq.codes, xq.scales, xq.g)
+    W = _exact_dequant(wq.codes, wq.scales, wq.g)
+    for m in range(5):
+        for n in range(3):
+            exact = sum(X[m][k] * W[n][k] for k in range(64))
+            absum = sum(abs(X[m][k] * W[n][k]) for k in range(64))
+            assert abs(y[m, n] - float(exact)) <= 1e-13 * float(absum) + 1e-300, (m, n)
+            assert abs(a[m, n] - float(absum)) <= 1e-13 * float(absum), (m, n)
+
+
 def check_gemm_constant(ref):
     """Constant operands: every block is full-range (code 6, scale 448), so Y = K * x^ * w^.
 
@@ -516,7 +535,7 @@ ALL_CHECKS = [
     check_e2m1_thresholds, check_global_scale, check_golden_given, check_golden_computed, check_golden_op_order, check_amax_block,
     check_outlier_locality, check_dynamic_g_outlier, check_pow2_equivariance, check_permutation,
     check_negation, check_zero_block, check_dequant_error_bound, check_byte_counts,
-    check_gemm_bruteforce, check_gemm_constant, check_gemm_onehot, check_gemm_identity,
+    check_gemm_bruteforce, check_gemm_dequantized_bruteforce, check_gemm_constant, check_gemm_onehot, check_gemm_identity,
     check_fused_concat, check_fused_pitfall, check_tolerance_fn,
     check_transpose_columns, check_transpose_exact, check_backward_products,
 ]

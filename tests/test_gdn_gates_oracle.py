@@ -71,8 +71,16 @@ def m_tolerance_no_derivative(o):
     o.gates_tolerance = tol
 
 
+def m_within_relative(o):
+    def within(out_gpu, out_ref, tol):
+        err = np.abs(np.asarray(out_gpu, np.float64) - out_ref) / np.maximum(np.abs(out_ref), 1e-300)
+        worst = float(err.max()) if err.size else 0.0
+        return bool(worst <= 1e-5), worst
+    o.within = within
+
+
 MUTANTS = [m_softplus_no_log, m_softplus_unshifted, m_sigmoid_sign, m_decay_no_exp_A, m_decay_no_bias, m_decay_sign,
-           m_gates_off_by_one, m_gates_swapped, m_tolerance_no_derivative]
+           m_gates_off_by_one, m_gates_swapped, m_tolerance_no_derivative, m_within_relative]
 
 
 @pytest.mark.parametrize("mutate", MUTANTS, ids=lambda m: m.__name__)

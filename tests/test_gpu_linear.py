@@ -138,3 +138,29 @@ def test_amax_fallback_when_peers_do_not_publish(shape, monkeypatch):
         x = workloads.random_matrix(1301, 3, 2048, dtype="bf16")
         w = workloads.random_matrix(1302, 300, 2048, 0.05, dtype="bf16")
         _check(x, "bf16", [w], "bf16", "3x2048x300, amax fallback", calls=2)
+
+
+@pytest.mark.parametrize("M", [4, 16, 64])
+def test_side_stream(M):
+    """The conveniences on a stream other than the current one: the workspace and g are allocated and
+    filled on that stream, after the current stream's work, so the results equal the same calls on the
+    current stream (few tokens: the one-kernel path with its zero-filled workspace)."""
+    say(f"linear/gemm on a side stream: M={M} K=1024 N=320")
+    x = workloads.random_matrix(1200 + M, M, 1024, dtype="bf16")
+    w = workloads.random_matrix(1300 + M, 320, 1024, 0.05, dtype="bf16")
+    xd = to_dev(x, "bf16")
+    pw = nv.PackedWeight([nv.quantize(to_dev(w, "bf16"))], 1024)
+    y0, c0, s0, g0 = nv.linear(xd, pw)
+    y0g = nv.gemm(c0, s0, g0, pw)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    for _ in range(3):
+        y1, c1, s1, g1 = nv.linear(xd, pw, stream=side)
+        y1g = nv.gemm(c1, s1, g1, pw, stream=side)
+        y1h, _, _, _ = nv.linear(xd, pw, g=1.0, stream=side.cuda_stream)   # raw handle, given g
+        side.synchronize()
+        assert torch.equal(c1, c0) and torch.equal(s1, s0) and torch.equal(g1, g0)
+        assert torch.equal(y1, y0) and torch.equal(y1g, y0g)
+    y2, _, _, _ = nv.linear(xd, pw, g=1.0)
+    torch.cuda.synchronize()
+    assert torch.equal(y1h, y2)

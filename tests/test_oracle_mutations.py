@@ -145,6 +145,14 @@ def m_gemm_transposed(o):
     o.gemm = gemm
 
 
+def m_gemm_dequantized_no_abs(o):
+    o.gemm_dequantized = lambda xh, wh: (xh @ wh.T, np.abs(xh @ wh.T))
+
+
+def m_gemm_dequantized_transposed(o):
+    o.gemm_dequantized = lambda xh, wh: ((wh @ xh.T).T[:, ::-1].copy(), (np.abs(wh) @ np.abs(xh).T).T[:, ::-1].copy())
+
+
 def m_block_32(o):
     orig_q = o.quantize
     def quantize(x, g_mode="compute", g=None):
@@ -217,7 +225,8 @@ def m_t_no_transpose_layout(o):
 MUTANTS = [m_ties_away, m_ties_down, m_e2m1_truncate, m_no_sign, m_zero_drops_sign, m_no_sat, m_no_div6,
            m_div6_before_mul, m_recip_inverted, m_recip_no_zero_rule, m_nibble_swap, m_range_448, m_range_6,
            m_no_zero_tensor_rule, m_dequant_no_g, m_dequant_scale_shift, m_gemm_modules_reversed,
-           m_gemm_shared_scale, m_gemm_transposed, m_block_32, m_amax_per_row, m_e4m3_bias8, m_tolerance_loose,
+           m_gemm_shared_scale, m_gemm_transposed, m_gemm_dequantized_no_abs,
+           m_gemm_dequantized_transposed, m_block_32, m_amax_per_row, m_e4m3_bias8, m_tolerance_loose,
            m_t_blocks_along_columns, m_t_g_first_column, m_t_no_transpose_layout]
 
 
