@@ -348,14 +348,11 @@ nvfp4_status nvfp4_unpack_weights(const nvfp4_weight_desc* w, uint8_t* codes, ui
  * y        : device, FP32, row m at y + m*ld_y; columns [0, w->n) are written
  * ld_y     : >= w->n
  * workspace: device, >= nvfp4_gemm_workspace_bytes(M, w) bytes, 256-byte aligned
- *            (may be NULL when that is 0).  For few tokens (1 <= M <= 16) the
- *            product is split along K over workgroups: the workspace holds a
- *            ticket counter and a few exchange words per group of weight rows
- *            and one partial tile per workgroup.  It must be ZERO before its
- *            first use, and every call leaves it zero; the last workgroup of a
- *            group to start adds the partials in a fixed order (results do not
- *            depend on scheduling).  Calls that may run concurrently must not
- *            share a workspace.
+ *            (may be NULL when that is 0, which it is for every shape of this
+ *            version: the product keeps no state between workgroups).  For few
+ *            tokens (1 <= M <= 16, K <= 8192) one workgroup takes each 16 rows
+ *            of the weight over all of K and adds its wavefronts' partial sums
+ *            in a fixed order, so results do not depend on scheduling.
  * ------------------------------------------------------------------------- */
 size_t nvfp4_gemm_workspace_bytes(int64_t M, const nvfp4_weight_desc* w);
 nvfp4_status nvfp4_gemm(int64_t M, const uint8_t* a_codes, const uint8_t* a_scales, const float* g_x,
@@ -368,13 +365,15 @@ nvfp4_status nvfp4_gemm(int64_t M, const uint8_t* a_codes, const uint8_t* a_scal
  * "Performance and Efficiency Gains").  Same codes, scales, g and Y bits as
  * nvfp4_quantize followed by nvfp4_gemm on the same stream.
  *
- * For few tokens (1 <= M <= 16) the whole call is one kernel: the workgroups
- * that share a K-slice of the weight stream quantize that slice of the
- * activations next to it, after exchanging per-slice max|x| with the other
- * workgroups of their row group (no second pass over the activations and no
- * extra launch).  The exchange waits a bounded number of polls for each peer
- * and otherwise reduces the missing slices itself, so it never depends on
- * another workgroup being resident; the environment variable
+ * For few tokens (1 <= M <= 16, K <= 8192) the whole call is one kernel.  On
+ * each of the 8 XCDs, 8 encoder workgroups reduce max|x| over the tensor (an
+ * eighth each, exchanged through that XCD's L2) and encode an eighth of the
+ * blocks each; the product workgroups stream and decode their weight
+ * rows meanwhile, wait for their own XCD's encoders and multiply.  Every XCD
+ * writes the same bytes into x_codes and x_scales.  A workgroup that runs on
+ * another XCD than its index is meant for, or whose wait exceeds a bound,
+ * encodes the activations itself (the same bytes), so no result depends on
+ * placement or on another workgroup being resident; the environment variable
  * NVFP4_AMAX_POLLS overrides the bound (0 forces the local path, for tests).
  *
  * x, in_dtype, ld_x     : as for nvfp4_quantize, rows = M, K = w->k (M*K/2 <= 2 GiB)
@@ -382,8 +381,12 @@ nvfp4_status nvfp4_gemm(int64_t M, const uint8_t* a_codes, const uint8_t* a_scal
  *                         input in NVFP4_G_GIVEN mode), as for nvfp4_quantize
  * w, y, ld_y            : as for nvfp4_gemm
  * workspace             : device, >= nvfp4_linear_workspace_bytes(M, in_dtype, w)
- *                         bytes, 256-byte aligned, zero-filled before its first
- *                         use (as the few-token workspace of nvfp4_gemm).
+ *                         bytes (at most 2048 + 4096), 256-byte aligned.  Its
+ *                         first 2048 bytes hold the few-token path's flags
+ *                         (tagged with the launch, so no call needs them reset):
+ *                         zero before the first use; the rest needs no
+ *                         initialisation.  Calls that may run concurrently
+ *                         must not share a workspace.
  * ------------------------------------------------------------------------- */
 size_t nvfp4_linear_workspace_bytes(int64_t M, int in_dtype, const nvfp4_weight_desc* w);
 nvfp4_status nvfp4_linear(const void* x, int in_dtype, int64_t M, int64_t ld_x, uint8_t* x_codes,

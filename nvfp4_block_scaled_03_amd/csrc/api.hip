@@ -456,10 +456,15 @@ nvfp4_status nvfp4_gemm_gated(int64_t M, const uint8_t* a_codes, const uint8_t* 
     return gemm_impl(M, a_codes, a_scales, g_x, w, gp, y, ld_y, workspace, workspace_bytes, stream);
 }
 
+// The counters of the one-launch few-token path come first, reserved for every
+// M, so that the amax partials of the two-launch path (quantize, then the
+// product) never land on them: one workspace may serve calls with any M.
+static size_t linear_counter_bytes(int64_t, const nvfp4_weight_desc&) { return nvfp4::kSkinnyCounterBytes; }
+
 size_t nvfp4_linear_workspace_bytes(int64_t M, int in_dtype, const nvfp4_weight_desc* w) {
     if (w == nullptr || M < 0 || w->k <= 0 || w->n_padded <= 0) return 0;
     (void)in_dtype;
-    return nvfp4::gemm_workspace_bytes(M, *w) + nvfp4_quantize_workspace_bytes(M, w->k);
+    return linear_counter_bytes(M, *w) + nvfp4_quantize_workspace_bytes(M, w->k);
 }
 
 static nvfp4_status linear_impl(const void* x, int in_dtype, int64_t M, int64_t ld_x, uint8_t* x_codes,
@@ -492,9 +497,10 @@ static nvfp4_status linear_impl(const void* x, int in_dtype, int64_t M, int64_t 
             return fail(NVFP4_ERR_UNSUPPORTED, "x_codes must be 16-byte, x_scales 4-byte and y element aligned");
     }
     const size_t need = nvfp4_linear_workspace_bytes(M, in_dtype, w);
-    if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256)))
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256))) {
         return fail(NVFP4_ERR_WORKSPACE, "linear workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
                     workspace_bytes);
+    }
     st = check_device();
     if (st != NVFP4_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -503,15 +509,15 @@ static nvfp4_status linear_impl(const void* x, int in_dtype, int64_t M, int64_t 
     const int64_t esize = in_dtype == NVFP4_IN_BF16 ? 2 : 4;
     const bool skinny = nvfp4::skinny_applies(M, *w);
     const bool fused = skinny && M * ld_x * esize <= INT32_MAX;
-    const size_t gemm_ws = nvfp4::gemm_workspace_bytes(M, *w);   // the product's part comes first
-    float* partials = reinterpret_cast<float*>(wsb + gemm_ws);
+    const size_t counter_bytes = linear_counter_bytes(M, *w);   // the counters come first
+    float* partials = reinterpret_cast<float*>(wsb + counter_bytes);
     const int n_partials = nvfp4::quantize_partials_count(M, K);
     if (M == 0 || !fused) {
         hipError_t e = nvfp4::launch_quantize(x, in_dtype, M, K, ld_x, x_codes, x_scales, g_x, g_mode, partials,
                                               n_partials, s);
         if (e != hipSuccess) return fail(NVFP4_ERR_HIP, "linear quantize launch: %s", hipGetErrorString(e));
         if (M == 0) return ok();
-        return launched(nvfp4::launch_gemm(M, x_codes, x_scales, g_x, *w, y, ld_y, workspace, gemm_ws, gp, s),
+        return launched(nvfp4::launch_gemm(M, x_codes, x_scales, g_x, *w, y, ld_y, nullptr, 0, gp, s),
                         "linear gemm launch");
     }
     return launched(nvfp4::launch_skinny(M, x, in_dtype, ld_x, g_x, g_mode, x_codes, x_scales, true, *w, y, ld_y,

@@ -192,12 +192,13 @@ __device__ __forceinline__ void rht16(float v[16], uint32_t signs) {
 }
 
 // Encode one 16-element block held in v[16], whose max |v| is bamax, with the
-// tensor's s_enc and its table of s_enc / S.
+// tensor's s_enc and its table of s_enc / S (or, with rtab == nullptr, that
+// entry divided out here: the same correctly rounded quotient).
 __device__ __forceinline__ void encode_block(const float v[16], float bamax, float s_enc, const float* rtab,
                                              uint32_t& lo, uint32_t& hi, uint32_t& scale) {
     const float t = bamax * s_enc;
     const uint32_t S = e4m3_rne_sat(div6(t));
-    const float r = rtab[S];
+    const float r = rtab ? rtab[S] : (S == 0 ? 0.0f : s_enc / e4m3_to_f32(S));
     float q[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) q[i] = v[i] * r;
@@ -254,18 +255,6 @@ __device__ __forceinline__ _Float16 scale_byte(uint32_t packed, int i) {
 
 __device__ __forceinline__ uint32_t word_of(const uint4& v, int i) {
     return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
-}
-
-// One k-step of the skinny product: decode the weight and activation chunks
-// (one E4M3 scale per 16-element block) and accumulate four 16x16x32 products.
-__device__ __forceinline__ void skinny_step(float4v& acc, const uint4& wv, uint32_t ws, const uint4& xv,
-                                            uint32_t xs) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const half8 a = decode8(word_of(wv, c), scale_byte(ws, c >> 1));
-        const half8 b = decode8(word_of(xv, c), scale_byte(xs, c >> 1));
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -370,9 +359,11 @@ hipError_t launch_gemm(int64_t M, const uint8_t* a_codes, const uint8_t* a_scale
                        const nvfp4_weight_desc& d, float* y, int64_t ld_y, void* ws, size_t ws_bytes,
                        const Epilogue& gp, hipStream_t stream);
 
-// Few-token products (skinny.hip).  The workspace starts with one 32-bit counter
-// per 64-row weight group, which must be zero before first use (each call
-// leaves it zero), followed by the split-K partial tiles.
+// Few-token products (skinny.hip).  With the activations encoded in the same
+// launch (nvfp4_linear) the workspace holds 256 bytes of launch-tagged flags
+// per XCD (zero before the first use; no launch needs them reset).  The
+// product alone needs none.
+constexpr size_t kSkinnyCounterBytes = 2048;
 bool skinny_applies(int64_t M, const nvfp4_weight_desc& d);
 size_t skinny_workspace_bytes(const nvfp4_weight_desc& d);
 hipError_t launch_skinny(int64_t M, const void* x, int in_dtype, int64_t ld_x, float* g_x, int g_mode,

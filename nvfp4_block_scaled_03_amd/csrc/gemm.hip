@@ -537,9 +537,7 @@ static int64_t column_split(int64_t M, const nvfp4_weight_desc& d) {
     return all_small < all_large ? 0 : d.n_padded;
 }
 
-size_t gemm_workspace_bytes(int64_t M, const nvfp4_weight_desc& d) {
-    return skinny_applies(M, d) ? skinny_workspace_bytes(d) : 0;
-}
+size_t gemm_workspace_bytes(int64_t, const nvfp4_weight_desc&) { return 0; }
 
 // One launch over the weight's columns [c0, c1) (multiples of the tile width;
 // c1 <= n_padded): operand, column-scale and output pointers move to column

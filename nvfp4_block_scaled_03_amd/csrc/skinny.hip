@@ -1,397 +1,449 @@
-// Few-token (M <= 16) NVFP4 products, bound by the weight stream from HBM.
+// Few-token (1 <= M <= 16) NVFP4 products, bound by the weight stream from HBM.
 //
-// Work split.  The weight rows are cut into groups of R 16-row blocks and K
-// into S slices of NKSL k-steps (128 elements each).  Workgroup (g, s) has R
-// wavefronts; wavefront w owns block g*R + w over slice s.  R, NKSL and S are
-// chosen on the host so that the workgroups cover the 256 compute units
-// evenly (5120 rows: 64 groups of 5 blocks x 4 slices = 256 workgroups): a
-// compute unit's share of the weight stream, not its arithmetic, sets when it
-// finishes, so one unit with twice the share finishes twice as late.
+// Work split.  One product workgroup per 16-row block of the packed weight,
+// over all of K: W wavefronts, wavefront w owns the k-steps [w*NKW, (w+1)*NKW).
+// Each wavefront issues all its weight loads at the start and decodes them to
+// FP16 registers as they arrive, so nothing stands in front of the weight
+// stream.  The W partial 16x16 tiles are added through LDS in wavefront order
+// (a fixed order: the result never depends on timing) and the workgroup writes
+// its 16 columns of Y.  No workgroup adds another's partials.
 //
-// Per workgroup.  The activation-side loads are issued first, without
-// branches (rows >= M read as zero through the buffer bounds), then the first
-// kDepth k-steps of every wavefront's weights.  The activations of the slice
-// are prepared once, as exact FP16 values code x scale in LDS, laid out in the
-// B-operand order of the 16x16x32 matrix instruction:
-//   CODES (nvfp4_gemm): decode the caller's codes and scales;
-//   QUANT (nvfp4_linear): quantize the raw activations with the global scale
-//     (given, or reduced from the amax partials of the preceding kernel) and
-//     decode them; the workgroups of group 0 also store the codes and scales.
-// Each wavefront then walks its k-steps: decode the weight chunk, four matrix
-// instructions, and issue the loads kDepth k-steps ahead.
+// Activations are the B operand of the 16x16x32 instruction, read straight
+// from the canonical encoding: lane (token t, lane group kg) needs, per k-step
+// ks, the code bytes [ks*64 + 16kg, +16) of token t's row (the 32 elements the
+// weight lane (row, kg) holds) and the scales [ks*8 + 2kg, +2); rows t >= M
+// read zero through the buffer bounds.
+//   nvfp4_gemm: the encoding is an input, loaded together with the weights.
+//   nvfp4_linear: the encoding is made in the same launch, once per XCD.
 //
-// Summing the slices.  No workgroup ever waits for one that may not have
-// started.  Each workgroup draws a ticket from its group's counter when it
-// starts; the one drawing S-1 (the last to start) is the reducer, the others
-// store their partial tiles past the caches and finish.  A stored partial is
-// negated after -0 is turned into +0, so none of its words is zero; the
-// reducer polls each partial until all its words are nonzero, adds the S
-// partials in slice order 0..S-1 (its own from registers), so the result does
-// not depend on timing, writes Y = sum * g_x * g_w, zeroes the partials it
-// read and resets the counter: the workspace is zero again for the next call.
+// Encoding inside one XCD.  Each XCD has its own L2, and a hand-over between
+// workgroups of one XCD goes through that L2 (a few hundred ns), while one
+// between XCDs goes to memory (microseconds under a full weight stream).  So
+// every XCD encodes the activations itself, into the same canonical buffer
+// (the bytes are the same whoever writes them), and its product workgroups
+// wait only for their own XCD's encoders:
+//   - workgroups 0 .. 8E-1 are encoders: workgroup i encodes share i / 8 for
+//     the XCD it runs on (the hardware hands out workgroups round-robin over
+//     the XCDs, from an XCD that depends on earlier launches, so any 8
+//     consecutive workgroups cover the 8 XCDs once each);
+//   - the E encoders of an XCD each reduce max|x| over 1/E of the tensor and
+//     exchange the partial maxima through the L2 (or take the given g), then
+//     encode their 1/E of the 16-element blocks and raise their `ready` flag;
+//   - a product workgroup decodes its weights, waits for the E flags of its
+//     XCD and then loads the encoding past its L1.
+// Every workgroup reads the XCD it runs on from the XCC_ID hardware register.
+// One whose wait exceeds a bound (its XCD lacks an encoder share, if the
+// hand-out ever differs from the above) encodes all the blocks itself instead
+// (the same bytes), so no result depends on where workgroups run or on
+// another one being resident.
+// The hand-over uses no atomics: each encoder owns its words and writes them
+// with plain stores, which land in its XCD's L2 (after a wait for the data
+// they publish), and readers poll them with loads past their L1.  A flag holds
+// a tag of the launch (dispatch id and queue), so a flag left by an earlier
+// launch reads as not raised: nothing is reset after a launch and no
+// workgroup waits for another to finish.
 #include <cstdlib>
+#include <type_traits>
 
 #include "common.h"
 
+#pragma clang fp contract(off)
+
+// The launch's dispatch id (a user SGPR the command processor sets for every
+// dispatch), through the LLVM intrinsic that reads it.
+extern "C" __device__ uint64_t nvfp4_llvm_dispatch_id() __asm("llvm.amdgcn.dispatch.id");
+
 namespace nvfp4 {
 
-constexpr int kWriteThrough = 1 | 16;   // sc0|sc1: store past the non-coherent caches
-constexpr int kDepth = 4;               // weight k-steps in flight per wavefront ahead of the math
-constexpr int kMaxSlices = 8;           // K-slices per group (the reducer polls at most 7 partials)
-constexpr int kSpinLimit = 1 << 20;     // polls before the reducer gives up (a misuse, never a hang)
-constexpr int kMaxPre = 10;             // longest slice (bf16 input; 4 for fp32) whose weights are decoded
-                                        // ahead of the activations (16 VGPRs per k-step)
+constexpr int kXcds = 8;                 // MI355X
+constexpr int kEncPerXcd = 8;            // encoder workgroups per XCD (nvfp4_linear); with 16 the 448
+                                         // workgroups of the decode layer no longer all fit at once
+constexpr int kWaves = 8;                // wavefronts per product workgroup (fewer when K is short)
+constexpr int kMaxNkw = 8;               // k-steps per wavefront: K <= 8 * 8 * 128
+constexpr int kEncBlocksPerThread = 2;   // blocks an encoder thread holds: 8 * 512 * 2 >= 16 * 8192 / 16
+constexpr int kDefaultPolls = 1 << 15;   // polls (each after a short sleep) before encoding locally
+constexpr uint32_t kDeadOffset = 0x80000000u;   // scalar offset past every buffer: the load reads zero
+// Cache policy of the hand-over loads: sc1.  Measured on MI355X between two
+// CUs of one XCD: loads with sc1 (or nt) see another CU's plain store within
+// 0.05-0.3 us (served by the XCD's L2), while plain or sc0 loads keep
+// returning the stale value even after an L1 invalidate.
+constexpr int kPastL1 = 16;
 
-constexpr int kAmaxSpin = 1 << 12;      // polls for a peer's slice max before reducing that slice here
+// Per-XCD words of the workspace (256 bytes): per encoder e, a 16-byte record
+// of its partial max|x| {tag low, tag high, max bits, check} (one store; the
+// check word, tag low ^ tag high ^ max ^ a constant, rejects a record read
+// while half written), and the launch tag once its blocks are encoded.
+struct XcdWords {
+    uint4 amax_rec[kEncPerXcd];
+    uint64_t ready_flag[kEncPerXcd];
+    uint32_t pad[16];
+};
+constexpr uint32_t kRecCheck = 0x5A17C3E5u;
+static_assert(sizeof(XcdWords) == 256, "two 128-byte lines per XCD");
+static_assert(kXcds * sizeof(XcdWords) <= kSkinnyCounterBytes, "the workspace holds every XCD's words");
 
-// Max over the workgroup (R wavefronts), via LDS scratch of R floats; all threads get it.
-template <int R>
-__device__ __forceinline__ float block_max_r(float v, float* s_red) {
-    v = wave_max(v);
-    __syncthreads();   // s_red may still be read from a previous call
-    if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = v;
-    __syncthreads();
-    float a = s_red[0];
-#pragma unroll
-    for (int i = 1; i < R; ++i) a = fmaxf(a, s_red[i]);
-    return a;
+// Wait for this wavefront's LDS accesses, then the workgroup barrier (outstanding
+// global loads stay in flight).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt left at their maxima
+    __builtin_amdgcn_s_barrier();
 }
 
-// Activation-operand LDS offset (bytes) of chunk c of k-step j for token m, lane group kg.
-__device__ __forceinline__ int xhat_offset(int j, int c, int m, int kg) {
-    return ((j * 4 + c) * 64 + m + 16 * kg) * 16;
+// The XCD this wavefront runs on.
+__device__ __forceinline__ uint32_t hw_xcc_id() {
+    return (uint32_t)__builtin_amdgcn_s_getreg((20) | (0 << 6) | (3 << 11)) & 0xFu;   // hwreg(HW_REG_XCC_ID, 0, 4)
 }
 
-// Write the two FP16 chunks of one decoded 16-element block (local block kb of the slice, token m);
-// a thread without a block (past the slice) writes to the spare 32 bytes at `spare` instead, so the
-// preparation has no branch around it.
-__device__ __forceinline__ void put_block(uint8_t* lds, int kb, int m, bool valid, int spare, const half8& lo,
-                                          const half8& hi) {
-    const int j = kb >> 3, b8 = kb & 7, kg = b8 >> 1, c0 = (b8 & 1) * 2;
-    const int o0 = valid ? xhat_offset(j, c0, m, kg) : spare;
-    const int o1 = valid ? xhat_offset(j, c0 + 1, m, kg) : spare + 16;
-    *reinterpret_cast<half8*>(lds + o0) = lo;
-    *reinterpret_cast<half8*>(lds + o1) = hi;
+// Tag of this launch: the dispatch id mixed with the queue address (dispatch
+// ids count per queue); never 0, the value of an unused flag.
+__device__ __forceinline__ uint64_t launch_tag() {
+    const uint64_t q = (uint64_t)(uintptr_t)__builtin_amdgcn_queue_ptr();
+    const uint64_t h = ((nvfp4_llvm_dispatch_id() + 1) * 0x9E3779B97F4A7C15ull) ^ (q * 0xC2B2AE3D27D4EB4Full);
+    return h | 1u;
 }
 
-template <typename T, int NKSL, int R, bool QUANT, bool PRE, bool EPI>
-__global__ __launch_bounds__(R * 64) void skinny_kernel(
-    int M, int64_t K, const T* __restrict__ x, int64_t ld_x, float* __restrict__ g_x, int g_given,
-    uint8_t* __restrict__ x_codes, uint8_t* __restrict__ x_scales, const uint8_t* __restrict__ w_codes,
-    const uint8_t* __restrict__ w_scales, const float* __restrict__ colscale, int64_t N, int64_t n_pad,
-    float* __restrict__ y, int64_t ld_y, uint32_t* __restrict__ counters, uint32_t* __restrict__ slots,
-    float* __restrict__ partials, int S, int amax_polls, Epilogue gp) {
-    constexpr int kThreads = R * 64;
-    constexpr int kXhatBytes = NKSL * 4 * 64 * 16;
-    constexpr int kD = NKSL < kDepth ? NKSL : kDepth;
-    __shared__ __attribute__((aligned(16))) uint8_t xhat[kXhatBytes + 32];   // + spare slot
-    __shared__ float s_red[R];
-    __shared__ float s_slotmax[kMaxSlices];
-    __shared__ uint32_t s_ticket;
-    __shared__ float rtab[QUANT ? 128 : 1];
+// Raise this encoder's flag: the data it publishes (stored by every thread of
+// the workgroup before the barrier that precedes this call) is in the L2.
+__device__ __forceinline__ void raise_flag(uint64_t* flag, uint64_t tag) {
+    __builtin_amdgcn_s_waitcnt(0);
+    *reinterpret_cast<volatile uint64_t*>(flag) = tag;
+}
 
-    const int grp = blockIdx.x / S, slice = blockIdx.x - grp * S;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int KS = (int)(K / kPackK);
-    const int r16 = lane & 15, kg = lane >> 4;
-    const int nb = grp * R + wave;                 // this wavefront's 16-row weight block
-    const int ks0 = slice * NKSL;
-
-    // Activation-side loads of the slice (branch-free; rows >= M and slots past
-    // the slice read as zero through the buffer bounds).
-    constexpr int kSliceBlocks = NKSL * 8;          // 16-element blocks per token in the slice
-    constexpr int kBPT = (16 * kSliceBlocks + kThreads - 1) / kThreads;
-    constexpr int kRawVec = QUANT ? (int)(sizeof(RawBlock<T>) / 16) : 1;
-    RawBlock<T> raw[QUANT ? kBPT : 1];
-    uint2 cw[QUANT ? 1 : kBPT];
-    uint32_t sw[QUANT ? 1 : kBPT];
-    auto load_activations = [&]() {
-        if constexpr (QUANT) {
-            const rsrc_t rx = make_rsrc(x, (uint64_t)M * ld_x * sizeof(T));
-#pragma unroll
-            for (int u = 0; u < kBPT; ++u) {
-                const int b = threadIdx.x + u * kThreads;
-                const int m = b / kSliceBlocks, kb = b - m * kSliceBlocks;
-                const uint32_t off =
-                    m < M ? (uint32_t)(((int64_t)m * ld_x + (int64_t)(ks0 * 8 + kb) * 16) * (int64_t)sizeof(T))
-                          : kOutOfBounds;
-#pragma unroll
-                for (int q = 0; q < kRawVec; ++q) raw[u].v[q] = bload16(rx, off, (uint32_t)q * 16);
-            }
-        } else {
-            const rsrc_t rxc = make_rsrc(x_codes, (uint64_t)M * K / 2);
-            const rsrc_t rxs = make_rsrc(x_scales, (uint64_t)M * K / 16);
-#pragma unroll
-            for (int u = 0; u < kBPT; ++u) {
-                const int b = threadIdx.x + u * kThreads;
-                const int m = b / kSliceBlocks, kb = b - m * kSliceBlocks;
-                const uint32_t blk = (uint32_t)(m * (int)(K / 16) + ks0 * 8 + kb);
-                cw[u] = bload8(rxc, m < M ? blk * 8 : kOutOfBounds, 0);
-                sw[u] = bload1(rxs, m < M ? blk : kOutOfBounds, 0);
-            }
-        }
-    };
-
-    // Weight slice: kD k-steps in flight ahead of their use.
-    const rsrc_t rwc = make_rsrc(w_codes, (uint64_t)n_pad * K / 2);
-    const rsrc_t rws = make_rsrc(w_scales, (uint64_t)n_pad * K / 16);
-    const uint32_t wc_off = (uint32_t)nb * KS * 1024 + kg * 256 + r16 * 16;
-    const uint32_t ws_off = (uint32_t)nb * KS * 128 + r16 * 8 + kg * 2;
-    uint4 wv[NKSL];
-    uint32_t wsv[NKSL];
-    auto load_weights = [&](int j) {
-        wv[j] = bload16(rwc, wc_off, (uint32_t)(ks0 + j) * 1024);
-        wsv[j] = bload2(rws, ws_off, (uint32_t)(ks0 + j) * 128);
-    };
-    const rsrc_t rcs = make_rsrc(colscale, (uint64_t)n_pad * 4);
-    float4v csv;
-    uint32_t ticket = 0;
-    // (built with the atomic optimizer off: it would turn this into a wave-wide
-    // operation whose result is needed at once, waiting here for every load above)
-    auto draw_ticket = [&]() {
-        if (S > 1 && threadIdx.x == 0)
-            ticket = __hip_atomic_fetch_add(&counters[grp], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    };
-    half8 adec[PRE ? NKSL : 1][4];
-
-    // Activations first (loads complete in issue order, so waiting for them
-    // leaves the weights in flight), then the weights' first kD k-steps.
-    load_activations();
-    csv = __builtin_bit_cast(float4v, bload16(rcs, (uint32_t)(nb * 16 + kg * 4) * 4, 0));
-#pragma unroll
-    for (int j = 0; j < kD; ++j) load_weights(j);
-    draw_ticket();
-    __builtin_amdgcn_sched_barrier(0);
-
-    // Global scale computed here (nvfp4_linear without a given scale): the S
-    // workgroups of a group hold the S slices of the same activations; each
-    // publishes its slice's max|x| as soon as its slice is in and collects the
-    // others' later.  A slice not published after kAmaxSpin polls is reduced
-    // here instead, so no workgroup depends on another one running.
-    const bool exchange = QUANT && !g_given;
-    uint32_t* gslots = slots + (size_t)grp * S;
-    float mine = 0.0f;
-    float bam[QUANT ? kBPT : 1];   // max |x| of each of this thread's blocks
-    if (exchange) {
-        float part = 0.0f;
-#pragma unroll
-        for (int u = 0; u < (QUANT ? kBPT : 0); ++u) {
-            float v[16];
-            widen(raw[u], v);
-            bam[u] = block_amax(v);
-            part = fmaxf(part, bam[u]);
-        }
-        mine = block_max_r<R>(part, s_red);
-        if (S > 1 && threadIdx.x == 0)   // (sign bit set: a published word is never zero)
-            __hip_atomic_store(gslots + slice, __float_as_uint(mine) | 0x80000000u, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-    }
-
-    if constexpr (PRE) {
-        // Decode the weights to FP16 registers as they arrive, while the slice
-        // maxima of the other workgroups travel; only the matrix instructions
-        // remain once the activations are prepared.
-#pragma unroll
-        for (int j = 0; j < NKSL; ++j) {
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                adec[j][c] = decode8(word_of(wv[j], c), scale_byte(wsv[j], c >> 1));
-                asm volatile("" : "+v"(adec[j][c]));   // decode now, not next to its use
-            }
-            if (j + kD < NKSL) load_weights(j + kD);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    }
-
-    float gx = (QUANT && !g_given) ? 0.0f : g_x[0];
-    if (exchange) {
-        if (threadIdx.x < (unsigned)S) {
-            float got = mine;
-            if ((int)threadIdx.x != slice) {
-                uint32_t w = 0;
-                for (int i = 0; i < amax_polls && w == 0; ++i) {
-                    w = __hip_atomic_load(gslots + threadIdx.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    if (w == 0) __builtin_amdgcn_s_sleep(2);
-                }
-                got = w != 0 ? __uint_as_float(w & 0x7FFFFFFFu) : -1.0f;
-            }
-            s_slotmax[threadIdx.x] = got;
-        }
-        __syncthreads();
-        float amax = 0.0f;
-        for (int t = 0; t < S; ++t) {
-            const float m_t = s_slotmax[t];
-            if (m_t >= 0.0f) {
-                amax = fmaxf(amax, m_t);
-            } else {   // this workgroup reduces slice t itself
-                float p = 0.0f;
-                for (int b = threadIdx.x; b < M * kSliceBlocks; b += kThreads) {
-                    const int m = b / kSliceBlocks, kb = b - m * kSliceBlocks;
-                    const T* src = x + (int64_t)m * ld_x + (int64_t)(t * kSliceBlocks + kb) * 16;
-                    float v[16];
-                    load8(src, v);
-                    load8(src + 8, v + 8);
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) p = fmaxf(p, __builtin_fabsf(v[i]));
-                }
-                amax = fmaxf(amax, block_max_r<R>(p, s_red));
-            }
-        }
-        gx = global_scale_from_amax(amax);
-        if (blockIdx.x == 0 && threadIdx.x == 0) g_x[0] = gx;
-    }
-
-    float s_enc = 0.0f;
-    if constexpr (QUANT) {
-        s_enc = 1.0f / gx;
-        fill_recip_table(rtab, s_enc, threadIdx.x, kThreads);
-        __syncthreads();
-    }
-
-    // The activations of the slice, once per workgroup, as exact FP16 in LDS.
-#pragma unroll
-    for (int u = 0; u < kBPT; ++u) {
-        const int b = threadIdx.x + u * kThreads;
-        const int m = b / kSliceBlocks, kb = b - m * kSliceBlocks;
-        const bool valid = b < 16 * kSliceBlocks;
-        half8 lo, hi;
-        if constexpr (QUANT) {
-            float v[16];
-            widen(raw[u], v);
-            uint32_t c_lo, c_hi, S8;
-            encode_block(v, exchange ? bam[u] : block_amax(v), s_enc, rtab, c_lo, c_hi, S8);
-            const _Float16 s16 = e4m3_to_f16(S8);
-            lo = decode8(c_lo, s16);
-            hi = decode8(c_hi, s16);
-            if (grp == 0 && m < M && valid) {   // one workgroup per slice stores the activations' encoding
-                const int64_t blk = (int64_t)m * (K / 16) + ks0 * 8 + kb;
-                *reinterpret_cast<uint2*>(x_codes + blk * 8) = make_uint2(c_lo, c_hi);
-                x_scales[blk] = (uint8_t)S8;
-            }
-        } else {
-            const _Float16 s16 = e4m3_to_f16(sw[u]);
-            lo = decode8(cw[u].x, s16);
-            hi = decode8(cw[u].y, s16);
-        }
-        put_block(xhat, kb, m, valid, kXhatBytes, lo, hi);
-    }
-    __syncthreads();
-
-    // 16x16x32 products over the slice (weights decoded here, loads kD k-steps
-    // ahead, unless already decoded above).
-    float4v acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int j = 0; j < NKSL; ++j) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            half8 a;
-            if constexpr (PRE) a = adec[j][c];
-            else a = decode8(word_of(wv[j], c), scale_byte(wsv[j], c >> 1));
-            const half8 b = *reinterpret_cast<const half8*>(xhat + xhat_offset(j, c, r16, kg));
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
-        }
-        if constexpr (!PRE) {
-            if (j + kD < NKSL) load_weights(j + kD);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    }
-
-    // Lane holds rows 4*kg..4*kg+3 of block nb for token r16.
-    const int64_t n_base = (int64_t)nb * 16 + kg * 4;
-    bool gated = false;   // only the row blocks that hold gate columns take the gated stores
-    if constexpr (EPI) gated = gates_touch((int64_t)nb * 16, (int64_t)nb * 16 + 16, gp);
-    if (S == 1) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int64_t n = n_base + r;
-            if (r16 < M && n < N) {
-                float v = acc[r] * (gx * csv[r]);
-                if (EPI && gated) v = gate(v, n, gp);
-                if constexpr (EPI)
-                    store_y(y, (int64_t)r16 * ld_y + n, v, gp);
-                else
-                    y[(int64_t)r16 * ld_y + n] = v;
-            }
-        }
-        return;
-    }
-    if (threadIdx.x == 0) s_ticket = ticket;
-    __syncthreads();
-    const bool reducer = s_ticket == (uint32_t)(S - 1);
-    float4v own;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) own[r] = acc[r] + 0.0f;   // -0 -> +0
-    constexpr int kTile = kThreads * 16;                    // bytes of one partial tile
-    const rsrc_t rpart = make_rsrc(partials, (uint64_t)gridDim.x * kTile);
-    const uint32_t poff = (uint32_t)threadIdx.x * 16;
-    if (!reducer) {
-        float4v neg;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) neg[r] = -own[r];
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, neg), rpart, (int)poff,
-                                               (int)(blockIdx.x * kTile), kWriteThrough);
-        return;
-    }
-    if (threadIdx.x == 0) __hip_atomic_store(&counters[grp], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-
-    // Poll every other slice's partial (all loads of a round in flight together).
-    float4v pt[kMaxSlices];
-    bool ready[kMaxSlices];
-#pragma unroll
-    for (int t = 0; t < kMaxSlices; ++t) ready[t] = !(t < S && t != slice);
-    for (int round = 0;; ++round) {
-#pragma unroll
-        for (int t = 0; t < kMaxSlices; ++t) {
-            if (!ready[t]) {
-                const uint32_t* src = reinterpret_cast<const uint32_t*>(
-                    reinterpret_cast<const uint8_t*>(partials) + (size_t)(grp * S + t) * kTile + poff);
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    pt[t][r] = __uint_as_float(
-                        __hip_atomic_load(src + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-            }
-        }
+// Poll the kEncPerXcd flags from the L2 until all hold `tag`, at most `polls`
+// times.  True when they did.
+__device__ __forceinline__ bool wait_flags(const uint64_t* flags, uint64_t tag, int polls) {
+    static_assert(kEncPerXcd % 2 == 0, "two flags per 16-byte load");
+    const rsrc_t r = make_rsrc(flags, kEncPerXcd * 8);
+    for (int i = 0; i < polls; ++i) {
         bool all = true;
 #pragma unroll
-        for (int t = 0; t < kMaxSlices; ++t) {
-            if (!ready[t]) {
-                ready[t] = __float_as_uint(pt[t][0]) != 0u && __float_as_uint(pt[t][1]) != 0u &&
-                           __float_as_uint(pt[t][2]) != 0u && __float_as_uint(pt[t][3]) != 0u;
-                all = all && ready[t];
+        for (int q = 0; q < kEncPerXcd / 2; ++q) {
+            const uint4 v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, 16 * q, 0, kPastL1));
+            all = all && ((uint64_t)v.y << 32 | v.x) == tag && ((uint64_t)v.w << 32 | v.z) == tag;
+        }
+        if (all) return true;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    return false;
+}
+
+// max over the workgroup of a non-negative 32-bit key; every thread gets it.
+__device__ __forceinline__ uint32_t wg_max_u32(uint32_t v, uint32_t* s_red, int nwaves) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));
+    if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = v;
+    lds_barrier();
+    uint32_t r = 0;
+    for (int i = 0; i < nwaves; ++i) r = max(r, s_red[i]);
+    lds_barrier();   // s_red may be reused
+    return r;
+}
+
+struct SkinnyParams {
+    int M;
+    int KS;                  // k-steps of 128 elements
+    int64_t K;
+    const void* x;           // raw activations (nvfp4_linear)
+    int64_t ld_x;
+    float* g_x;
+    int g_given;
+    uint8_t* x_codes;        // canonical encoding (input of nvfp4_gemm, output of nvfp4_linear)
+    uint8_t* x_scales;
+    const uint8_t* wc;       // packed weight codes, scales, column scales
+    const uint8_t* wsc;
+    const float* cs;
+    int64_t N, n_pad;
+    float* y;
+    int64_t ld_y;
+    XcdWords* xw;            // workspace: one XcdWords per XCD (nvfp4_linear)
+    int n_enc;               // encoder workgroups (kXcds * kEncPerXcd, or 0)
+    int polls;
+    Epilogue gp;
+};
+
+// ---------------------------------------------------------------------------
+// Encoding the activations (whole workgroup).
+// ---------------------------------------------------------------------------
+
+// Bits of max |v| over one raw block (finite values order like their bit patterns).
+template <typename T>
+__device__ __forceinline__ uint32_t raw_block_amax_bits(const RawBlock<T>& r) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int q = 0; q < (int)(sizeof(RawBlock<T>) / 16); ++q) {
+        const uint32_t w[4] = {r.v[q].x, r.v[q].y, r.v[q].z, r.v[q].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if constexpr (sizeof(T) == 2) {
+                m = max(m, (w[i] & 0x7FFFu) << 16);
+                m = max(m, w[i] & 0x7FFF0000u);
+            } else {
+                m = max(m, w[i] & 0x7FFFFFFFu);
             }
         }
-        if (all || round >= kSpinLimit) break;
-        __builtin_amdgcn_s_sleep(2);
     }
-    // every member has read the group's slice maxima by now (it stored its partial after)
-    if (QUANT && threadIdx.x < (unsigned)S)
-        __hip_atomic_store(slots + (size_t)grp * S + threadIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    float4v sum = {0.f, 0.f, 0.f, 0.f};
+    return m;
+}
+
+// Raw block b (token b / (K/16), block b % (K/16) of its row); zeros from nblk on.
+template <typename T>
+__device__ __forceinline__ RawBlock<T> load_raw_block(const SkinnyParams& p, const rsrc_t& rx, uint32_t b,
+                                                      uint32_t nblk) {
+    const uint32_t kb_per_row = (uint32_t)(p.K / 16);
+    const uint32_t t = b / kb_per_row, kb = b - t * kb_per_row;
+    const uint32_t off = b < nblk ? (uint32_t)((int64_t)t * p.ld_x * sizeof(T) + (int64_t)kb * 16 * sizeof(T))
+                                  : kOutOfBounds;
+    RawBlock<T> raw;
 #pragma unroll
-    for (int t = 0; t < kMaxSlices; ++t) {
-        if (t < S) {
+    for (int q = 0; q < (int)(sizeof(RawBlock<T>) / 16); ++q)
+        raw.v[q] = bload16(rx, b < nblk ? off + (uint32_t)q * 16 : kOutOfBounds, 0);
+    return raw;
+}
+
+// Encode one raw block with the global scale's table and store its code bytes
+// and scale into the canonical encoding.
+template <typename T>
+__device__ __forceinline__ void encode_store_block(const SkinnyParams& p, const RawBlock<T>& raw, uint32_t b,
+                                                   float s_enc, const float* rtab) {
+    float v[16];
+    widen(raw, v);
+    uint32_t lo, hi, S;
+    encode_block(v, block_amax(v), s_enc, rtab, lo, hi, S);
+    *reinterpret_cast<uint2*>(p.x_codes + (size_t)b * 8) = make_uint2(lo, hi);
+    p.x_scales[b] = (uint8_t)S;
+}
+
+// The whole encoding by one workgroup (the local path): max|x| over the
+// tensor (unless g is given), then every block.  One block in flight per
+// thread: a slow path that must not raise the kernel's registers above those
+// of the usual path.  Every thread's stores are complete on return.
+template <typename T>
+__device__ float encode_all_here(const SkinnyParams& p, uint32_t* s_red, float* rtab, int nthreads) {
+    const uint32_t nblk = (uint32_t)(p.M * (p.K / 16));
+    const rsrc_t rx = make_rsrc(p.x, (uint64_t)p.M * p.ld_x * sizeof(T));
+    float g;
+    if (p.g_given) {
+        g = p.g_x[0];
+    } else {
+        uint32_t m = 0;
+        for (uint32_t b = threadIdx.x; b < nblk; b += (uint32_t)nthreads)
+            m = max(m, raw_block_amax_bits<T>(load_raw_block<T>(p, rx, b, nblk)));
+        g = global_scale_from_amax(__uint_as_float(wg_max_u32(m, s_red, nthreads >> 6)));
+        if (threadIdx.x == 0) p.g_x[0] = g;
+    }
+    const float s_enc = 1.0f / g;
+    fill_recip_table(rtab, s_enc, threadIdx.x, nthreads);
+    lds_barrier();
+    for (uint32_t b = threadIdx.x; b < nblk; b += (uint32_t)nthreads)
+        encode_store_block<T>(p, load_raw_block<T>(p, rx, b, nblk), b, s_enc, rtab);
+    __builtin_amdgcn_s_waitcnt(0);   // this thread's stores are done
+    lds_barrier();
+    return g;
+}
+
+// Encoder e of XCD `xw`: its 1/E of the blocks, held in registers from the
+// start; the XCD's amax from the E partial maxima (or the given g); then the
+// blocks, and its `ready` flag.  If the exchange does not complete within the
+// bound it stops without raising it (the XCD's product workgroups then encode
+// locally).
+template <typename T>
+__device__ void run_encoder(const SkinnyParams& p, uint32_t e, XcdWords* xw, uint64_t tag, uint32_t* s_red,
+                            float* rtab, float* s_g, int nthreads) {
+    const uint32_t nblk = (uint32_t)(p.M * (p.K / 16));
+    const uint32_t per = (nblk + kEncPerXcd - 1) / kEncPerXcd;
+    const uint32_t b0 = min(nblk, e * per), b1 = min(nblk, b0 + per);
+    const rsrc_t rx = make_rsrc(p.x, (uint64_t)p.M * p.ld_x * sizeof(T));
+    RawBlock<T> raw[kEncBlocksPerThread];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sum[r] += t == slice ? own[r] : -pt[t][r];
+    for (int j = 0; j < kEncBlocksPerThread; ++j)
+        raw[j] = load_raw_block<T>(p, rx, b0 + threadIdx.x + j * nthreads, b1);
+
+    if (p.g_given) {
+        if (threadIdx.x == 0) *s_g = p.g_x[0];
+    } else {
+        uint32_t m = 0;
+#pragma unroll
+        for (int j = 0; j < kEncBlocksPerThread; ++j) m = max(m, raw_block_amax_bits<T>(raw[j]));
+        m = wg_max_u32(m, s_red, nthreads >> 6);
+        if (threadIdx.x == 0) {
+            const uint32_t lo = (uint32_t)tag, hi = (uint32_t)(tag >> 32);
+            xw->amax_rec[e] = make_uint4(lo, hi, m, lo ^ hi ^ m ^ kRecCheck);
+            // poll the E records from the L2 until all carry this launch's tag and a valid check
+            const rsrc_t rr = make_rsrc(xw->amax_rec, sizeof(xw->amax_rec));
+            bool all = false;
+            uint32_t amax = 0;
+            for (int i = 0; i < p.polls && !all; ++i) {
+                all = true;
+                amax = 0;
+#pragma unroll
+                for (int k = 0; k < kEncPerXcd; ++k) {
+                    const uint4 r = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rr, 16 * k, 0,
+                                                                                                   kPastL1));
+                    all = all && r.x == lo && r.y == hi && r.w == (lo ^ hi ^ r.z ^ kRecCheck);
+                    amax = max(amax, r.z);
+                }
+                if (!all) __builtin_amdgcn_s_sleep(1);
+            }
+            *s_g = all ? global_scale_from_amax(__uint_as_float(amax)) : -1.0f;
         }
     }
+    lds_barrier();
+    const float g = *s_g;
+    if (g < 0.0f) return;   // no g: this encoder's `ready` flag stays down and its XCD's product workgroups
+                            // encode locally
+    if (!p.g_given && e == 0 && threadIdx.x == 0) p.g_x[0] = g;
+    const float s_enc = 1.0f / g;
+#pragma unroll
+    for (int j = 0; j < kEncBlocksPerThread; ++j) {   // (r = s_enc / S divided per block: no table to fill)
+        const uint32_t b = b0 + threadIdx.x + j * nthreads;
+        if (b < b1) encode_store_block<T>(p, raw[j], b, s_enc, nullptr);
+    }
+    __builtin_amdgcn_s_waitcnt(0);   // every thread's codes, scales (and g) are in the L2
+    lds_barrier();
+    if (threadIdx.x == 0) raise_flag(&xw->ready_flag[e], tag);
+}
+
+// ---------------------------------------------------------------------------
+// The kernel.
+// ---------------------------------------------------------------------------
+template <typename T, int NKW, bool ENC, bool EPI>
+__global__ __launch_bounds__(kWaves * 64) void skinny_kernel(SkinnyParams p) {
+    __shared__ __attribute__((aligned(16))) float4v red[kWaves][64];
+    __shared__ uint32_t s_red[kWaves];
+    __shared__ float rtab[ENC ? 128 : 1];
+    __shared__ float s_g;
+    __shared__ int s_local;
+
+    const int nthreads = (int)blockDim.x;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int r16 = lane & 15, kg = lane >> 4;
+
+    uint64_t tag = 0;
+    uint32_t xcd = 0;
+    bool xcd_ok = false;
+    if constexpr (ENC) {
+        tag = launch_tag();
+        xcd = hw_xcc_id();
+        xcd_ok = xcd < (uint32_t)kXcds;
+        if ((int)blockIdx.x < p.n_enc) {   // encoder workgroup: share blockIdx / 8 of its XCD
+            if (xcd_ok) run_encoder<T>(p, (uint32_t)blockIdx.x / kXcds, p.xw + xcd, tag, s_red, rtab, &s_g, nthreads);
+            return;
+        }
+    }
+    const int nb = (int)blockIdx.x - (ENC ? p.n_enc : 0);   // this workgroup's 16-row weight block
+    const int ks0 = wave * NKW;
+
+    // Weights first: all NKW k-steps of this wavefront (k-steps past K read zero).
+    const rsrc_t rwc = make_rsrc(p.wc, (uint64_t)p.n_pad * p.K / 2);
+    const rsrc_t rws = make_rsrc(p.wsc, (uint64_t)p.n_pad * p.K / 16);
+    // (lane part in the vector offset, block and k-step in the scalar one: a dead
+    // k-step's scalar offset lies past the buffer, and the sum stays below 2^32)
+    const uint32_t wc_lane = kg * 256 + r16 * 16, ws_lane = r16 * 8 + kg * 2;
+    const uint32_t wc_blk = (uint32_t)nb * p.KS * 1024, ws_blk = (uint32_t)nb * p.KS * 128;
+    uint4 wv[NKW];
+    uint32_t wsv[NKW];
+#pragma unroll
+    for (int j = 0; j < NKW; ++j) {
+        const int ks = ks0 + j;
+        const bool live = ks < p.KS;   // (wavefront-uniform)
+        wv[j] = bload16(rwc, wc_lane, live ? wc_blk + (uint32_t)ks * 1024 : kDeadOffset);
+        wsv[j] = bload2(rws, ws_lane, live ? ws_blk + (uint32_t)ks * 128 : kDeadOffset);
+    }
+    const rsrc_t rcs = make_rsrc(p.cs, (uint64_t)p.n_pad * 4);
+    const float4v csv = __builtin_bit_cast(float4v, bload16(rcs, (uint32_t)(nb * 16 + kg * 4) * 4, 0));
+
+    // Activation operand: token r16's codes and scales for this wavefront's
+    // k-steps (whole offset per lane, scalar offset 0: tokens >= M and dead
+    // k-steps read zero).  Made in this launch, they are read past the L1.
+    uint4 xv[NKW];
+    uint32_t xsv[NKW];
+    auto load_x = [&](auto aux_tag) {
+        constexpr int aux = decltype(aux_tag)::value;
+        const rsrc_t rxc = make_rsrc(p.x_codes, (uint64_t)p.M * p.K / 2);
+        const rsrc_t rxs = make_rsrc(p.x_scales, (uint64_t)p.M * p.K / 16);
+        const bool row = r16 < p.M;
+        const uint32_t xc_row = (uint32_t)r16 * (uint32_t)(p.K / 2) + kg * 16;
+        const uint32_t xs_row = (uint32_t)r16 * (uint32_t)(p.K / 16) + kg * 2;
+#pragma unroll
+        for (int j = 0; j < NKW; ++j) {
+            const int ks = ks0 + j;
+            const bool live = row && ks < p.KS;
+            xv[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                   rxc, (int)(live ? xc_row + (uint32_t)ks * 64 : kOutOfBounds), 0,
+                                                   aux));
+            xsv[j] = (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(
+                rxs, (int)(live ? xs_row + (uint32_t)ks * 8 : kOutOfBounds), 0, aux);
+        }
+    };
+    if constexpr (!ENC) load_x(std::integral_constant<int, 0>{});
+
+    // Decode the weights as they arrive.
+    half8 a[NKW][4];
+#pragma unroll
+    for (int j = 0; j < NKW; ++j)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            a[j][c] = decode8(word_of(wv[j], c), scale_byte(wsv[j], c >> 1));
+            asm volatile("" : "+v"(a[j][c]));   // decode here, while waiting, not next to its use
+        }
+
+    float gx;
+    if constexpr (ENC) {
+        // Wait for this XCD's encoders (thread 0 polls the L2, the workgroup follows).
+        if (threadIdx.x == 0) {
+            const bool ok = xcd_ok && wait_flags(p.xw[xcd].ready_flag, tag, p.polls);
+            s_local = ok ? 0 : 1;
+        }
+        lds_barrier();
+        if (s_local) {
+            gx = encode_all_here<T>(p, s_red, rtab, nthreads);   // the same bytes the encoders would write
+        } else {
+            const rsrc_t rg = make_rsrc(p.g_x, 4);
+            gx = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rg, 0, 0, kPastL1));
+        }
+        load_x(std::integral_constant<int, kPastL1>{});
+    } else {
+        gx = p.g_x[0];
+    }
+
+    // 16x16x32 products over this wavefront's k-steps, into two accumulators
+    // (chunks 0, 1 and 2, 3 of each k-step) so that consecutive instructions do
+    // not wait for each other's results.
+    float4v acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < NKW; ++j)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const half8 b = decode8(word_of(xv[j], c), scale_byte(xsv[j], c >> 1));
+            if (c & 1) acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[j][c], b, acc1, 0, 0, 0);
+            else acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[j][c], b, acc0, 0, 0, 0);
+        }
+    const float4v acc = acc0 + acc1;
+
+    // Partial tiles summed in wavefront order.  Lane holds rows 4kg..4kg+3 of
+    // the block for token r16.
+    red[wave][lane] = acc;
+    lds_barrier();
+    if (wave != 0) return;
+    const int nw = nthreads >> 6;
+    float4v sum = red[0][lane];
+    for (int w = 1; w < nw; ++w) sum += red[w][lane];
+    const int64_t n_base = (int64_t)nb * 16 + kg * 4;
+    bool gated = false;   // only the row blocks that hold gate columns take the gated stores
+    if constexpr (EPI) gated = gates_touch((int64_t)nb * 16, (int64_t)nb * 16 + 16, p.gp);
+    if (r16 >= p.M) return;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int64_t n = n_base + r;
-        if (r16 < M && n < N) {
+        if (n < p.N) {
             float v = sum[r] * (gx * csv[r]);
-            if (EPI && gated) v = gate(v, n, gp);
-            if constexpr (EPI)
-                    store_y(y, (int64_t)r16 * ld_y + n, v, gp);
-                else
-                    y[(int64_t)r16 * ld_y + n] = v;
+            if constexpr (EPI) {
+                if (gated) v = gate(v, n, p.gp);
+                store_y(p.y, (int64_t)r16 * p.ld_y + n, v, p.gp);
+            } else {
+                p.y[(int64_t)r16 * p.ld_y + n] = v;
+            }
         }
-    }
-    const v4i zero = {0, 0, 0, 0};
-#pragma unroll
-    for (int t = 0; t < kMaxSlices; ++t) {
-        if (t < S && t != slice)
-            __builtin_amdgcn_raw_buffer_store_b128(zero, rpart, (int)poff, (int)((grp * S + t) * kTile),
-                                                   kWriteThrough);
     }
 }
 
@@ -402,131 +454,62 @@ __global__ __launch_bounds__(R * 64) void skinny_kernel(
 namespace {
 
 struct SkinnyPlan {
-    int R = 0, nksl = 0, S = 0;
-    int64_t groups = 0;
-    bool ok() const { return R > 0; }
-    int64_t workgroups() const { return groups * S; }
+    int waves = 0, nkw = 0;
+    bool ok() const { return waves > 0; }
 };
 
-const int kROptions[] = {4, 5, 8};
-const int kNkslOptions[] = {16, 10, 8, 5, 4, 2, 1};
-
-// The split whose workgroups spread most evenly over the compute units (each
-// unit's share of the weight stream sets its finishing time); ties go to fewer
-// slices (less to sum) and then to longer slices.
+// kWaves wavefronts (fewer when K has fewer k-steps), each with ceil(KS / waves) k-steps.
 SkinnyPlan plan_for(const nvfp4_weight_desc& d) {
-    SkinnyPlan best;
-    double best_eff = -1.0;
-    const int KS = (int)(d.k / kPackK);
-    const int64_t blocks = d.n_padded / kPackRows;
-    for (int R : kROptions) {
-        if (blocks % R != 0) continue;
-        for (int nksl : kNkslOptions) {
-            if (KS % nksl != 0 || KS / nksl > kMaxSlices) continue;
-            SkinnyPlan p;
-            p.R = R;
-            p.nksl = nksl;
-            p.S = KS / nksl;
-            p.groups = blocks / R;
-            const int64_t wgs = p.workgroups();
-            const int64_t rounds = (wgs + kComputeUnits - 1) / kComputeUnits;
-            const double eff = (double)wgs / (double)(rounds * kComputeUnits);
-            const bool better = eff > best_eff + 1e-9 ||
-                                (eff > best_eff - 1e-9 && (p.S < best.S || (p.S == best.S && nksl > best.nksl)));
-            if (better) {
-                best = p;
-                best_eff = eff;
-            }
-        }
-    }
-    return best;
+    SkinnyPlan p;
+    const int64_t KS = d.k / kPackK;
+    if (KS < 1 || KS > (int64_t)kWaves * kMaxNkw) return p;
+    p.waves = (int)(KS < kWaves ? KS : kWaves);
+    p.nkw = (int)((KS + p.waves - 1) / p.waves);
+    return p;
 }
 
-struct SkinnyArgs {
-    int M;
-    int64_t K;
-    const void* x;
-    int64_t ld_x;
-    float* g_x;
-    int g_given;
-    uint8_t* x_codes;
-    uint8_t* x_scales;
-    const uint8_t* wc;
-    const uint8_t* wsc;
-    const float* cs;
-    int64_t N, n_pad;
-    float* y;
-    int64_t ld_y;
-    uint32_t* counters;
-    uint32_t* slots;
-    float* partials;
-    int S;
-    int amax_polls;
-    Epilogue gp;
-    bool epi;
-};
-
-template <typename T, int NKSL, int R, bool QUANT>
-void launch_one(dim3 grid, hipStream_t stream, const SkinnyArgs& a) {
-    constexpr bool kPre = QUANT && NKSL <= kMaxPre / sizeof(T) * 2;
-    // the general epilogue (gates, bf16 output) only where asked for: the plain kernel keeps its registers
-    auto kern = a.epi ? skinny_kernel<T, NKSL, R, QUANT, kPre, true> : skinny_kernel<T, NKSL, R, QUANT, kPre, false>;
-    hipLaunchKernelGGL(kern, grid, dim3(R * 64), 0, stream, a.M, a.K, static_cast<const T*>(a.x), a.ld_x, a.g_x, a.g_given, a.x_codes, a.x_scales,
-                       a.wc, a.wsc, a.cs, a.N, a.n_pad, a.y, a.ld_y, a.counters, a.slots, a.partials, a.S,
-                       a.amax_polls, a.gp);
+template <typename T, int NKW, bool ENC>
+void launch_one(unsigned grid, int waves, hipStream_t stream, const SkinnyParams& a, bool epi) {
+    auto kern = epi ? skinny_kernel<T, NKW, ENC, true> : skinny_kernel<T, NKW, ENC, false>;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(waves * 64), 0, stream, a);
 }
 
-template <typename T, bool QUANT, int R>
-hipError_t launch_nksl(int nksl, dim3 grid, hipStream_t stream, const SkinnyArgs& a) {
-    switch (nksl) {
-        case 1: launch_one<T, 1, R, QUANT>(grid, stream, a); break;
-        case 2: launch_one<T, 2, R, QUANT>(grid, stream, a); break;
-        case 4: launch_one<T, 4, R, QUANT>(grid, stream, a); break;
-        case 5: launch_one<T, 5, R, QUANT>(grid, stream, a); break;
-        case 8: launch_one<T, 8, R, QUANT>(grid, stream, a); break;
-        case 10: launch_one<T, 10, R, QUANT>(grid, stream, a); break;
-        case 16: launch_one<T, 16, R, QUANT>(grid, stream, a); break;
+template <typename T, bool ENC>
+hipError_t launch_nkw(const SkinnyPlan& pl, unsigned grid, hipStream_t stream, const SkinnyParams& a, bool epi) {
+    switch (pl.nkw) {
+        case 1: launch_one<T, 1, ENC>(grid, pl.waves, stream, a, epi); break;
+        case 2: launch_one<T, 2, ENC>(grid, pl.waves, stream, a, epi); break;
+        case 3: launch_one<T, 3, ENC>(grid, pl.waves, stream, a, epi); break;
+        case 4: launch_one<T, 4, ENC>(grid, pl.waves, stream, a, epi); break;
+        case 5: launch_one<T, 5, ENC>(grid, pl.waves, stream, a, epi); break;
+        case 6: launch_one<T, 6, ENC>(grid, pl.waves, stream, a, epi); break;
+        case 7: launch_one<T, 7, ENC>(grid, pl.waves, stream, a, epi); break;
+        case 8: launch_one<T, 8, ENC>(grid, pl.waves, stream, a, epi); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
-template <typename T, bool QUANT>
-hipError_t launch_plan(const SkinnyPlan& p, hipStream_t stream, const SkinnyArgs& a) {
-    const dim3 grid((unsigned)p.workgroups());
-    switch (p.R) {
-        case 4: return launch_nksl<T, QUANT, 4>(p.nksl, grid, stream, a);
-        case 5: return launch_nksl<T, QUANT, 5>(p.nksl, grid, stream, a);
-        case 8: return launch_nksl<T, QUANT, 8>(p.nksl, grid, stream, a);
-        default: return hipErrorInvalidValue;
-    }
-}
-
-// Workspace: one ticket counter per group, S published slice maxima per group,
-// then one partial tile per workgroup.
-size_t counters_bytes(const SkinnyPlan& p) { return (size_t)((p.groups * (1 + p.S) * 4 + 255) / 256 * 256); }
-
 }  // namespace
 
 bool skinny_applies(int64_t M, const nvfp4_weight_desc& d) {
     if (M < 1 || M > kSkinnyM) return false;
-    return plan_for(d).ok();
+    const SkinnyPlan pl = plan_for(d);
+    // an encoder thread holds at most kEncBlocksPerThread blocks of its XCD share
+    return pl.ok() && (M * (d.k / 16) + kEncPerXcd - 1) / kEncPerXcd <= (int64_t)kEncBlocksPerThread * pl.waves * 64;
 }
 
-size_t skinny_workspace_bytes(const nvfp4_weight_desc& d) {
-    const SkinnyPlan p = plan_for(d);
-    if (!p.ok()) return 0;
-    return counters_bytes(p) + (size_t)p.workgroups() * (size_t)p.R * 64 * 16;
-}
+size_t skinny_workspace_bytes(const nvfp4_weight_desc& d) { return plan_for(d).ok() ? kSkinnyCounterBytes : 0; }
 
 hipError_t launch_skinny(int64_t M, const void* x, int in_dtype, int64_t ld_x, float* g_x, int g_mode,
                          uint8_t* x_codes, uint8_t* x_scales, bool quantize, const nvfp4_weight_desc& d, float* y,
                          int64_t ld_y, void* ws, const Epilogue& gp, hipStream_t stream) {
-    const SkinnyPlan p = plan_for(d);
-    if (!p.ok()) return hipErrorInvalidValue;
+    if (!skinny_applies(M, d)) return hipErrorInvalidValue;
+    const SkinnyPlan pl = plan_for(d);
     const uint8_t* blob = static_cast<const uint8_t*>(d.blob);
-    SkinnyArgs a;
+    SkinnyParams a;
     a.M = (int)M;
+    a.KS = (int)(d.k / kPackK);
     a.K = d.k;
     a.x = x;
     a.ld_x = ld_x;
@@ -541,17 +524,17 @@ hipError_t launch_skinny(int64_t M, const void* x, int in_dtype, int64_t ld_x, f
     a.n_pad = d.n_padded;
     a.y = y;
     a.ld_y = ld_y;
-    a.counters = static_cast<uint32_t*>(ws);
-    a.slots = a.counters + p.groups;
-    a.partials = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + counters_bytes(p));
-    a.S = p.S;
+    a.xw = static_cast<XcdWords*>(ws);
+    a.n_enc = quantize ? kXcds * kEncPerXcd : 0;
     a.gp = gp;
-    a.epi = gp.n_a > 0 || gp.n_b > 0 || gp.out_bf16;
-    a.amax_polls = kAmaxSpin;
-    if (const char* e = std::getenv("NVFP4_AMAX_POLLS")) a.amax_polls = std::atoi(e);   // testing the fallback
-    if (!quantize) return launch_plan<uint16_t, false>(p, stream, a);
-    if (in_dtype == NVFP4_IN_BF16) return launch_plan<uint16_t, true>(p, stream, a);
-    return launch_plan<float, true>(p, stream, a);
+    a.polls = kDefaultPolls;
+    if (const char* e = std::getenv("NVFP4_AMAX_POLLS")) a.polls = std::atoi(e);   // testing the local path
+    const bool epi = gp.n_a > 0 || gp.n_b > 0 || gp.out_bf16;
+    const unsigned blocks = (unsigned)((d.n + kPackRows - 1) / kPackRows);   // blocks holding real rows
+    if (!quantize) return launch_nkw<uint16_t, false>(pl, blocks, stream, a, epi);
+    const unsigned grid = blocks + (unsigned)a.n_enc;
+    if (in_dtype == NVFP4_IN_BF16) return launch_nkw<uint16_t, true>(pl, grid, stream, a, epi);
+    return launch_nkw<float, true>(pl, grid, stream, a, epi);
 }
 
 }  // namespace nvfp4

@@ -15,8 +15,12 @@ LIB = os.path.join(ROOT, "nvfp4_block_scaled_03_amd", "libnvfp4.so")
 
 
 def _ensure_built():
-    if not os.path.exists(LIB):
-        from nvfp4_block_scaled_03_amd import build as b
+    if not os.path.exists(LIB):   # build.py by path: the package refuses to import before the library exists
+        import importlib.util
+        spec = importlib.util.spec_from_file_location(
+            "_nvfp4_build", os.path.join(ROOT, "nvfp4_block_scaled_03_amd", "build.py"))
+        b = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(b)
         b.build()
 
 
@@ -270,7 +274,9 @@ def test_gemm_valid_stops_at_device_check_without_gpu():
 def test_linear_validation():
     d = make_desc(rows=(5120,), K=5120)
     need = nv.lib.nvfp4_linear_workspace_bytes(16, nv.NVFP4_IN_BF16, ctypes.byref(d))
-    assert need >= 4 * (d.n_padded // 64) + (d.n_padded // 64) * 256 * 16    # counters + one partial tile per group
+    # the one-launch path's per-XCD flags (8 x 256 bytes), then the two-launch path's amax partials
+    assert need == 2048 + nv.nvfp4_quantize_workspace_bytes(16, 5120)
+    assert nv.lib.nvfp4_gemm_workspace_bytes(16, ctypes.byref(d)) == 0      # the product alone needs none
 
     def call(**kw):
         a = dict(x=FAKE, dt=nv.NVFP4_IN_BF16, M=16, ld_x=5120, c=FAKE, s=FAKE, g=FAKE, mode=0, d=d, y=FAKE,

@@ -1,9 +1,9 @@
 """nvfp4_linear (quantize + GEMM in one call) against the oracle and against the two-call path.
 
-For few tokens the call is an amax pass plus one kernel that quantizes each K-slice of the
-activations and takes the split-K product; its codes, scales, g and Y must equal
-nvfp4_quantize followed by nvfp4_gemm bit for bit (the same k-slices, summed in the same
-slice order), and the oracle within the GEMM tolerance."""
+For few tokens the call is one kernel: its first workgroups encode the activations and the
+others multiply them as soon as the encoding is published; its codes, scales, g and Y must
+equal nvfp4_quantize followed by nvfp4_gemm bit for bit (the same product kernel and the
+same order of sums), and the oracle within the GEMM tolerance."""
 import numpy as np
 import pytest
 import torch
@@ -46,7 +46,12 @@ def test_decode_workload():
     _check(wl.x, "bf16", wl.w, "bf16", "decode")
 
 
-@pytest.mark.parametrize("M,K,N", [(1, 512, 64), (7, 2048, 300), (16, 1024, 512), (3, 8192, 128), (16, 640, 96)])
+@pytest.mark.parametrize("M,K,N", [(1, 512, 64), (7, 2048, 300), (16, 1024, 512), (3, 8192, 128), (16, 640, 96),
+                                   # k-steps that do not fill every wavefront (dead k-steps read zero): 23 over
+                                   # 8 x 3, 39 over 8 x 5; one wavefront per k-step below 8
+                                   (5, 2944, 200), (16, 4992, 5120), (2, 384, 33),
+                                   # K above the one-workgroup-per-row-block limit: quantize + tiled product
+                                   (9, 9216, 256)])
 def test_shapes(M, K, N):
     x = workloads.random_matrix(700 + M, M, K, dtype="bf16")
     w = workloads.random_matrix(800 + M, N, K, 0.05, dtype="bf16")
@@ -108,7 +113,7 @@ def test_graph_replays():
 
 def test_alternating_inputs_see_fresh_codes():
     """Consecutive calls with different activations into the same code buffers: every call must use its
-    own freshly encoded activations, and the split-K counters must be back at zero after each call."""
+    own freshly encoded activations, and the publication counters must be back at zero after each call."""
     wl = workloads.make_decode()
     say("linear alternating inputs")
     xs = [to_dev(wl.x, "bf16"), to_dev(workloads.random_matrix(1234, wl.M, wl.K, 3.0, dtype="bf16"), "bf16")]
@@ -128,8 +133,9 @@ def test_alternating_inputs_see_fresh_codes():
 
 @pytest.mark.parametrize("shape", ["decode", "3x2048x300"])
 def test_amax_fallback_when_peers_do_not_publish(shape, monkeypatch):
-    """The few-token kernel takes the global amax from the slice maxima its peer workgroups publish;
-    with a poll bound of zero every workgroup reduces all slices itself. Same bits either way."""
+    """The few-token kernel's product workgroups wait for the encoder workgroups to publish the
+    activations' encoding; with a poll bound of zero each of them encodes everything itself (the
+    same bytes). Same bits either way, and the counters still end at zero (calls=2)."""
     monkeypatch.setenv("NVFP4_AMAX_POLLS", "0")
     if shape == "decode":
         wl = workloads.make_decode()
@@ -164,3 +170,23 @@ def test_side_stream(M):
     y2, _, _, _ = nv.linear(xd, pw, g=1.0)
     torch.cuda.synchronize()
     assert torch.equal(y1h, y2)
+
+
+def test_workspace_shared_across_token_counts():
+    """One workspace for calls with many tokens (two launches: amax partials in the workspace) and few
+    tokens (one launch: counters in the workspace), interleaved: the partials never touch the counters,
+    so every call equals the same call with a fresh workspace."""
+    say("linear: one workspace for M = 300, 16, 40, 3, 16")
+    K, N = 1024, 320
+    w = workloads.random_matrix(1401, N, K, 0.05, dtype="bf16")
+    pw = nv.PackedWeight([nv.quantize(to_dev(w, "bf16"))], K)
+    shared = torch.zeros((nv.nvfp4_linear_workspace_bytes(300, nv.NVFP4_IN_BF16, pw.desc),), dtype=torch.uint8,
+                         device=DEV)
+    for i, M in enumerate([300, 16, 40, 3, 16]):
+        xd = to_dev(workloads.random_matrix(1410 + i, M, K, dtype="bf16"), "bf16")
+        assert nv.nvfp4_linear_workspace_bytes(M, nv.NVFP4_IN_BF16, pw.desc) <= shared.numel()
+        y, c, s, g = nv.linear(xd, pw, shared)
+        y2, c2, s2, g2 = nv.linear(xd, pw)          # fresh zeroed workspace
+        torch.cuda.synchronize()
+        assert torch.equal(c, c2) and torch.equal(s, s2) and torch.equal(g, g2), f"call {i} M={M}"
+        assert torch.equal(y, y2), f"call {i} M={M}"
