@@ -394,6 +394,28 @@ nvfp4_status nvfp4_linear(const void* x, int in_dtype, int64_t M, int64_t ld_x, 
                           int64_t ld_y, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * nvfp4_linear without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  Same arguments, results and bits as nvfp4_linear
+ * otherwise.
+ *
+ * The workspace nvfp4_linear would take (the few-token kernel's counters, then
+ * the quantizer's amax partials) is a static 16 KiB device array inside
+ * the library instead, which every shape fits (nvfp4_linear_workspace_bytes
+ * never exceeds it; a larger request would give NVFP4_ERR_UNSUPPORTED).  Each
+ * GPU holds its own copy until the process ends; the first call on a device
+ * looks its address up and clears it with a small kernel on `stream`.  The
+ * call itself allocates and frees nothing.
+ *
+ * Every call on one GPU shares that GPU's array: calls that may overlap on a
+ * GPU (other streams, other host threads) race on it and must be ordered by
+ * the caller.  Calls on one stream are ordered by the stream.
+ * ------------------------------------------------------------------------- */
+nvfp4_status nvfp4_linear_noalloc(const void* x, int in_dtype, int64_t M, int64_t ld_x, uint8_t* x_codes,
+                                  uint8_t* x_scales, float* g_x, int g_mode, const nvfp4_weight_desc* w, float* y,
+                                  int64_t ld_y, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Gate epilogue of a fused Gated DeltaNet input projection (anthology-of-the-
  * sota record theory-128, Kozyrev and Maiboroda 2026, section "The account",
  * its paragraph on the gates' parameterization: the state decay is

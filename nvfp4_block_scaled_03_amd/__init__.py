@@ -139,6 +139,8 @@ def _load():
         "nvfp4_gemm_workspace_bytes": (c_sz, [c_i64, ctypes.POINTER(WeightDesc)]),
         "nvfp4_gemm": (c_int, [c_i64, c_vp, c_vp, c_vp, ctypes.POINTER(WeightDesc), c_vp, c_i64, c_vp, c_sz, c_vp]),
         "nvfp4_linear_workspace_bytes": (c_sz, [c_i64, c_int, ctypes.POINTER(WeightDesc)]),
+        "nvfp4_linear_noalloc": (c_int, [c_vp, c_int, c_i64, c_i64, c_vp, c_vp, c_vp, c_int,
+                                         ctypes.POINTER(WeightDesc), c_vp, c_i64, c_vp]),
         "nvfp4_linear": (c_int, [c_vp, c_int, c_i64, c_i64, c_vp, c_vp, c_vp, c_int, ctypes.POINTER(WeightDesc), c_vp,
                                  c_i64, c_vp, c_sz, c_vp]),
         "nvfp4_gemm_gated": (c_int, [c_i64, c_vp, c_vp, c_vp, ctypes.POINTER(WeightDesc),
@@ -386,6 +388,19 @@ def nvfp4_linear(x, x_codes, x_scales, g_x, desc: WeightDesc, y, workspace, g_mo
         _check(_lib.nvfp4_linear_gated(_ptr(x), in_dtype, M, ld_x, _ptr(x_codes), _ptr(x_scales), _ptr(g_x), g_mode,
                                        ctypes.byref(desc), ctypes.byref(gates.desc), _ptr(y), ld_y, _ptr(workspace),
                                        ws_bytes, _stream(stream)))
+
+
+def nvfp4_linear_noalloc(x, x_codes, x_scales, g_x, desc: WeightDesc, y, g_mode=NVFP4_G_COMPUTE, stream=None, *,
+                         M=None, ld_x=None, in_dtype=None, ld_y=None):
+    """nvfp4_linear with the library's static scratch instead of a workspace (FP32 y, no gates)."""
+    if M is None:
+        M = x.shape[0]
+        ld_x = x.stride(0) if M > 1 else x.shape[1]
+        in_dtype = NVFP4_IN_BF16 if x.dtype == torch.bfloat16 else NVFP4_IN_F32
+    if ld_y is None:
+        ld_y = y.stride(0) if y.dim() == 2 and y.shape[0] > 1 else desc.n
+    _check(_lib.nvfp4_linear_noalloc(_ptr(x), in_dtype, M, ld_x, _ptr(x_codes), _ptr(x_scales), _ptr(g_x), g_mode,
+                                     ctypes.byref(desc), _ptr(y), ld_y, _stream(stream)))
 
 
 # ---------------------------------------------------------------------------

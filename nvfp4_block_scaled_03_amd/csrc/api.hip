@@ -2,6 +2,7 @@
 // any HIP call), descriptor construction, device check and kernel dispatch.
 #include <atomic>
 #include <cstdarg>
+#include <mutex>
 #include <cstdio>
 #include <cstring>
 #include <string>
@@ -105,6 +106,51 @@ nvfp4_status check_desc(const nvfp4_weight_desc* w) {
         if (ref.module_row_offset[s] != w->module_row_offset[s])
             return fail(NVFP4_ERR_DESCRIPTOR, "weight descriptor module offsets are inconsistent");
     if (w->blob == nullptr || !aligned(w->blob, 256)) return fail(NVFP4_ERR_DESCRIPTOR, "weight blob is NULL or not 256-byte aligned");
+    return NVFP4_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Scratch for nvfp4_linear_noalloc: the workspace of nvfp4_linear (the few-token
+// kernel's counters, then the quantizer's amax partials) in a device array
+// of the library, so that entry point allocates nothing.  Each GPU holds its own
+// copy; host code reaches it only through the address hipGetSymbolAddress
+// returns on that device (the array's name is a host-side stand-in).
+// ---------------------------------------------------------------------------
+constexpr size_t kNoAllocScratchBytes = 16384;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+__global__ void clear_scratch_kernel(uint32_t* p, int n) {
+    for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0u;
+}
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];   // per device, once set up
+
+// Device address of the current device's scratch, set up (address looked up,
+// contents cleared by a kernel on `stream`) on the first call on that device.
+nvfp4_status scratch_for_current_device(hipStream_t stream, void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        return fail(NVFP4_ERR_NO_DEVICE, "no usable HIP device for the static scratch");
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || ptr == nullptr) {
+            (void)hipGetLastError();
+            return fail(NVFP4_ERR_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                        hipGetErrorString(e));
+        }
+        hipLaunchKernelGGL(clear_scratch_kernel, dim3(1), dim3(256), 0, stream, static_cast<uint32_t*>(ptr),
+                           (int)(kNoAllocScratchBytes / 4));
+        e = hipGetLastError();
+        if (e != hipSuccess) return fail(NVFP4_ERR_HIP, "scratch clear launch: %s", hipGetErrorString(e));
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
     return NVFP4_OK;
 }
 
@@ -467,10 +513,12 @@ size_t nvfp4_linear_workspace_bytes(int64_t M, int in_dtype, const nvfp4_weight_
     return linear_counter_bytes(M, *w) + nvfp4_quantize_workspace_bytes(M, w->k);
 }
 
+// use_static: the workspace is the library's static scratch (nvfp4_linear_noalloc),
+// looked up after the arguments are validated and a device is present.
 static nvfp4_status linear_impl(const void* x, int in_dtype, int64_t M, int64_t ld_x, uint8_t* x_codes,
                                 uint8_t* x_scales, float* g_x, int g_mode, const nvfp4_weight_desc* w,
                                 const nvfp4::Epilogue& gp, void* y_out, int64_t ld_y, void* workspace,
-                                size_t workspace_bytes, void* stream) {
+                                size_t workspace_bytes, void* stream, bool use_static = false) {
     float* y = static_cast<float*>(y_out);   // bf16 storage when gp.out_bf16 (the kernels store through store_y)
     nvfp4_status st = check_desc(w);
     if (st != NVFP4_OK) return st;
@@ -497,13 +545,23 @@ static nvfp4_status linear_impl(const void* x, int in_dtype, int64_t M, int64_t 
             return fail(NVFP4_ERR_UNSUPPORTED, "x_codes must be 16-byte, x_scales 4-byte and y element aligned");
     }
     const size_t need = nvfp4_linear_workspace_bytes(M, in_dtype, w);
-    if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256))) {
+    if (use_static) {
+        if (need > kNoAllocScratchBytes)
+            return fail(NVFP4_ERR_UNSUPPORTED, "nvfp4_linear_noalloc: this shape needs %zu bytes of scratch, above "
+                        "the library's static %zu bytes; use nvfp4_linear with a workspace", need,
+                        kNoAllocScratchBytes);
+    } else if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256))) {
         return fail(NVFP4_ERR_WORKSPACE, "linear workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
                     workspace_bytes);
     }
     st = check_device();
     if (st != NVFP4_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (use_static) {
+        st = scratch_for_current_device(s, &workspace);
+        if (st != NVFP4_OK) return st;
+        workspace_bytes = kNoAllocScratchBytes;
+    }
     uint8_t* wsb = static_cast<uint8_t*>(workspace);
     // the fused few-token kernel addresses the activations with 32-bit offsets
     const int64_t esize = in_dtype == NVFP4_IN_BF16 ? 2 : 4;
@@ -530,6 +588,13 @@ nvfp4_status nvfp4_linear(const void* x, int in_dtype, int64_t M, int64_t ld_x, 
                           void* workspace, size_t workspace_bytes, void* stream) {
     return linear_impl(x, in_dtype, M, ld_x, x_codes, x_scales, g_x, g_mode, w, nvfp4::Epilogue{}, y, ld_y,
                        workspace, workspace_bytes, stream);
+}
+
+nvfp4_status nvfp4_linear_noalloc(const void* x, int in_dtype, int64_t M, int64_t ld_x, uint8_t* x_codes,
+                                  uint8_t* x_scales, float* g_x, int g_mode, const nvfp4_weight_desc* w, float* y,
+                                  int64_t ld_y, void* stream) {
+    return linear_impl(x, in_dtype, M, ld_x, x_codes, x_scales, g_x, g_mode, w, nvfp4::Epilogue{}, y, ld_y, nullptr,
+                       0, stream, true);
 }
 
 // Epilogue descriptor -> the kernels' form.

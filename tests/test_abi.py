@@ -417,3 +417,33 @@ def test_pack_weights_train_validation():
     if _no_gpu():
         assert pt() == nv.NVFP4_ERR_NO_DEVICE
         assert pt(ws=None, wsb=0, g_mode=nv.NVFP4_G_GIVEN, ld=390, w=FAKE + 2) == nv.NVFP4_ERR_NO_DEVICE
+
+
+def test_linear_noalloc_validation():
+    """The allocation-free layer call validates like nvfp4_linear (no workspace argument to check) and, with
+    no GPU, stops at the device check before it looks up or touches its static scratch."""
+    d = make_desc(rows=(5120,), K=5120)
+
+    def call(**kw):
+        a = dict(x=FAKE, dt=nv.NVFP4_IN_BF16, M=16, ld_x=5120, c=FAKE, s=FAKE, g=FAKE, mode=0, d=d, y=FAKE,
+                 ld_y=5120)
+        a.update(kw)
+        return nv.lib.nvfp4_linear_noalloc(a["x"], a["dt"], a["M"], a["ld_x"], a["c"], a["s"], a["g"], a["mode"],
+                                           ctypes.byref(a["d"]) if a["d"] is not None else None, a["y"],
+                                           a["ld_y"], None)
+    assert call(d=None) == nv.NVFP4_ERR_INVALID_ARG
+    assert call(dt=5) == nv.NVFP4_ERR_INVALID_ARG
+    assert call(mode=9) == nv.NVFP4_ERR_INVALID_ARG
+    assert call(M=-1) == nv.NVFP4_ERR_SHAPE
+    assert call(ld_x=100) == nv.NVFP4_ERR_SHAPE
+    assert call(ld_y=100) == nv.NVFP4_ERR_SHAPE
+    assert call(y=None) == nv.NVFP4_ERR_INVALID_ARG
+    assert call(x=FAKE + 8) == nv.NVFP4_ERR_UNSUPPORTED
+    # every shape's workspace fits the static scratch (16 KiB), counters first for every M
+    assert nv.lib.nvfp4_linear_workspace_bytes(300, nv.NVFP4_IN_BF16, ctypes.byref(d)) == \
+        2048 + nv.nvfp4_quantize_workspace_bytes(300, 5120)
+    for M, K in [(16, 5120), (1, 128), (32768, 16384), (300, 8192), (4096, 5120)]:
+        dd = make_desc(rows=(256,), K=K)
+        assert nv.lib.nvfp4_linear_workspace_bytes(M, nv.NVFP4_IN_F32, ctypes.byref(dd)) <= 16384
+    if _no_gpu():
+        assert call() == nv.NVFP4_ERR_NO_DEVICE
