@@ -20,7 +20,9 @@ from typing import Sequence
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libnvfp4.so")
+# The library next to this file; NVFP4_LIBRARY names another build of the same sources (an instrumented
+# build of the host code, say).
+LIB_PATH = os.environ.get("NVFP4_LIBRARY") or os.path.join(_HERE, "libnvfp4.so")
 
 NVFP4_OK = 0
 NVFP4_ERR_INVALID_ARG = 1

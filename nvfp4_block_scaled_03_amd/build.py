@@ -34,10 +34,6 @@ FLAGS = [
     "-ffp-contract=off",
     # no packed FP32 instructions anywhere
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # the few-token kernel draws its ticket with a single-lane atomic whose result is read
-    # only at the end; the atomic optimizer would widen it and wait for it (and every load
-    # issued before it) on the spot
-    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wall",
 ]
 

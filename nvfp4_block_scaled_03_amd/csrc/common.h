@@ -40,9 +40,11 @@ constexpr int kMaxAmaxPartials = 1024;   // upper bound of quantize_partials_cou
 // Encodings (IEEE FP32 decisions, no fused operations).
 // ---------------------------------------------------------------------------
 
-// Non-negative finite u -> E4M3 byte, nearest value, ties to even, saturating at 448.
+// Non-negative u -> E4M3 byte, nearest value, ties to even, saturating at 448.
+// Infinity (a block amax times a caller's very large 1/g) and the NaN that
+// div6 makes of it saturate too.
 __device__ __forceinline__ uint32_t e4m3_rne_sat(float u) {
-    if (u >= kE4M3Max) return 0x7Eu;
+    if (!(u < kE4M3Max)) return 0x7Eu;
     if (u < 0.015625f) {                              // below 2^-6: subnormal grid m * 2^-9
         return (uint32_t)__builtin_rintf(u * 512.0f); // exact scaling, RNE to 0..8 (8 = 2^-6)
     }

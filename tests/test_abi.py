@@ -11,7 +11,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "nvfp4.h")
-LIB = os.path.join(ROOT, "nvfp4_block_scaled_03_amd", "libnvfp4.so")
+LIB = os.environ.get("NVFP4_LIBRARY") or os.path.join(ROOT, "nvfp4_block_scaled_03_amd", "libnvfp4.so")
 
 
 def _ensure_built():
