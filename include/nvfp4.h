@@ -381,12 +381,19 @@ nvfp4_status nvfp4_gemm(int64_t M, const uint8_t* a_codes, const uint8_t* a_scal
  *                         input in NVFP4_G_GIVEN mode), as for nvfp4_quantize
  * w, y, ld_y            : as for nvfp4_gemm
  * workspace             : device, >= nvfp4_linear_workspace_bytes(M, in_dtype, w)
- *                         bytes (at most 2048 + 4096), 256-byte aligned.  Its
- *                         first 2048 bytes hold the few-token path's flags
+ *                         bytes (at most 2048 + 73728 + 4096), 256-byte aligned.
+ *                         Its first 2048 bytes hold the few-token path's flags
  *                         (tagged with the launch, so no call needs them reset):
- *                         zero before the first use; the rest needs no
- *                         initialisation.  Calls that may run concurrently
- *                         must not share a workspace.
+ *                         zero before the first use.  Then, for weights with
+ *                         K <= 8192, K/128 * 1152 bytes (rounded up to 256) where
+ *                         the few-token kernel's encoders leave a second copy of
+ *                         the activation encoding in the order its products read
+ *                         (per 128-element k-step the 16 token slots' code bytes,
+ *                         then their scale bytes); then the amax partials of the
+ *                         two-launch path.  Both need no initialisation.  The
+ *                         sizes do not depend on M, so one workspace serves any
+ *                         token count.  Calls that may run concurrently must not
+ *                         share a workspace.
  * ------------------------------------------------------------------------- */
 size_t nvfp4_linear_workspace_bytes(int64_t M, int in_dtype, const nvfp4_weight_desc* w);
 nvfp4_status nvfp4_linear(const void* x, int in_dtype, int64_t M, int64_t ld_x, uint8_t* x_codes,
@@ -399,8 +406,8 @@ nvfp4_status nvfp4_linear(const void* x, int in_dtype, int64_t M, int64_t ld_x, 
  * that forbid allocation.  Same arguments, results and bits as nvfp4_linear
  * otherwise.
  *
- * The workspace nvfp4_linear would take (the few-token kernel's counters, then
- * the quantizer's amax partials) is a static 16 KiB device array inside
+ * The workspace nvfp4_linear would take (the few-token kernel's flags and
+ * activation copy, then the quantizer's amax partials) is a static 80 KiB device array inside
  * the library instead, which every shape fits (nvfp4_linear_workspace_bytes
  * never exceeds it; a larger request would give NVFP4_ERR_UNSUPPORTED).  Each
  * GPU holds its own copy until the process ends; the first call on a device

@@ -1,5 +1,6 @@
 // Host side of the C ABI declared in include/nvfp4.h: argument validation (before
 // any HIP call), descriptor construction, device check and kernel dispatch.
+#include <algorithm>
 #include <atomic>
 #include <cstdarg>
 #include <mutex>
@@ -116,7 +117,7 @@ nvfp4_status check_desc(const nvfp4_weight_desc* w) {
 // copy; host code reaches it only through the address hipGetSymbolAddress
 // returns on that device (the array's name is a host-side stand-in).
 // ---------------------------------------------------------------------------
-constexpr size_t kNoAllocScratchBytes = 16384;
+constexpr size_t kNoAllocScratchBytes = 81920;   // every shape's workspace fits (at most 2048 + 73728 + 4096)
 static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
 
 __global__ void clear_scratch_kernel(uint32_t* p, int n) {
@@ -505,7 +506,12 @@ nvfp4_status nvfp4_gemm_gated(int64_t M, const uint8_t* a_codes, const uint8_t* 
 // The counters of the one-launch few-token path come first, reserved for every
 // M, so that the amax partials of the two-launch path (quantize, then the
 // product) never land on them: one workspace may serve calls with any M.
-static size_t linear_counter_bytes(int64_t, const nvfp4_weight_desc&) { return nvfp4::kSkinnyCounterBytes; }
+// The few-token kernel's part of the workspace (flags, then its copy of the
+// activation encoding), reserved whatever M is, so that one workspace serves
+// calls with any token count; the quantizer's partial maxima follow it.
+static size_t linear_counter_bytes(int64_t, const nvfp4_weight_desc& w) {
+    return std::max(nvfp4::kSkinnyCounterBytes, nvfp4::skinny_workspace_bytes(w));
+}
 
 size_t nvfp4_linear_workspace_bytes(int64_t M, int in_dtype, const nvfp4_weight_desc* w) {
     if (w == nullptr || M < 0 || w->k <= 0 || w->n_padded <= 0) return 0;

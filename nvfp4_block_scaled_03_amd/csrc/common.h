@@ -95,6 +95,27 @@ __device__ __forceinline__ void load8(const uint16_t* p, float v[8]) {
         v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
     }
 }
+// The same as streaming loads (nontemporal: the lines are not kept in the
+// caches), for passes that read each byte once.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load16_stream(const void* p) {
+    const u32x4_t q = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(q.x, q.y, q.z, q.w);
+}
+__device__ __forceinline__ void load8_stream(const uint16_t* p, float v[8]) {
+    const uint4 u = load16_stream(p);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(w[i] << 16);
+        v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+}
+__device__ __forceinline__ void load8_stream(const float* p, float v[8]) {
+    const uint4 a = load16_stream(p), b = load16_stream(p + 4);
+    v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y); v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
+    v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y); v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
+}
 __device__ __forceinline__ void load8(const float* p, float v[8]) {
     float4 a = *reinterpret_cast<const float4*>(p);
     float4 b = *reinterpret_cast<const float4*>(p + 4);

@@ -156,6 +156,7 @@ struct SkinnyParams {
     float* y;
     int64_t ld_y;
     XcdWords* xw;            // workspace: one XcdWords per XCD (nvfp4_linear)
+    uint8_t* xf;             // workspace: the encoding again, in the product's order (nvfp4_linear)
     int n_enc;               // encoder workgroups (kXcds * kEncPerXcd, or 0)
     int polls;
     Epilogue gp;
@@ -211,6 +212,11 @@ __device__ __forceinline__ void encode_store_block(const SkinnyParams& p, const 
     encode_block(v, block_amax(v), s_enc, rtab, lo, hi, S);
     *reinterpret_cast<uint2*>(p.x_codes + (size_t)b * 8) = make_uint2(lo, hi);
     p.x_scales[b] = (uint8_t)S;
+    // product order: block kb of token t goes to k-step kb / 8, slot kb % 8 of that token's 64 bytes
+    const uint32_t kb_per_row = (uint32_t)(p.K / 16), t = b / kb_per_row, kb = b - t * kb_per_row;
+    const uint32_t ks = kb >> 3, j = kb & 7;
+    *reinterpret_cast<uint2*>(p.xf + ks * 1024 + t * 64 + j * 8) = make_uint2(lo, hi);
+    p.xf[(uint32_t)p.KS * 1024 + ks * 128 + t * 8 + j] = (uint8_t)S;
 }
 
 // The whole encoding by one workgroup (the local path): max|x| over the
@@ -357,22 +363,39 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_kernel(SkinnyParams p) {
     // k-steps read zero).  Made in this launch, they are read past the L1.
     uint4 xv[NKW];
     uint32_t xsv[NKW];
+    // nvfp4_gemm reads the canonical encoding (token t's row at t * K/2), where
+    // one load touches 16 rows; the fused kernel reads the product-order copy
+    // its encoders wrote (k-step ks: the 16 tokens' 64 code bytes in 1 KB, then
+    // their 8 scale bytes in 128 B), where it touches one contiguous span.
     auto load_x = [&](auto aux_tag) {
         constexpr int aux = decltype(aux_tag)::value;
-        const rsrc_t rxc = make_rsrc(p.x_codes, (uint64_t)p.M * p.K / 2);
-        const rsrc_t rxs = make_rsrc(p.x_scales, (uint64_t)p.M * p.K / 16);
         const bool row = r16 < p.M;
-        const uint32_t xc_row = (uint32_t)r16 * (uint32_t)(p.K / 2) + kg * 16;
-        const uint32_t xs_row = (uint32_t)r16 * (uint32_t)(p.K / 16) + kg * 2;
+        rsrc_t rxc, rxs;
+        uint32_t xc_row, xs_row, xc_ks, xs_ks;
+        if constexpr (ENC) {
+            rxc = make_rsrc(p.xf, (uint64_t)p.KS * 1024);
+            rxs = make_rsrc(p.xf + (size_t)p.KS * 1024, (uint64_t)p.KS * 128);
+            xc_row = (uint32_t)r16 * 64 + kg * 16;
+            xs_row = (uint32_t)r16 * 8 + kg * 2;
+            xc_ks = 1024;
+            xs_ks = 128;
+        } else {
+            rxc = make_rsrc(p.x_codes, (uint64_t)p.M * p.K / 2);
+            rxs = make_rsrc(p.x_scales, (uint64_t)p.M * p.K / 16);
+            xc_row = (uint32_t)r16 * (uint32_t)(p.K / 2) + kg * 16;
+            xs_row = (uint32_t)r16 * (uint32_t)(p.K / 16) + kg * 2;
+            xc_ks = 64;
+            xs_ks = 8;
+        }
 #pragma unroll
         for (int j = 0; j < NKW; ++j) {
             const int ks = ks0 + j;
             const bool live = row && ks < p.KS;
             xv[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                   rxc, (int)(live ? xc_row + (uint32_t)ks * 64 : kOutOfBounds), 0,
+                                                   rxc, (int)(live ? xc_row + (uint32_t)ks * xc_ks : kOutOfBounds), 0,
                                                    aux));
             xsv[j] = (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(
-                rxs, (int)(live ? xs_row + (uint32_t)ks * 8 : kOutOfBounds), 0, aux);
+                rxs, (int)(live ? xs_row + (uint32_t)ks * xs_ks : kOutOfBounds), 0, aux);
         }
     };
     if constexpr (!ENC) load_x(std::integral_constant<int, 0>{});
@@ -499,7 +522,12 @@ bool skinny_applies(int64_t M, const nvfp4_weight_desc& d) {
     return pl.ok() && (M * (d.k / 16) + kEncPerXcd - 1) / kEncPerXcd <= (int64_t)kEncBlocksPerThread * pl.waves * 64;
 }
 
-size_t skinny_workspace_bytes(const nvfp4_weight_desc& d) { return plan_for(d).ok() ? kSkinnyCounterBytes : 0; }
+// The flags, then the product-order copy of the activation encoding (16 token
+// slots per k-step: 1 KB of codes and 128 B of scales).
+static size_t product_order_bytes(const nvfp4_weight_desc& d) { return (size_t)(d.k / kPackK) * 1152; }
+size_t skinny_workspace_bytes(const nvfp4_weight_desc& d) {
+    return plan_for(d).ok() ? kSkinnyCounterBytes + (product_order_bytes(d) + 255) / 256 * 256 : 0;
+}
 
 hipError_t launch_skinny(int64_t M, const void* x, int in_dtype, int64_t ld_x, float* g_x, int g_mode,
                          uint8_t* x_codes, uint8_t* x_scales, bool quantize, const nvfp4_weight_desc& d, float* y,
@@ -525,6 +553,7 @@ hipError_t launch_skinny(int64_t M, const void* x, int in_dtype, int64_t ld_x, f
     a.y = y;
     a.ld_y = ld_y;
     a.xw = static_cast<XcdWords*>(ws);
+    a.xf = quantize ? static_cast<uint8_t*>(ws) + kSkinnyCounterBytes : nullptr;
     a.n_enc = quantize ? kXcds * kEncPerXcd : 0;
     a.gp = gp;
     a.polls = kDefaultPolls;

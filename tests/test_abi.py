@@ -274,8 +274,9 @@ def test_gemm_valid_stops_at_device_check_without_gpu():
 def test_linear_validation():
     d = make_desc(rows=(5120,), K=5120)
     need = nv.lib.nvfp4_linear_workspace_bytes(16, nv.NVFP4_IN_BF16, ctypes.byref(d))
-    # the one-launch path's per-XCD flags (8 x 256 bytes), then the two-launch path's amax partials
-    assert need == 2048 + nv.nvfp4_quantize_workspace_bytes(16, 5120)
+    # the one-launch path's per-XCD flags (8 x 256 bytes) and its product-order copy of the activation
+    # encoding (40 k-steps x 1152 bytes, rounded to 256), then the two-launch path's amax partials
+    assert need == 2048 + 46080 + nv.nvfp4_quantize_workspace_bytes(16, 5120)
     assert nv.lib.nvfp4_gemm_workspace_bytes(16, ctypes.byref(d)) == 0      # the product alone needs none
 
     def call(**kw):
@@ -439,11 +440,11 @@ def test_linear_noalloc_validation():
     assert call(ld_y=100) == nv.NVFP4_ERR_SHAPE
     assert call(y=None) == nv.NVFP4_ERR_INVALID_ARG
     assert call(x=FAKE + 8) == nv.NVFP4_ERR_UNSUPPORTED
-    # every shape's workspace fits the static scratch (16 KiB), counters first for every M
+    # every shape's workspace fits the static scratch (80 KiB), the few-token part first for every M
     assert nv.lib.nvfp4_linear_workspace_bytes(300, nv.NVFP4_IN_BF16, ctypes.byref(d)) == \
-        2048 + nv.nvfp4_quantize_workspace_bytes(300, 5120)
-    for M, K in [(16, 5120), (1, 128), (32768, 16384), (300, 8192), (4096, 5120)]:
+        2048 + 46080 + nv.nvfp4_quantize_workspace_bytes(300, 5120)
+    for M, K in [(16, 5120), (1, 128), (32768, 16384), (300, 8192), (4096, 5120), (16, 8192), (16, 8320)]:
         dd = make_desc(rows=(256,), K=K)
-        assert nv.lib.nvfp4_linear_workspace_bytes(M, nv.NVFP4_IN_F32, ctypes.byref(dd)) <= 16384
+        assert nv.lib.nvfp4_linear_workspace_bytes(M, nv.NVFP4_IN_F32, ctypes.byref(dd)) <= 81920
     if _no_gpu():
         assert call() == nv.NVFP4_ERR_NO_DEVICE
