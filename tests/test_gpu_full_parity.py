@@ -64,6 +64,7 @@ def assert_every_byte(codes, scales, g, x, what):
                                  f"gpu 0x{c[r0 + r, j]:02x} oracle 0x{q.codes[r, j]:02x}")
 
 
+@pytest.mark.timeout(300)
 @pytest.mark.parametrize("name", ["gdn", "ngpt", "large"])
 def test_workload_every_byte(name):
     """All operands of the workload, quantized whole on the device, against the oracle byte for byte."""
@@ -81,6 +82,7 @@ def test_workload_every_byte(name):
         del c, s, g
 
 
+@pytest.mark.timeout(300)
 def test_large_dense_slab():
     """The large layer (32768 x 16384 by 16384 x 16384) in the timed launch configuration (one workspace,
     the layer call); 256 whole output rows, every column, against the FP64 oracle product of the oracle's
