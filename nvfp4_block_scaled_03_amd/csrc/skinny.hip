@@ -19,18 +19,20 @@
 // Encoding inside one XCD.  Each XCD has its own L2, and a hand-over between
 // workgroups of one XCD goes through that L2 (a few hundred ns), while one
 // between XCDs goes to memory (microseconds under a full weight stream).  So
-// every XCD encodes the activations itself, into the same canonical buffer
-// (the bytes are the same whoever writes them), and its product workgroups
-// wait only for their own XCD's encoders:
+// every XCD encodes the activations itself, into a copy in the product's
+// order in the workspace (the bytes are the same whoever writes them), and its
+// product workgroups wait only for their own XCD's encoders:
 //   - workgroups 0 .. 8E-1 are encoders: workgroup i encodes share i / 8 for
 //     the XCD it runs on (the hardware hands out workgroups round-robin over
 //     the XCDs, from an XCD that depends on earlier launches, so any 8
 //     consecutive workgroups cover the 8 XCDs once each);
 //   - the E encoders of an XCD each reduce max|x| over 1/E of the tensor and
 //     exchange the partial maxima through the L2 (or take the given g), then
-//     encode their 1/E of the 16-element blocks and raise their `ready` flag;
+//     encode their 1/E of the 16-element blocks into the product-order copy,
+//     raise their `ready` flag, and then write the same blocks into the
+//     canonical encoding, the call's output, off the products' path;
 //   - a product workgroup decodes its weights, waits for the E flags of its
-//     XCD and then loads the encoding past its L1.
+//     XCD and then loads the product-order copy past its L1.
 // Every workgroup reads the XCD it runs on from the XCC_ID hardware register.
 // One whose wait exceeds a bound (its XCD lacks an encoder share, if the
 // hand-out ever differs from the above) encodes all the blocks itself instead
@@ -201,28 +203,46 @@ __device__ __forceinline__ RawBlock<T> load_raw_block(const SkinnyParams& p, con
     return raw;
 }
 
-// Encode one raw block with the global scale's table and store its code bytes
-// and scale into the canonical encoding.
+// One encoded block: its 8 code bytes and its scale byte.
+struct CodedBlock {
+    uint32_t lo, hi, S;
+};
 template <typename T>
-__device__ __forceinline__ void encode_store_block(const SkinnyParams& p, const RawBlock<T>& raw, uint32_t b,
-                                                   float s_enc, const float* rtab) {
+__device__ __forceinline__ CodedBlock encode_raw_block(const RawBlock<T>& raw, float s_enc, const float* rtab) {
     float v[16];
     widen(raw, v);
-    uint32_t lo, hi, S;
-    encode_block(v, block_amax(v), s_enc, rtab, lo, hi, S);
-    *reinterpret_cast<uint2*>(p.x_codes + (size_t)b * 8) = make_uint2(lo, hi);
-    p.x_scales[b] = (uint8_t)S;
-    // product order: block kb of token t goes to k-step kb / 8, slot kb % 8 of that token's 64 bytes
+    CodedBlock c;
+    encode_block(v, block_amax(v), s_enc, rtab, c.lo, c.hi, c.S);
+    return c;
+}
+// Block b into the canonical encoding (the call's output).
+__device__ __forceinline__ void store_canonical(const SkinnyParams& p, uint32_t b, const CodedBlock& c) {
+    *reinterpret_cast<uint2*>(p.x_codes + (size_t)b * 8) = make_uint2(c.lo, c.hi);
+    p.x_scales[b] = (uint8_t)c.S;
+}
+// Block b into the product-order copy: block kb of token t goes to k-step
+// kb / 8, slot kb % 8 of that token's 64 code bytes (and 8 scale bytes).
+__device__ __forceinline__ void store_product_order(const SkinnyParams& p, uint32_t b, const CodedBlock& c) {
     const uint32_t kb_per_row = (uint32_t)(p.K / 16), t = b / kb_per_row, kb = b - t * kb_per_row;
     const uint32_t ks = kb >> 3, j = kb & 7;
-    *reinterpret_cast<uint2*>(p.xf + ks * 1024 + t * 64 + j * 8) = make_uint2(lo, hi);
-    p.xf[(uint32_t)p.KS * 1024 + ks * 128 + t * 8 + j] = (uint8_t)S;
+    *reinterpret_cast<uint2*>(p.xf + ks * 1024 + t * 64 + j * 8) = make_uint2(c.lo, c.hi);
+    p.xf[(uint32_t)p.KS * 1024 + ks * 128 + t * 8 + j] = (uint8_t)c.S;
+}
+
+// g from max|x| over the whole tensor, by one workgroup, one block in flight
+// per thread (the slow paths: they must not raise the kernel's registers above
+// those of the usual path).
+template <typename T>
+__device__ float g_here(const SkinnyParams& p, const rsrc_t& rx, uint32_t nblk, uint32_t* s_red, int nthreads) {
+    uint32_t m = 0;
+    for (uint32_t b = threadIdx.x; b < nblk; b += (uint32_t)nthreads)
+        m = max(m, raw_block_amax_bits<T>(load_raw_block<T>(p, rx, b, nblk)));
+    return global_scale_from_amax(__uint_as_float(wg_max_u32(m, s_red, nthreads >> 6)));
 }
 
 // The whole encoding by one workgroup (the local path): max|x| over the
-// tensor (unless g is given), then every block.  One block in flight per
-// thread: a slow path that must not raise the kernel's registers above those
-// of the usual path.  Every thread's stores are complete on return.
+// tensor (unless g is given), then every block.  Every thread's stores are
+// complete on return.
 template <typename T>
 __device__ float encode_all_here(const SkinnyParams& p, uint32_t* s_red, float* rtab, int nthreads) {
     const uint32_t nblk = (uint32_t)(p.M * (p.K / 16));
@@ -231,27 +251,28 @@ __device__ float encode_all_here(const SkinnyParams& p, uint32_t* s_red, float* 
     if (p.g_given) {
         g = p.g_x[0];
     } else {
-        uint32_t m = 0;
-        for (uint32_t b = threadIdx.x; b < nblk; b += (uint32_t)nthreads)
-            m = max(m, raw_block_amax_bits<T>(load_raw_block<T>(p, rx, b, nblk)));
-        g = global_scale_from_amax(__uint_as_float(wg_max_u32(m, s_red, nthreads >> 6)));
+        g = g_here<T>(p, rx, nblk, s_red, nthreads);
         if (threadIdx.x == 0) p.g_x[0] = g;
     }
     const float s_enc = 1.0f / g;
     fill_recip_table(rtab, s_enc, threadIdx.x, nthreads);
     lds_barrier();
     for (uint32_t b = threadIdx.x; b < nblk; b += (uint32_t)nthreads)
-        encode_store_block<T>(p, load_raw_block<T>(p, rx, b, nblk), b, s_enc, rtab);
+    {
+        const CodedBlock c = encode_raw_block<T>(load_raw_block<T>(p, rx, b, nblk), s_enc, rtab);
+        store_canonical(p, b, c);
+        store_product_order(p, b, c);
+    }
     __builtin_amdgcn_s_waitcnt(0);   // this thread's stores are done
     lds_barrier();
     return g;
 }
 
 // Encoder e of XCD `xw`: its 1/E of the blocks, held in registers from the
-// start; the XCD's amax from the E partial maxima (or the given g); then the
-// blocks, and its `ready` flag.  If the exchange does not complete within the
-// bound it stops without raising it (the XCD's product workgroups then encode
-// locally).
+// start; the XCD's amax from the E partial maxima (or the given g; or, if the
+// exchange does not complete within the bound, from the whole tensor read
+// here); then g and its blocks in the product's order, and its `ready` flag;
+// then its blocks in the canonical encoding.
 template <typename T>
 __device__ void run_encoder(const SkinnyParams& p, uint32_t e, XcdWords* xw, uint64_t tag, uint32_t* s_red,
                             float* rtab, float* s_g, int nthreads) {
@@ -294,19 +315,27 @@ __device__ void run_encoder(const SkinnyParams& p, uint32_t e, XcdWords* xw, uin
         }
     }
     lds_barrier();
-    const float g = *s_g;
-    if (g < 0.0f) return;   // no g: this encoder's `ready` flag stays down and its XCD's product workgroups
-                            // encode locally
+    float g = *s_g;
+    if (g < 0.0f) g = g_here<T>(p, rx, nblk, s_red, nthreads);   // (uniform: every thread read the same word)
+    // g for this XCD's product workgroups (they read it after the flags; every XCD writes the same value)
     if (!p.g_given && e == 0 && threadIdx.x == 0) p.g_x[0] = g;
     const float s_enc = 1.0f / g;
+    CodedBlock c[kEncBlocksPerThread];
 #pragma unroll
     for (int j = 0; j < kEncBlocksPerThread; ++j) {   // (r = s_enc / S divided per block: no table to fill)
         const uint32_t b = b0 + threadIdx.x + j * nthreads;
-        if (b < b1) encode_store_block<T>(p, raw[j], b, s_enc, nullptr);
+        c[j] = encode_raw_block<T>(raw[j], s_enc, nullptr);
+        if (b < b1) store_product_order(p, b, c[j]);
     }
-    __builtin_amdgcn_s_waitcnt(0);   // every thread's codes, scales (and g) are in the L2
+    __builtin_amdgcn_s_waitcnt(0);   // every thread's product-order blocks (and g) are in the L2
     lds_barrier();
     if (threadIdx.x == 0) raise_flag(&xw->ready_flag[e], tag);
+    // The call's output encoding, off the products' path (the same bytes from every XCD).
+#pragma unroll
+    for (int j = 0; j < kEncBlocksPerThread; ++j) {
+        const uint32_t b = b0 + threadIdx.x + j * nthreads;
+        if (b < b1) store_canonical(p, b, c[j]);
+    }
 }
 
 // ---------------------------------------------------------------------------
