@@ -161,6 +161,7 @@ struct SkinnyParams {
     uint8_t* xf;             // workspace: the encoding again, in the product's order (nvfp4_linear)
     int n_enc;               // encoder workgroups (kXcds * kEncPerXcd, or 0)
     int polls;
+    uint32_t kb_magic;       // ceil(2^32 / (K/16)): b / (K/16) = umulhi(b, kb_magic) for every block index b
     Epilogue gp;
 };
 
@@ -193,7 +194,7 @@ template <typename T>
 __device__ __forceinline__ RawBlock<T> load_raw_block(const SkinnyParams& p, const rsrc_t& rx, uint32_t b,
                                                       uint32_t nblk) {
     const uint32_t kb_per_row = (uint32_t)(p.K / 16);
-    const uint32_t t = b / kb_per_row, kb = b - t * kb_per_row;
+    const uint32_t t = __umulhi(b, p.kb_magic), kb = b - t * kb_per_row;
     const uint32_t off = b < nblk ? (uint32_t)((int64_t)t * p.ld_x * sizeof(T) + (int64_t)kb * 16 * sizeof(T))
                                   : kOutOfBounds;
     RawBlock<T> raw;
@@ -223,7 +224,7 @@ __device__ __forceinline__ void store_canonical(const SkinnyParams& p, uint32_t 
 // Block b into the product-order copy: block kb of token t goes to k-step
 // kb / 8, slot kb % 8 of that token's 64 code bytes (and 8 scale bytes).
 __device__ __forceinline__ void store_product_order(const SkinnyParams& p, uint32_t b, const CodedBlock& c) {
-    const uint32_t kb_per_row = (uint32_t)(p.K / 16), t = b / kb_per_row, kb = b - t * kb_per_row;
+    const uint32_t kb_per_row = (uint32_t)(p.K / 16), t = __umulhi(b, p.kb_magic), kb = b - t * kb_per_row;
     const uint32_t ks = kb >> 3, j = kb & 7;
     *reinterpret_cast<uint2*>(p.xf + ks * 1024 + t * 64 + j * 8) = make_uint2(c.lo, c.hi);
     p.xf[(uint32_t)p.KS * 1024 + ks * 128 + t * 8 + j] = (uint8_t)c.S;
@@ -320,11 +321,13 @@ __device__ void run_encoder(const SkinnyParams& p, uint32_t e, XcdWords* xw, uin
     // g for this XCD's product workgroups (they read it after the flags; every XCD writes the same value)
     if (!p.g_given && e == 0 && threadIdx.x == 0) p.g_x[0] = g;
     const float s_enc = 1.0f / g;
+    fill_recip_table(rtab, s_enc, threadIdx.x, nthreads);
+    lds_barrier();
     CodedBlock c[kEncBlocksPerThread];
 #pragma unroll
-    for (int j = 0; j < kEncBlocksPerThread; ++j) {   // (r = s_enc / S divided per block: no table to fill)
+    for (int j = 0; j < kEncBlocksPerThread; ++j) {
         const uint32_t b = b0 + threadIdx.x + j * nthreads;
-        c[j] = encode_raw_block<T>(raw[j], s_enc, nullptr);
+        c[j] = encode_raw_block<T>(raw[j], s_enc, rtab);
         if (b < b1) store_product_order(p, b, c[j]);
     }
     __builtin_amdgcn_s_waitcnt(0);   // every thread's product-order blocks (and g) are in the L2
@@ -586,6 +589,8 @@ hipError_t launch_skinny(int64_t M, const void* x, int in_dtype, int64_t ld_x, f
     a.n_enc = quantize ? kXcds * kEncPerXcd : 0;
     a.gp = gp;
     a.polls = kDefaultPolls;
+    // exact for b < 2^32 / (K/16) (ceil(2^32/d)*d - 2^32 < d): every block index here is below 2^17
+    a.kb_magic = (uint32_t)(((uint64_t(1) << 32) + (uint64_t)(d.k / 16) - 1) / (uint64_t)(d.k / 16));
     if (const char* e = std::getenv("NVFP4_AMAX_POLLS")) a.polls = std::atoi(e);   // testing the local path
     const bool epi = gp.n_a > 0 || gp.n_b > 0 || gp.out_bf16;
     const unsigned blocks = (unsigned)((d.n + kPackRows - 1) / kPackRows);   // blocks holding real rows
