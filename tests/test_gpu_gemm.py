@@ -302,3 +302,12 @@ def test_graph_replays_match_eager(name, M):
         assert torch.equal(y, want[0]) and torch.equal(codes, want[1]) and torch.equal(scales, want[2]) \
             and torch.equal(g, want[3]), f"replay {i} differs from eager"
         _ = (xd.float() * 2).sum().item()      # unrelated eager work between replays
+
+
+def test_odd_kstep_count_many_tokens():
+    """K = 9 k-steps of 128 with two thousand tokens: the 256 x 256 tiles read their activation scales by
+    aligned pairs of k-steps and need an even count, so this product runs on the smaller tiles (a ragged last
+    row tile too): every output within the oracle's bound."""
+    x = workloads.random_matrix(1401, 2000, 1152, dtype="bf16")
+    ws = [workloads.random_matrix(1402, 1024, 1152, 0.05, dtype="bf16")]
+    check_dense(x, "bf16", ws, "bf16", "odd k-step count, M=2000 K=1152 N=1024")
