@@ -31,8 +31,8 @@ namespace nvfp4 {
 //
 // Operands move global -> LDS by buffer loads that write LDS directly (no
 // register staging), into a four-stage ring: the loads of k-step ks+3 are
-// issued during k-step ks, between its first matrix instructions, so each has
-// two k-steps to arrive.  The
+// issued during the first half of k-step ks, between its matrix instructions,
+// so each has two k-steps to arrive.  The
 // wavefronts read their fragments one half k-step ahead (the second half of
 // ks while multiplying the first, the first half of ks+1 while multiplying the
 // second), and decode each 8-element chunk while the previous chunk's matrix
@@ -46,7 +46,11 @@ namespace nvfp4 {
 //   A scales [row block RB][lane 64][4]             block scales 4h..4h+3 of the row
 //   B scales [col block CB][lane 64][4]
 // so every fragment read is one ds_read_b128 (or b32) of a contiguous,
-// bank-conflict-free 1 KB (256 B) span.
+// bank-conflict-free 1 KB (256 B) span.  256 x 256 tiles hold their scales as
+//   A scales [row 256][16]   the row's scale bytes of the aligned k-step pair
+//   B scales [column 256][8]
+// instead (one 16-byte load per wavefront and operand; the 4-byte scale reads
+// then see 2- to 4-way bank conflicts, a few cycles per k-step).
 //
 // Workgroups are numbered so that the ones sharing an XCD (consecutive
 // hardware ids go round-robin over the 8 XCDs) work on a compact group of
