@@ -20,6 +20,7 @@
 // Reads past the end of a tensor return zero, which is how rows beyond M (a
 // ragged last tile) contribute nothing without any clamping.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 
@@ -477,22 +478,42 @@ __device__ __forceinline__ void store_tile_cols(const float16v (&acc)[TM][TN], i
             if (live[j]) gc[j] = gate_col(n, gp);
         }
     }
+    const int64_t m0 = (int64_t)tm * G::BM + wm * (TM * 32) + h * 4;
+    using Out = std::conditional_t<BF16, uint16_t, float>;
+    if ((int64_t)(tm + 1) * G::BM <= M && (int64_t)(tn + 1) * G::BN <= N) {
+        // Interior tile: no bounds to check.  One lane pointer; each row adds a
+        // uniform multiple of ld_y and the column blocks are immediate offsets.
+        // (rows 0..3, 8..11, 16..19, 24..27 of each 32-row block: the pointer steps one row, or five
+        // after every fourth)
+        Out* pr = reinterpret_cast<Out*>(y) + m0 * ld_y + n0;
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int64_t m = (int64_t)tm * G::BM + wm * (TM * 32) + i * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
-            if (m >= M) continue;
+            for (int r = 0; r < 16; ++r) {
 #pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                if (!live[j]) continue;
-                const int64_t n = n0 + j * 32;
-                float v = acc[i][j][r] * cs[j];
-                if constexpr (GATED) v = gate_apply(v, gc[j]);
-                if constexpr (BF16)
-                    reinterpret_cast<uint16_t*>(y)[m * ld_y + n] = f32_to_bf16_rne(v);
-                else
-                    y[m * ld_y + n] = v;
+                for (int j = 0; j < TN; ++j) {
+                    float v = acc[i][j][r] * cs[j];
+                    if constexpr (GATED) v = gate_apply(v, gc[j]);
+                    if constexpr (BF16) pr[j * 32] = f32_to_bf16_rne(v);
+                    else pr[j * 32] = v;
+                }
+                pr += (r & 3) == 3 ? 5 * ld_y : ld_y;
+            }
+    } else {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t m = m0 + i * 32 + (r >> 2) * 8 + (r & 3);
+                if (m >= M) continue;
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    if (!live[j]) continue;
+                    float v = acc[i][j][r] * cs[j];
+                    if constexpr (GATED) v = gate_apply(v, gc[j]);
+                    if constexpr (BF16) reinterpret_cast<Out*>(y)[m * ld_y + n0 + j * 32] = f32_to_bf16_rne(v);
+                    else reinterpret_cast<Out*>(y)[m * ld_y + n0 + j * 32] = v;
+                }
             }
         }
     }
