@@ -370,8 +370,9 @@ nvfp4_status nvfp4_gemm(int64_t M, const uint8_t* a_codes, const uint8_t* a_scal
  * eighth each, exchanged through that XCD's L2) and encode an eighth of the
  * blocks each, into a copy in the order the products read (in the workspace);
  * the product workgroups stream and decode their weight rows meanwhile, wait
- * for their own XCD's encoders and multiply.  The encoders then write the
- * same bytes into x_codes and x_scales, off that path.  A workgroup that runs on
+ * for their own XCD's encoders and multiply, and each writes its share of the
+ * 128-element k-steps of x_codes and x_scales from the operand it multiplied
+ * (every output byte once).  A workgroup that runs on
  * another XCD than its index is meant for, or whose wait exceeds a bound,
  * encodes the activations itself (the same bytes), so no result depends on
  * placement or on another workgroup being resident; the environment variable

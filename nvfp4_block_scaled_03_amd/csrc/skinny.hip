@@ -28,11 +28,13 @@
 //     consecutive workgroups cover the 8 XCDs once each);
 //   - the E encoders of an XCD each reduce max|x| over 1/E of the tensor and
 //     exchange the partial maxima through the L2 (or take the given g), then
-//     encode their 1/E of the 16-element blocks into the product-order copy,
-//     raise their `ready` flag, and then write the same blocks into the
-//     canonical encoding, the call's output, off the products' path;
+//     encode their 1/E of the 16-element blocks into the product-order copy
+//     and raise their `ready` flag;
 //   - a product workgroup decodes its weights, waits for the E flags of its
-//     XCD and then loads the product-order copy past its L1.
+//     XCD and then loads the product-order copy past its L1; after its
+//     products it writes its share of the k-steps (the product workgroups
+//     split them) of the canonical encoding, the call's output, from those
+//     registers, so each output byte is written once rather than once per XCD.
 // Every workgroup reads the XCD it runs on from the XCC_ID hardware register.
 // One whose wait exceeds a bound (its XCD lacks an encoder share, if the
 // hand-out ever differs from the above) encodes all the blocks itself instead
@@ -272,8 +274,7 @@ __device__ float encode_all_here(const SkinnyParams& p, uint32_t* s_red, float* 
 // Encoder e of XCD `xw`: its 1/E of the blocks, held in registers from the
 // start; the XCD's amax from the E partial maxima (or the given g; or, if the
 // exchange does not complete within the bound, from the whole tensor read
-// here); then g and its blocks in the product's order, and its `ready` flag;
-// then its blocks in the canonical encoding.
+// here); then g and its blocks in the product's order, and its `ready` flag.
 template <typename T>
 __device__ void run_encoder(const SkinnyParams& p, uint32_t e, XcdWords* xw, uint64_t tag, uint32_t* s_red,
                             float* rtab, float* s_g, int nthreads) {
@@ -333,12 +334,6 @@ __device__ void run_encoder(const SkinnyParams& p, uint32_t e, XcdWords* xw, uin
     __builtin_amdgcn_s_waitcnt(0);   // every thread's product-order blocks (and g) are in the L2
     lds_barrier();
     if (threadIdx.x == 0) raise_flag(&xw->ready_flag[e], tag);
-    // The call's output encoding, off the products' path (the same bytes from every XCD).
-#pragma unroll
-    for (int j = 0; j < kEncBlocksPerThread; ++j) {
-        const uint32_t b = b0 + threadIdx.x + j * nthreads;
-        if (b < b1) store_canonical(p, b, c[j]);
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -370,6 +365,14 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_kernel(SkinnyParams p) {
     }
     const int nb = (int)blockIdx.x - (ENC ? p.n_enc : 0);   // this workgroup's 16-row weight block
     const int ks0 = wave * NKW;
+    // k-steps [cks0, cks1) of the call's output encoding are this workgroup's to
+    // write (the G product workgroups split the KS k-steps; each is written once)
+    int cks0 = 0, cks1 = 0;
+    if constexpr (ENC) {
+        const int G = (int)gridDim.x - p.n_enc;
+        cks0 = nb * p.KS / G;
+        cks1 = (nb + 1) * p.KS / G;
+    }
 
     // Weights first: all NKW k-steps of this wavefront (k-steps past K read zero).
     const rsrc_t rwc = make_rsrc(p.wc, (uint64_t)p.n_pad * p.K / 2);
@@ -464,15 +467,37 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_kernel(SkinnyParams p) {
     // 16x16x32 products over this wavefront's k-steps, into two accumulators
     // (chunks 0, 1 and 2, 3 of each k-step) so that consecutive instructions do
     // not wait for each other's results.
+    // In the fused kernel each k-step of this workgroup's share of the call's
+    // output encoding is stored from the same registers (token r16: code bytes
+    // kg*16 .. kg*16+15 of the k-step and its scale bytes 2kg, 2kg+1); a
+    // workgroup that encoded locally has written all of it already.
+    // (buffer stores: rows r16 >= M fall past the buffers and are dropped)
+    bool out_enc = false;
+    if constexpr (ENC) out_enc = !s_local;
+    const rsrc_t roc = make_rsrc(p.x_codes, (uint64_t)p.M * p.K / 2);
+    const rsrc_t ros = make_rsrc(p.x_scales, (uint64_t)p.M * p.K / 16);
+    if constexpr (ENC) {
+        // (the scale offset is the code offset / 8: r16*K/16 + 2kg)
+        const uint32_t oc = (uint32_t)r16 * (uint32_t)(p.K / 2) + kg * 16;
+#pragma unroll
+        for (int j = 0; j < NKW; ++j) {
+            const int ks = ks0 + j;
+            if (out_enc && ks >= cks0 && ks < cks1) {   // (workgroup-uniform)
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, xv[j]), roc, (int)oc, ks * 64, 0);
+                __builtin_amdgcn_raw_buffer_store_b16((unsigned short)xsv[j], ros, (int)(oc >> 3), ks * 8, 0);
+            }
+        }
+    }
     float4v acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < NKW; ++j)
+    for (int j = 0; j < NKW; ++j) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const half8 b = decode8(word_of(xv[j], c), scale_byte(xsv[j], c >> 1));
             if (c & 1) acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[j][c], b, acc1, 0, 0, 0);
             else acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[j][c], b, acc0, 0, 0, 0);
         }
+    }
     const float4v acc = acc0 + acc1;
 
     // Partial tiles summed in wavefront order.  Lane holds rows 4kg..4kg+3 of
