@@ -78,6 +78,9 @@ constexpr uint32_t kDeadOffset = 0x80000000u;   // scalar offset past every buff
 // 0.05-0.3 us (served by the XCD's L2), while plain or sc0 loads keep
 // returning the stale value even after an L1 invalidate.
 constexpr int kPastL1 = 16;
+// Cache policy of the weight loads: nontemporal (every weight byte is read
+// once per launch; measured on the decode layer: 8.39 -> 8.09 us per step).
+constexpr int kStreamed = 2;
 
 // Per-XCD words of the workspace (256 bytes): per encoder e, a 16-byte record
 // of its partial max|x| {tag low, tag high, max bits, check} (one store; the
@@ -399,8 +402,11 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_kernel(SkinnyParams p) {
         for (int j = 0; j < NKW; ++j) {
             const int ks = ks0 + j;
             const bool live = ks < p.KS && blk < row_blocks;   // (wavefront-uniform)
-            wv[rb][j] = bload16(rwc, wc_lane, live ? wc_blk + (uint32_t)ks * 1024 : kDeadOffset);
-            wsv[rb][j] = bload2(rws, ws_lane, live ? ws_blk + (uint32_t)ks * 128 : kDeadOffset);
+            const uint32_t oc = live ? wc_blk + (uint32_t)ks * 1024 : kDeadOffset;
+            const uint32_t os = live ? ws_blk + (uint32_t)ks * 128 : kDeadOffset;
+            wv[rb][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rwc, (int)wc_lane, (int)oc,
+                                                                                          kStreamed));
+            wsv[rb][j] = (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rws, (int)ws_lane, (int)os, kStreamed);
         }
     }
     const rsrc_t rcs = make_rsrc(p.cs, (uint64_t)p.n_pad * 4);
