@@ -7,12 +7,12 @@
 // so nothing stands in front of the weight stream.  Per block the W partial
 // 16x16 tiles are added through LDS in wavefront order (a fixed order: the
 // result never depends on timing, nor on RB) and the workgroup writes the
-// block's 16 columns of Y.  No workgroup adds another's partials.  RB = 2 in
-// the fused kernel when K <= 5120 (NKW <= 5, the two blocks' decoded weights
-// then fit two wavefronts per SIMD): each activation fragment then serves 32
-// weight rows, which halves the activation reads from the L2, and every
-// workgroup has its compute unit to itself (the decode layer: 11.2 -> 8.4 us
-// per step); RB = 1 otherwise.
+// block's 16 columns of Y.  No workgroup adds another's partials.  RB = 2
+// when K <= 5120 (NKW <= 5, the two blocks' decoded weights then fit two
+// wavefronts per SIMD): each activation fragment then serves 32 weight rows,
+// which halves the activation reads from the L2, and every workgroup has its
+// compute unit to itself (the decode layer: fused step 11.2 -> 8.4 us,
+// product alone 9.5 -> 8.0 us); RB = 1 otherwise.
 //
 // Activations are the B operand of the 16x16x32 instruction, read straight
 // from the canonical encoding: lane (token t, lane group kg) needs, per k-step
@@ -581,12 +581,12 @@ SkinnyPlan plan_for(const nvfp4_weight_desc& d) {
     return p;
 }
 
-// Row blocks per product workgroup: two in the fused kernel while both blocks'
-// decoded weights fit the registers of two wavefronts per SIMD (NKW <= 5), so
-// that each workgroup's activation loads from the L2 serve 32 weight rows and
-// every workgroup runs alone on its compute unit; one otherwise.
+// Row blocks per product workgroup: two while both blocks' decoded weights fit
+// the registers of two wavefronts per SIMD (NKW <= 5), so that each
+// workgroup's activation loads serve 32 weight rows and every workgroup runs
+// alone on its compute unit; one otherwise.
 template <int NKW, bool ENC>
-struct RowBlocks : std::integral_constant<int, (ENC && NKW <= 5) ? 2 : 1> {};
+struct RowBlocks : std::integral_constant<int, NKW <= 5 ? 2 : 1> {};
 
 template <typename T, int NKW, bool ENC>
 void launch_one(unsigned blocks, unsigned n_enc, int waves, hipStream_t stream, const SkinnyParams& a, bool epi) {
