@@ -350,9 +350,10 @@ nvfp4_status nvfp4_unpack_weights(const nvfp4_weight_desc* w, uint8_t* codes, ui
  * workspace: device, >= nvfp4_gemm_workspace_bytes(M, w) bytes, 256-byte aligned
  *            (may be NULL when that is 0, which it is for every shape of this
  *            version: the product keeps no state between workgroups).  For few
- *            tokens (1 <= M <= 16, K <= 8192) one workgroup takes each 16 rows
- *            of the weight over all of K and adds its wavefronts' partial sums
- *            in a fixed order, so results do not depend on scheduling.
+ *            tokens (1 <= M <= 16, K <= 8192) one workgroup takes each 32 rows
+ *            of the weight (16 when K > 5120) over all of K and adds its
+ *            wavefronts' partial sums per 16 rows in a fixed order, so results
+ *            do not depend on scheduling.
  * ------------------------------------------------------------------------- */
 size_t nvfp4_gemm_workspace_bytes(int64_t M, const nvfp4_weight_desc* w);
 nvfp4_status nvfp4_gemm(int64_t M, const uint8_t* a_codes, const uint8_t* a_scales, const float* g_x,
