@@ -54,6 +54,20 @@ def parse():
     return p.parse_args()
 
 
+def quantizer_launches(rows, K, dtype, cus=256):
+    """Kernels nvfp4_quantize runs for a dense, aligned tensor with g computed (the library's rule):
+    one for up to 8192 blocks (every workgroup reduces the whole tensor), one for tensors with at least
+    1024 amax segments of 8192 elements that fit one workgroup per compute unit holding 1024 threads x 8
+    (bf16) or 4 (FP32) blocks (the one-pass quantizer), two otherwise (amax pass, then the encoder)."""
+    blocks = rows * (K // 16)
+    if blocks <= 1024 * (8 if dtype == "bf16" else 4):
+        return 1
+    segments = -(-(rows * K) // 8192)
+    if segments >= 1024 and blocks <= cus * 1024 * (8 if dtype == "bf16" else 4):
+        return 1
+    return 2
+
+
 def measured_traffic(workload):
     """HBM bytes per launch of the dominant kernel, from the committed counter runs (profiles/traffic.json),
     or None when there are none for this workload or the kernel's sources have changed since."""
@@ -143,7 +157,7 @@ def main():
     skinny = M <= 16     # few-token path: one kernel (amax, quantize and product)
     y = torch.empty((M, N), dtype=torch.float32, device=dev)
     gemm_ws = torch.zeros((max(nv.nvfp4_gemm_workspace_bytes(M, packed.desc), 256),), dtype=torch.uint8,
-                          device=dev)       # split-K counters start at zero; every call leaves them so
+                          device=dev)       # (the product needs none at these shapes; a minimal one is passed)
     if wl.quantize_w_in_step:
         wq_bufs = [nv.empty_quantized(w.shape[0], K, dev) for w in w_dev]
         wq_ws = [torch.empty((max(nv.nvfp4_quantize_workspace_bytes(w.shape[0], K), 256),), dtype=torch.uint8,
@@ -495,11 +509,14 @@ def main():
                    "weight_copies": copies, "graph": not args.no_graph, "variants_timed": extra},
         "roofline": roof,
         "cpu_baseline": cpu,
-        # launches: few tokens one kernel; otherwise amax + encode + product (two product launches when the
-        # weight has a ragged column edge, as the GDN projection); tiny adds the weights' quantize and pack
+        # launches: few tokens one kernel; otherwise the quantizer's (one or two, quantizer_launches) and
+        # the product's (two when the weight has a ragged column edge, as the GDN projection); tiny adds
+        # the weights' quantize and pack
         "step_breakdown_us": {"step (nvfp4_linear)": t_step * 1e6,
-                              "launches_per_step": 1 if skinny else (5 if wl.quantize_w_in_step else
-                                                                     (4 if N % 256 else 3)),
+                              "launches_per_step": 1 if skinny else (
+                                  quantizer_launches(M, K, wl.x_dtype) + (2 if N % 256 else 1)
+                                  + (sum(quantizer_launches(w.shape[0], K, wl.w_dtype) for w in wl.w) + 1
+                                     if wl.quantize_w_in_step else 0)),
                               "quantize alone": t_quant * 1e6, "gemm alone": t_gemm * 1e6,
                               "step with g given (no amax pass)": t_given * 1e6 if t_given else None,
                               "hot-cache step (one weight copy, resident in the Infinity Cache)":

@@ -14,7 +14,12 @@
 // Robust" and "Critical Lessons for Model Serving").  Every decision is taken
 // in IEEE FP32 with one rounding per operation (contraction disabled below),
 // so codes and scales are bit-for-bit reproducible.
+#include <atomic>
+#include <cstdlib>
+#include <type_traits>
+
 #include "common.h"
+#include "launch_tag.h"
 
 #pragma clang fp contract(off)
 
@@ -497,6 +502,176 @@ static hipError_t launch_small(int p, const T* x, int64_t rows, int64_t K, int64
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// One pass for a tensor that fits the register files (up to 64 MB): every
+// workgroup (one per compute unit, all resident at once) loads its share of
+// the blocks into registers, reduces its max|x| and publishes it; every
+// workgroup then reads all the published maxima, derives the same g and
+// encodes its blocks from its registers, so x is read from memory once
+// instead of twice.  The exchange spans all XCDs, so both words of a record
+// are device-scope atomics (stored through to memory, loaded from it): the
+// writer stores the max, waits for that store to complete, then stores the
+// launch tag; a reader that has loaded the current tag loads the max after
+// that load completed.  Only these atomic words cross workgroups, so no L2
+// write-back or invalidate is needed (with them the exchange took ~5 us
+// longer).  A workgroup whose wait exceeds a bound (a workgroup not resident,
+// if another kernel holds compute units) reduces max|x| over the whole tensor
+// itself: the same g.
+// ---------------------------------------------------------------------------
+struct AmaxRecord {
+    uint32_t max_bits;
+    uint32_t pad;
+    uint64_t tag;
+};
+constexpr int kResThreads = 1024;
+// records of one launch fit the partials' part of the workspace (256 of them)
+constexpr int kResMaxGrid = kMaxAmaxPartials * (int)sizeof(float) / (int)sizeof(AmaxRecord);
+template <typename T>
+struct ResBlocks : std::integral_constant<int, sizeof(T) == 2 ? 8 : 4> {};   // 64 raw registers per thread
+constexpr int kResDefaultPolls = 1 << 15;
+
+template <typename T>
+__global__ __launch_bounds__(kResThreads) void quantize_resident_kernel(const T* __restrict__ x, int64_t rows,
+                                                                        int64_t K, int64_t ld,
+                                                                        uint8_t* __restrict__ codes,
+                                                                        uint8_t* __restrict__ scales,
+                                                                        float* __restrict__ g_out, AmaxRecord* rec,
+                                                                        int polls) {
+    constexpr int R = ResBlocks<T>::value;
+    __shared__ int s_fail;
+    __shared__ float rtab[128];
+    if (threadIdx.x == 0) s_fail = 0;   // (ordered before its uses by the barriers in block_max)
+    const int G = (int)gridDim.x;
+    const uint32_t bpr = (uint32_t)(K / 16), nblk = (uint32_t)rows * bpr;
+    const uint32_t per = (nblk + (uint32_t)G - 1) / (uint32_t)G;
+    const uint32_t b0 = blockIdx.x * per, b1 = min(nblk, b0 + per);
+    const rsrc_t rx = make_rsrc(x, (uint64_t)rows * ld * sizeof(T));
+    const bool dense = (ld == K);
+    RawBlock<T> raw[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) {   // branch-free: blocks past the share read as zero
+        const uint32_t b = b0 + threadIdx.x + (uint32_t)i * kResThreads;
+        uint32_t off = kOutOfBounds;
+        if (b < b1) {
+            const uint32_t r = dense ? 0u : b / bpr, kb = dense ? b : b - r * bpr;
+            off = (uint32_t)(((int64_t)r * ld + (int64_t)kb * 16) * (int64_t)sizeof(T));
+        }
+#pragma unroll
+        for (int q = 0; q < (int)(sizeof(RawBlock<T>) / 16); ++q)
+            raw[i].v[q] = bload16(rx, off, (uint32_t)q * 16);
+    }
+    // block maxima from the raw bits (finite magnitudes order like their bit patterns), without widening
+    float bm[R], m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+        uint32_t mb = 0;
+#pragma unroll
+        for (int q = 0; q < (int)(sizeof(RawBlock<T>) / 16); ++q) {
+            const uint32_t w[4] = {raw[i].v[q].x, raw[i].v[q].y, raw[i].v[q].z, raw[i].v[q].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if constexpr (sizeof(T) == 2) {
+                    mb = max(mb, (w[e] & 0x7FFFu) << 16);
+                    mb = max(mb, w[e] & 0x7FFF0000u);
+                } else {
+                    mb = max(mb, w[e] & 0x7FFFFFFFu);
+                }
+            }
+        }
+        bm[i] = __uint_as_float(mb);
+        m = fmaxf(m, bm[i]);
+    }
+    m = block_max<kResThreads>(m);
+    const uint64_t tag = launch_tag();
+    if (threadIdx.x == 0) {
+        __hip_atomic_store(&rec[blockIdx.x].max_bits, __float_as_uint(m), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_waitcnt(0);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __hip_atomic_store(&rec[blockIdx.x].tag, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    // thread t waits for record t, then (after the barrier, so every record is in) loads its max
+    if ((int)threadIdx.x < G) {
+        bool ok = false;
+        for (int i = 0; i < polls && !ok; ++i) {
+            ok = __hip_atomic_load(&rec[threadIdx.x].tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == tag;
+            if (!ok) __builtin_amdgcn_s_sleep(1);
+        }
+        if (!ok) s_fail = 1;
+    }
+    __syncthreads();
+    const float mt = (int)threadIdx.x < G && !s_fail
+                         ? __uint_as_float(__hip_atomic_load(&rec[threadIdx.x].max_bits, __ATOMIC_RELAXED,
+                                                             __HIP_MEMORY_SCOPE_AGENT))
+                         : 0.0f;
+    float amax = block_max<kResThreads>(mt);
+    if (s_fail) {   // (uniform: written before the barriers of block_max)
+        float w = 0.0f;
+        for (uint32_t b = threadIdx.x; b < nblk; b += kResThreads) {
+            const uint32_t r = b / bpr, kb = b - r * bpr;
+            const uint32_t off = (uint32_t)(((int64_t)r * ld + (int64_t)kb * 16) * (int64_t)sizeof(T));
+            RawBlock<T> rb;
+#pragma unroll
+            for (int q = 0; q < (int)(sizeof(RawBlock<T>) / 16); ++q) rb.v[q] = bload16(rx, off, (uint32_t)q * 16);
+            float v[16];
+            widen(rb, v);
+            w = fmaxf(w, block_amax(v));
+        }
+        amax = block_max<kResThreads>(w);
+    }
+    const float g = global_scale_from_amax(amax);
+    if (blockIdx.x == 0 && threadIdx.x == 0) g_out[0] = g;
+    const float s_enc = 1.0f / g;
+    fill_recip_table(rtab, s_enc, threadIdx.x, kResThreads);
+    __syncthreads();
+    // (the raw blocks stay packed until here: widened all at once they would not fit the registers)
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+        for (int q = 0; q < (int)(sizeof(RawBlock<T>) / 16); ++q)
+            asm volatile("" : "+v"(raw[i].v[q].x), "+v"(raw[i].v[q].y), "+v"(raw[i].v[q].z), "+v"(raw[i].v[q].w));
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+        const uint32_t b = b0 + threadIdx.x + (uint32_t)i * kResThreads;
+        if (b < b1) {
+            float v[16];
+            widen(raw[i], v);
+            uint32_t lo, hi, S;
+            encode_block(v, bm[i], s_enc, rtab, lo, hi, S);
+            store_code_block(codes, scales, (int64_t)b, lo, hi, S);
+        }
+    }
+}
+
+// Compute units of the current device (cached per device).
+static int cu_count() {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        cached[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+// Workgroups of the one-pass path for this tensor, or 0 when it does not apply.
+static int resident_grid(int64_t rows, int64_t K, int64_t ld, int in_dtype, const void* x, const float* partials,
+                         int n_partials) {
+    const int esize = in_dtype == NVFP4_IN_BF16 ? 2 : 4;
+    const int per_thread = in_dtype == NVFP4_IN_BF16 ? ResBlocks<uint16_t>::value : ResBlocks<float>::value;
+    // the records need the whole partials area, aligned for their 64-bit tags
+    if (n_partials < kMaxAmaxPartials || reinterpret_cast<uintptr_t>(partials) % 16 != 0) return 0;
+    if (reinterpret_cast<uintptr_t>(x) % 16 != 0 || (ld * esize) % 16 != 0) return 0;
+    if (rows * ld * esize > INT32_MAX) return 0;
+    const int cus = cu_count();
+    const int grid = cus < kResMaxGrid ? cus : kResMaxGrid;
+    if (grid < 1) return 0;
+    const int64_t nblk = rows * (K / 16);
+    return nblk <= (int64_t)grid * kResThreads * per_thread ? grid : 0;
+}
+
 int quantize_partials_count(int64_t rows, int64_t K) {
     const int64_t elems = rows * K;
     int64_t segs = (elems + kSegElems - 1) / kSegElems;
@@ -842,6 +1017,19 @@ hipError_t launch_quantize(const void* x, int in_dtype, int64_t rows, int64_t K,
         if (p <= 4)
             return launch_small<float>(p, static_cast<const float*>(x), rows, K, ld_x, codes, scales, g, given,
                                        stream);
+    }
+    const int rg = (given || rht) ? 0 : resident_grid(rows, K, ld_x, in_dtype, x, partials, n_partials);
+    if (rg > 0) {
+        int polls = kResDefaultPolls;
+        if (const char* e = std::getenv("NVFP4_AMAX_POLLS")) polls = std::atoi(e);   // testing the local path
+        AmaxRecord* rec = reinterpret_cast<AmaxRecord*>(partials);
+        if (in_dtype == NVFP4_IN_BF16)
+            hipLaunchKernelGGL(quantize_resident_kernel<uint16_t>, dim3(rg), dim3(kResThreads), 0, stream,
+                               static_cast<const uint16_t*>(x), rows, K, ld_x, codes, scales, g, rec, polls);
+        else
+            hipLaunchKernelGGL(quantize_resident_kernel<float>, dim3(rg), dim3(kResThreads), 0, stream,
+                               static_cast<const float*>(x), rows, K, ld_x, codes, scales, g, rec, polls);
+        return hipGetLastError();
     }
     const int grid = encode_grid(rows, K);
     if (in_dtype == NVFP4_IN_BF16)

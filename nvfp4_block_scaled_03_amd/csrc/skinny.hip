@@ -56,12 +56,9 @@
 #include <type_traits>
 
 #include "common.h"
+#include "launch_tag.h"
 
 #pragma clang fp contract(off)
-
-// The launch's dispatch id (a user SGPR the command processor sets for every
-// dispatch), through the LLVM intrinsic that reads it.
-extern "C" __device__ uint64_t nvfp4_llvm_dispatch_id() __asm("llvm.amdgcn.dispatch.id");
 
 namespace nvfp4 {
 
@@ -105,14 +102,6 @@ __device__ __forceinline__ void lds_barrier() {
 // The XCD this wavefront runs on.
 __device__ __forceinline__ uint32_t hw_xcc_id() {
     return (uint32_t)__builtin_amdgcn_s_getreg((20) | (0 << 6) | (3 << 11)) & 0xFu;   // hwreg(HW_REG_XCC_ID, 0, 4)
-}
-
-// Tag of this launch: the dispatch id mixed with the queue address (dispatch
-// ids count per queue); never 0, the value of an unused flag.
-__device__ __forceinline__ uint64_t launch_tag() {
-    const uint64_t q = (uint64_t)(uintptr_t)__builtin_amdgcn_queue_ptr();
-    const uint64_t h = ((nvfp4_llvm_dispatch_id() + 1) * 0x9E3779B97F4A7C15ull) ^ (q * 0xC2B2AE3D27D4EB4Full);
-    return h | 1u;
 }
 
 // Raise this encoder's flag: the data it publishes (stored by every thread of

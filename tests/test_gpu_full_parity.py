@@ -8,60 +8,17 @@ parallel on the host cores.
 
 Pages: "Why Gated DeltaNet Survives 4-Bit Quantization", section "Why the 'Fragile' Recurrence is
 Actually Robust" (16-element blocks, each with an E4M3 scale, and an FP32 tensor scale)."""
-import os
-from concurrent.futures import ThreadPoolExecutor
-
 import numpy as np
 import pytest
 import torch
 
 import nvfp4_block_scaled_03_amd as nv
 import workloads
-from gpu_util import DEV, host, say, to_dev
+from gpu_util import DEV, assert_every_byte, host, oracle_quantize_whole, oracle_threads, say, to_dev
 from oracle import nvfp4_ref as ref
 
 pytestmark = pytest.mark.gpu
 F32 = np.float32
-CHUNK_ROWS = 256
-
-
-def _threads():
-    return max(1, min(16, len(os.sched_getaffinity(0))))
-
-
-def _oracle_chunks(x, g, chunk=CHUNK_ROWS):
-    """Oracle quantization of row chunks of x with the tensor scale g, yielded as (r0, Quantized) in order."""
-    starts = range(0, x.shape[0], chunk)
-    with ThreadPoolExecutor(_threads()) as ex:
-        yield from zip(starts, ex.map(lambda r0: ref.quantize(x[r0:r0 + chunk], "given", g), starts))
-
-
-def oracle_quantize_whole(x):
-    """Oracle quantization of the whole tensor (g from its amax), assembled from row chunks."""
-    g = ref.global_scale(F32(np.max(np.abs(x))) if x.size else F32(0))
-    codes = np.empty((x.shape[0], x.shape[1] // 2), np.uint8)
-    scales = np.empty((x.shape[0], x.shape[1] // 16), np.uint8)
-    for r0, q in _oracle_chunks(x, g):
-        codes[r0:r0 + q.codes.shape[0]] = q.codes
-        scales[r0:r0 + q.scales.shape[0]] = q.scales
-    return ref.Quantized(codes, scales, g)
-
-
-def assert_every_byte(codes, scales, g, x, what):
-    """Device codes/scales/g of x against the oracle, every byte, chunk by chunk."""
-    c, s, gv = host(codes), host(scales), F32(host(g)[0])
-    g_ref = ref.global_scale(F32(np.max(np.abs(x))) if x.size else F32(0))
-    assert gv.tobytes() == F32(g_ref).tobytes(), f"{what}: g {gv!r} != oracle {g_ref!r}"
-    for r0, q in _oracle_chunks(x, g_ref):
-        r1 = r0 + q.codes.shape[0]
-        if not np.array_equal(s[r0:r1], q.scales):
-            r, b = np.argwhere(s[r0:r1] != q.scales)[0]
-            raise AssertionError(f"{what}: scale byte differs at row {r0 + r} block {b}: "
-                                 f"gpu 0x{s[r0 + r, b]:02x} oracle 0x{q.scales[r, b]:02x}")
-        if not np.array_equal(c[r0:r1], q.codes):
-            r, j = np.argwhere(c[r0:r1] != q.codes)[0]
-            raise AssertionError(f"{what}: code byte differs at row {r0 + r} byte {j}: "
-                                 f"gpu 0x{c[r0 + r, j]:02x} oracle 0x{q.codes[r, j]:02x}")
 
 
 @pytest.mark.timeout(300)
@@ -69,7 +26,7 @@ def assert_every_byte(codes, scales, g, x, what):
 def test_workload_every_byte(name):
     """All operands of the workload, quantized whole on the device, against the oracle byte for byte."""
     wl = workloads.make(name)
-    say(f"every-byte parity: {name} X {wl.x.shape} {wl.x_dtype} ({_threads()} oracle threads)")
+    say(f"every-byte parity: {name} X {wl.x.shape} {wl.x_dtype} ({oracle_threads()} oracle threads)")
     c, s, g = nv.quantize(to_dev(wl.x, wl.x_dtype))
     torch.cuda.synchronize()
     assert_every_byte(c, s, g, wl.x, f"{name} X")

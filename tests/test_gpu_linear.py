@@ -135,7 +135,7 @@ def test_alternating_inputs_see_fresh_codes():
 def test_amax_fallback_when_peers_do_not_publish(shape, monkeypatch):
     """The few-token kernel's product workgroups wait for the encoder workgroups to publish the
     activations' encoding; with a poll bound of zero each of them encodes everything itself (the
-    same bytes). Same bits either way, and the counters still end at zero (calls=2)."""
+    same bytes). Same bits either way, also with the workspace reused by a second call."""
     monkeypatch.setenv("NVFP4_AMAX_POLLS", "0")
     if shape == "decode":
         wl = workloads.make_decode()

@@ -1,0 +1,89 @@
+"""The one-pass quantizer: tensors of about 8.4M to 32M elements (16 to 64 MB of bf16) are quantized by
+one workgroup per compute unit, each holding its share of the blocks in registers while the
+workgroups exchange their maxima, so x is read once.  Codes, scales and g must equal the oracle's
+bit for bit, every byte: bf16 and FP32, dense and strided rows, the tensor maximum in the first or
+the last workgroup's share, sizes at both ends of the range, and the local path a workgroup takes
+when the exchange does not complete (forced with a poll bound of zero: every workgroup then reduces
+max|x| over the whole tensor itself).
+
+Pages: "Why Gated DeltaNet Survives 4-Bit Quantization", section "Why the 'Fragile' Recurrence is
+Actually Robust" (16-element blocks with E4M3 scales and one FP32 tensor scale)."""
+import numpy as np
+import pytest
+import torch
+
+import nvfp4_block_scaled_03_amd as nv
+from gpu_util import assert_every_byte, say, to_dev
+
+pytestmark = pytest.mark.gpu
+F32 = np.float32
+
+
+def _tensor(seed, rows, K, where):
+    """Student-t(3) values with one outlier of 60 in the first or last row (the tensor maximum then
+    sits in the first or the last workgroup's share)."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_t(3, size=(rows, K)).astype(F32)
+    np.clip(x, -40.0, 40.0, out=x)
+    r = 0 if where == "first" else rows - 1
+    x[r, int(rng.integers(K))] = F32(-60.0 if where == "first" else 60.0)
+    return x
+
+
+def _quantize(x, dtype, ld_pad=0):
+    rows, K = x.shape
+    if ld_pad:
+        big = np.zeros((rows, K + ld_pad), F32)
+        big[:, :K] = x
+        xd = to_dev(big, dtype)[:, :K]
+    else:
+        xd = to_dev(x, dtype)
+    out = nv.quantize(xd)
+    torch.cuda.synchronize()
+    return out
+
+
+def _as_dtype(x, dtype):
+    """Host values of the device dtype (bf16: rounded to nearest even, as the device holds them)."""
+    return x if dtype == "f32" else torch.from_numpy(x).to(torch.bfloat16).float().numpy()
+
+
+# (dtype, rows, K, row padding, where the maximum is): the smallest size that takes the path
+# (1024 amax partials' worth of elements), a ragged share per workgroup, the bf16 capacity
+# (32M elements, nGPT's activations), the FP32 capacity (16M elements), strided rows
+CASES = [("bf16", 2048, 4112, 0, "last"), ("bf16", 3000, 8192, 0, "first"), ("bf16", 8192, 4096, 0, "last"),
+         ("f32", 2048, 8192, 0, "first"), ("bf16", 2100, 4096, 64, "last")]
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("dtype,rows,K,ld_pad,where", CASES)
+def test_one_pass_every_byte(dtype, rows, K, ld_pad, where):
+    say(f"one-pass quantizer: {dtype} {rows}x{K} ld pad {ld_pad}, maximum in the {where} share")
+    x = _as_dtype(_tensor(rows * 7 + K, rows, K, where), dtype)
+    c, s, g = _quantize(x, dtype, ld_pad)
+    assert_every_byte(c, s, g, x, f"{dtype} {rows}x{K}")
+
+
+@pytest.mark.timeout(300)
+def test_one_pass_local_path(monkeypatch):
+    """A poll bound of zero: no workgroup waits for the others' maxima; each reads the whole tensor."""
+    monkeypatch.setenv("NVFP4_AMAX_POLLS", "0")
+    say("one-pass quantizer, local path: bf16 2048x4112")
+    x = _as_dtype(_tensor(11, 2048, 4112, "last"), "bf16")
+    c, s, g = _quantize(x, "bf16")
+    assert_every_byte(c, s, g, x, "local path")
+
+
+def test_one_pass_repeated_calls():
+    """Records of an earlier call stay in the workspace; the next call's tags tell them apart: three calls
+    on different tensors through one workspace, each against the oracle."""
+    rows, K = 2048, 4112
+    ws = torch.empty(nv.nvfp4_quantize_workspace_bytes(rows, K), dtype=torch.uint8, device="cuda")
+    for i, scale in enumerate((1.0, 1e-3, 30.0)):
+        say(f"one-pass quantizer, call {i} (scale {scale}) on one workspace")
+        x = _as_dtype((_tensor(100 + i, rows, K, "first" if i % 2 else "last") * F32(scale)).astype(F32), "bf16")
+        xd = to_dev(x, "bf16")
+        c, s, g = nv.empty_quantized(rows, K)
+        nv.nvfp4_quantize(xd, c, s, g, nv.NVFP4_G_COMPUTE, ws)
+        torch.cuda.synchronize()
+        assert_every_byte(c, s, g, x, f"call {i}")
