@@ -119,7 +119,10 @@ nvfp4_status nvfp4_device_check(void);
  * scales   : device, rows * K/16 bytes, written (dense, row stride K/16)
  * g        : device, one float; written in COMPUTE mode, read in GIVEN mode
  * workspace: device, >= nvfp4_quantize_workspace_bytes(rows, K) bytes
- *            (may be NULL when that is 0); contents need no initialisation
+ *            (may be NULL when that is 0); contents need no initialisation.
+ *            It holds the per-workgroup maxima of the call (tagged with the
+ *            launch where the workgroups exchange them), so calls that may run
+ *            concurrently must not share a workspace.
  * ------------------------------------------------------------------------- */
 size_t nvfp4_quantize_workspace_bytes(int64_t rows, int64_t K);
 nvfp4_status nvfp4_quantize(const void* x, int in_dtype, int64_t rows, int64_t K, int64_t ld_x,
