@@ -1,14 +1,18 @@
 // NVFP4 activation/weight quantizer for gfx950.
 //
-// Two kernels, because the per-tensor scale is a global dependency of every
-// block's encoding:
-//   1. amax_partials: each workgroup reduces max|x| over its share of the tensor
-//      and writes one partial (no atomics, no initialised memory needed).
+// The per-tensor scale is a global dependency of every block's encoding, so a
+// large tensor takes two kernels:
+//   1. amax: each workgroup reduces max|x| over its share of the tensor and
+//      writes one partial (no atomics, no initialised memory needed).
 //   2. encode: every workgroup reduces the partials itself (a few KB from L2),
 //      derives g and s_enc = fl32(1/g), and encodes 16-element blocks along K:
 //      bamax -> E4M3 scale of fl32(fl32(bamax*s_enc)/6) -> r = fl32(s_enc/S)
 //      (from a 128-entry table per workgroup)
 //      -> E2M1 code of fl32(x*r) per element -> two codes per byte.
+// A small tensor takes one kernel whose workgroups each reduce the whole tensor
+// (quantize_small_kernel); one of up to 64 MB takes one kernel whose workgroups
+// keep their shares in registers while they exchange their maxima
+// (quantize_resident_kernel), so it is read once.
 // The block structure and per-tensor scale follow "Why Gated DeltaNet Survives
 // 4-Bit Quantization" (sections "Why the 'Fragile' Recurrence is Actually
 // Robust" and "Critical Lessons for Model Serving").  Every decision is taken
