@@ -52,7 +52,7 @@ def _as_dtype(x, dtype):
 # (1024 amax partials' worth of elements), a ragged share per workgroup, the bf16 capacity
 # (32M elements, nGPT's activations), the FP32 capacity (16M elements), strided rows
 CASES = [("bf16", 2048, 4112, 0, "last"), ("bf16", 3000, 8192, 0, "first"), ("bf16", 8192, 4096, 0, "last"),
-         ("f32", 2048, 8192, 0, "first"), ("bf16", 2100, 4096, 64, "last")]
+         ("f32", 2048, 8192, 0, "first"), ("bf16", 2100, 4096, 64, "last"), ("f32", 1100, 8192, 4, "first")]
 
 
 @pytest.mark.timeout(300)
@@ -87,3 +87,12 @@ def test_one_pass_repeated_calls():
         nv.nvfp4_quantize(xd, c, s, g, nv.NVFP4_G_COMPUTE, ws)
         torch.cuda.synchronize()
         assert_every_byte(c, s, g, x, f"call {i}")
+
+
+def test_one_pass_zero_tensor():
+    """An all-zero tensor in the one-pass range: every workgroup publishes 0, g = 1, codes and scales 0."""
+    say("one-pass quantizer: zeros bf16 2048x4112")
+    x = np.zeros((2048, 4112), F32)
+    c, s, g = _quantize(x, "bf16")
+    assert_every_byte(c, s, g, x, "zeros")
+    assert float(g.cpu()[0]) == 1.0
