@@ -485,11 +485,10 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_kernel(SkinnyParams p) {
     // kg*16 .. kg*16+15 of the k-step and its scale bytes 2kg, 2kg+1); a
     // workgroup that encoded locally has written all of it already.
     // (buffer stores: rows r16 >= M fall past the buffers and are dropped)
-    bool out_enc = false;
-    if constexpr (ENC) out_enc = !s_local;
-    const rsrc_t roc = make_rsrc(p.x_codes, (uint64_t)p.M * p.K / 2);
-    const rsrc_t ros = make_rsrc(p.x_scales, (uint64_t)p.M * p.K / 16);
     if constexpr (ENC) {
+        const bool out_enc = !s_local;
+        const rsrc_t roc = make_rsrc(p.x_codes, (uint64_t)p.M * p.K / 2);
+        const rsrc_t ros = make_rsrc(p.x_scales, (uint64_t)p.M * p.K / 16);
         // (the scale offset is the code offset / 8: r16*K/16 + 2kg)
         const uint32_t oc = (uint32_t)r16 * (uint32_t)(p.K / 2) + kg * 16;
 #pragma unroll
