@@ -96,3 +96,54 @@ def test_one_pass_zero_tensor():
     c, s, g = _quantize(x, "bf16")
     assert_every_byte(c, s, g, x, "zeros")
     assert float(g.cpu()[0]) == 1.0
+
+
+def _quantize_t(x, dtype, ld_pad=0, both=False):
+    rows, cols = x.shape
+    if ld_pad:
+        big = np.zeros((rows, cols + ld_pad), F32)
+        big[:, :cols] = x
+        xd = to_dev(big, dtype)[:, :cols]
+    else:
+        xd = to_dev(x, dtype)
+    ws = torch.empty(nv.nvfp4_quantize_workspace_bytes(rows, cols), dtype=torch.uint8, device="cuda")
+    ct, st, g = nv.empty_quantized(cols, rows)
+    if both:
+        cr, sr, _ = nv.empty_quantized(rows, cols)
+        nv.nvfp4_quantize_both(xd, cr, sr, ct, st, g, nv.NVFP4_G_COMPUTE, ws)
+        torch.cuda.synchronize()
+        return (cr, sr), (ct, st), g
+    nv.nvfp4_quantize_t(xd, ct, st, g, nv.NVFP4_G_COMPUTE, ws)
+    torch.cuda.synchronize()
+    return None, (ct, st), g
+
+
+# (dtype, rows, cols, row padding): nGPT's activations and weight (the backward products' operands), FP32,
+# strided rows, and a width that leaves the last workgroups' column tiles partly past the tensor
+T_CASES = [("bf16", 8192, 4096, 0), ("bf16", 4096, 4096, 0), ("f32", 2048, 8192, 0), ("bf16", 4096, 2560, 64),
+           ("bf16", 6144, 2000, 0)]
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("dtype,rows,cols,ld_pad", T_CASES)
+@pytest.mark.parametrize("both", [False, True])
+def test_one_pass_transposed_every_byte(dtype, rows, cols, ld_pad, both):
+    """x^T's encoding (and with both=True x's too, from the same registers) against the oracle, every byte."""
+    if both and cols % 16:
+        pytest.skip("the encoding both ways needs whole 16-column blocks")
+    say(f"one-pass transposed encoder: {dtype} {rows}x{cols} ld pad {ld_pad} both={both}")
+    x = _as_dtype(_tensor(rows + 3 * cols, rows, cols, "last"), dtype)
+    rowq, (ct, st), g = _quantize_t(x, dtype, ld_pad, both)
+    assert_every_byte(ct, st, g, np.ascontiguousarray(x.T), f"x^T {dtype} {rows}x{cols}")
+    if both:
+        assert_every_byte(rowq[0], rowq[1], g, x, f"x {dtype} {rows}x{cols}")
+
+
+@pytest.mark.timeout(300)
+def test_one_pass_transposed_local_path(monkeypatch):
+    monkeypatch.setenv("NVFP4_AMAX_POLLS", "0")
+    say("one-pass transposed encoder, local path: bf16 4096x4096 both ways")
+    x = _as_dtype(_tensor(77, 4096, 4096, "first"), "bf16")
+    rowq, (ct, st), g = _quantize_t(x, "bf16", both=True)
+    assert_every_byte(ct, st, g, np.ascontiguousarray(x.T), "x^T local path")
+    assert_every_byte(rowq[0], rowq[1], g, x, "x local path")
