@@ -670,10 +670,12 @@ __global__ __launch_bounds__(kResThreads) void quantize_resident_kernel(const T*
 // each of the first nq (1, 2 or 4) 256-thread quarters of a workgroup holds one
 // tile of the transposed encoder (512 rows x 8 lanes' columns, one 16-row patch
 // per lane) in registers, quarters stacked along the rows and workgroups
-// numbered column-major as there (the host takes the largest nq that leaves no
-// compute unit idle, so the encoding after the exchange is spread over all of
-// them); the workgroups exchange their maxima as in quantize_resident_kernel,
-// then every lane encodes its patch from registers.
+// numbered column-major as there (the host takes the smallest nq whose grid
+// fits one workgroup per compute unit, so the encoding after the exchange is
+// spread over as many units as it can be); the workgroups exchange their maxima
+// as in quantize_resident_kernel, then every lane encodes its patch from
+// registers. Quarters past nq, and lanes whose 16 rows or kVec columns lie past
+// the tensor, load nothing, publish 0 and encode nothing.
 template <typename T, int MODE>
 __global__ __launch_bounds__(kResThreads) void quantize_t_resident_kernel(
     const T* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, uint8_t* __restrict__ codes,

@@ -119,9 +119,11 @@ def _quantize_t(x, dtype, ld_pad=0, both=False):
 
 
 # (dtype, rows, cols, row padding): nGPT's activations and weight (the backward products' operands), FP32,
-# strided rows, and a width that leaves the last workgroups' column tiles partly past the tensor
+# strided rows, a width that leaves the last workgroups' column tiles partly past the tensor, and heights
+# that leave the last row tile (four quarters of 512 rows) with one live 16-row patch per column lane
+# (4112 rows) or with quarters 2 and 3 almost or wholly past the tensor (FP32, 1040 rows)
 T_CASES = [("bf16", 8192, 4096, 0), ("bf16", 4096, 4096, 0), ("f32", 2048, 8192, 0), ("bf16", 4096, 2560, 64),
-           ("bf16", 6144, 2000, 0)]
+           ("bf16", 6144, 2000, 0), ("bf16", 4112, 4096, 0), ("f32", 1040, 8192, 0)]
 
 
 @pytest.mark.timeout(300)
