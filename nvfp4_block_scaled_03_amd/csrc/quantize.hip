@@ -552,9 +552,9 @@ constexpr int kResDefaultPolls = 1 << 15;
 // every workgroup), from the records of all the grid's workgroups, or, if they
 // do not all arrive within `polls`, from the whole tensor x [rows][K] (row
 // stride ld) read by this workgroup.  *s_fail: a shared word, 0 on entry.
-template <typename T>
+template <typename T, bool RHT = false>
 __device__ float exchange_amax(float m, AmaxRecord* rec, int polls, const T* __restrict__ x, int64_t rows, int64_t K,
-                               int64_t ld, int* s_fail) {
+                               int64_t ld, int* s_fail, uint32_t signs = 0) {
     const int G = (int)gridDim.x;
     const uint64_t tag = launch_tag();
     if (threadIdx.x == 0) {
@@ -581,21 +581,34 @@ __device__ float exchange_amax(float m, AmaxRecord* rec, int polls, const T* __r
     float amax = block_max<kResThreads>(mt);
     if (*s_fail) {   // (uniform: written before the barriers of block_max)
         float w = 0.0f;
-        for (int64_t r = threadIdx.x / (kResThreads / 64); r < rows; r += 64)   // 64 rows at a time,
-            for (int64_t c = threadIdx.x % (kResThreads / 64); c < K; c += kResThreads / 64)   // 16 lanes a row
-                w = fmaxf(w, __builtin_fabsf(elem_f32(x[r * ld + c])));
+        if constexpr (RHT) {   // max |v| over the transformed blocks, one block per thread at a time
+            const int64_t bpr = K / 16, nblk = rows * bpr;
+            for (int64_t b = threadIdx.x; b < nblk; b += kResThreads) {
+                const int64_t r = b / bpr;
+                const T* src = x + r * ld + (b - r * bpr) * 16;
+                float v[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) v[i] = elem_f32(src[i]);
+                rht16(v, signs);
+                w = fmaxf(w, block_amax(v));
+            }
+        } else {
+            for (int64_t r = threadIdx.x / (kResThreads / 64); r < rows; r += 64)   // 64 rows at a time,
+                for (int64_t c = threadIdx.x % (kResThreads / 64); c < K; c += kResThreads / 64)   // 16 lanes a row
+                    w = fmaxf(w, __builtin_fabsf(elem_f32(x[r * ld + c])));
+        }
         amax = block_max<kResThreads>(w);
     }
     return amax;
 }
 
-template <typename T>
+template <typename T, bool RHT>
 __global__ __launch_bounds__(kResThreads) void quantize_resident_kernel(const T* __restrict__ x, int64_t rows,
                                                                         int64_t K, int64_t ld,
                                                                         uint8_t* __restrict__ codes,
                                                                         uint8_t* __restrict__ scales,
                                                                         float* __restrict__ g_out, AmaxRecord* rec,
-                                                                        int polls) {
+                                                                        int polls, uint32_t signs) {
     constexpr int R = ResBlocks<T>::value;
     __shared__ int s_fail;
     __shared__ float rtab[128];
@@ -619,10 +632,20 @@ __global__ __launch_bounds__(kResThreads) void quantize_resident_kernel(const T*
         for (int q = 0; q < (int)(sizeof(RawBlock<T>) / 16); ++q)
             raw[i].v[q] = bload16(rx, off, (uint32_t)q * 16);
     }
-    // block maxima from the raw bits (finite magnitudes order like their bit patterns), without widening
+    // block maxima from the raw bits (finite magnitudes order like their bit patterns), without widening;
+    // with the transform, of each block widened and transformed (the packed block stays, and is
+    // transformed again for the encoding)
     float bm[R], m = 0.0f;
 #pragma unroll
     for (int i = 0; i < R; ++i) {
+        if constexpr (RHT) {
+            float v[16];
+            widen(raw[i], v);
+            rht16(v, signs);
+            bm[i] = block_amax(v);
+            m = fmaxf(m, bm[i]);
+            continue;
+        }
         uint32_t mb = 0;
 #pragma unroll
         for (int q = 0; q < (int)(sizeof(RawBlock<T>) / 16); ++q) {
@@ -641,7 +664,7 @@ __global__ __launch_bounds__(kResThreads) void quantize_resident_kernel(const T*
         m = fmaxf(m, bm[i]);
     }
     m = block_max<kResThreads>(m);
-    const float amax = exchange_amax<T>(m, rec, polls, x, rows, K, ld, &s_fail);
+    const float amax = exchange_amax<T, RHT>(m, rec, polls, x, rows, K, ld, &s_fail, signs);
     const float g = global_scale_from_amax(amax);
     if (blockIdx.x == 0 && threadIdx.x == 0) g_out[0] = g;
     const float s_enc = 1.0f / g;
@@ -659,6 +682,7 @@ __global__ __launch_bounds__(kResThreads) void quantize_resident_kernel(const T*
         if (b < b1) {
             float v[16];
             widen(raw[i], v);
+            if constexpr (RHT) rht16(v, signs);
             uint32_t lo, hi, S;
             encode_block(v, bm[i], s_enc, rtab, lo, hi, S);
             store_code_block(codes, scales, (int64_t)b, lo, hi, S);
@@ -1165,16 +1189,31 @@ hipError_t launch_quantize(const void* x, int in_dtype, int64_t rows, int64_t K,
             return launch_small<float>(p, static_cast<const float*>(x), rows, K, ld_x, codes, scales, g, given,
                                        stream);
     }
-    const int rg = (given || rht) ? 0 : resident_grid(rows, K, ld_x, in_dtype, x, partials, n_partials);
+    int rg = given ? 0 : resident_grid(rows, K, ld_x, in_dtype, x, partials, n_partials);
+    // With the transform, each block is transformed twice in one pass (for its max, then for its encoding),
+    // which pays only with several blocks per thread: measured, 2 per thread (2048 x 4112 bf16) 13.2 us
+    // against 12.5 us in two passes, 5 per thread (4096 x 5120) 19.0 against 22.1 us.
+    if (rht && rg > 0 && rows * (K / 16) < 4 * (int64_t)rg * kResThreads) rg = 0;
     if (rg > 0) {
         const int polls = resident_polls();
         AmaxRecord* rec = reinterpret_cast<AmaxRecord*>(partials);
-        if (in_dtype == NVFP4_IN_BF16)
-            hipLaunchKernelGGL(quantize_resident_kernel<uint16_t>, dim3(rg), dim3(kResThreads), 0, stream,
-                               static_cast<const uint16_t*>(x), rows, K, ld_x, codes, scales, g, rec, polls);
-        else
-            hipLaunchKernelGGL(quantize_resident_kernel<float>, dim3(rg), dim3(kResThreads), 0, stream,
-                               static_cast<const float*>(x), rows, K, ld_x, codes, scales, g, rec, polls);
+        if (in_dtype == NVFP4_IN_BF16) {
+            const uint16_t* xb = static_cast<const uint16_t*>(x);
+            if (rht)
+                hipLaunchKernelGGL((quantize_resident_kernel<uint16_t, true>), dim3(rg), dim3(kResThreads), 0, stream,
+                                   xb, rows, K, ld_x, codes, scales, g, rec, polls, signs);
+            else
+                hipLaunchKernelGGL((quantize_resident_kernel<uint16_t, false>), dim3(rg), dim3(kResThreads), 0,
+                                   stream, xb, rows, K, ld_x, codes, scales, g, rec, polls, 0u);
+        } else {
+            const float* xf = static_cast<const float*>(x);
+            if (rht)
+                hipLaunchKernelGGL((quantize_resident_kernel<float, true>), dim3(rg), dim3(kResThreads), 0, stream,
+                                   xf, rows, K, ld_x, codes, scales, g, rec, polls, signs);
+            else
+                hipLaunchKernelGGL((quantize_resident_kernel<float, false>), dim3(rg), dim3(kResThreads), 0, stream,
+                                   xf, rows, K, ld_x, codes, scales, g, rec, polls, 0u);
+        }
         return hipGetLastError();
     }
     const int grid = encode_grid(rows, K);

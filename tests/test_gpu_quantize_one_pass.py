@@ -4,7 +4,8 @@ workgroups exchange their maxima, so x is read once.  Codes, scales and g must e
 bit for bit, every byte: bf16 and FP32, dense and strided rows, the tensor maximum in the first or
 the last workgroup's share, sizes at both ends of the range, and the local path a workgroup takes
 when the exchange does not complete (forced with a poll bound of zero: every workgroup then reduces
-max|x| over the whole tensor itself).
+max|x| over the whole tensor itself); the same for the transposed encoder (and the encoding both
+ways) and for the encoding behind the randomized Hadamard transform.
 
 Pages: "Why Gated DeltaNet Survives 4-Bit Quantization", section "Why the 'Fragile' Recurrence is
 Actually Robust" (16-element blocks with E4M3 scales and one FP32 tensor scale)."""
@@ -14,6 +15,7 @@ import torch
 
 import nvfp4_block_scaled_03_amd as nv
 from gpu_util import assert_every_byte, say, to_dev
+from oracle import rht
 
 pytestmark = pytest.mark.gpu
 F32 = np.float32
@@ -30,15 +32,16 @@ def _tensor(seed, rows, K, where):
     return x
 
 
+def _dev(x, dtype, ld_pad=0):
+    if not ld_pad:
+        return to_dev(x, dtype)
+    big = np.zeros((x.shape[0], x.shape[1] + ld_pad), F32)
+    big[:, :x.shape[1]] = x
+    return to_dev(big, dtype)[:, :x.shape[1]]
+
+
 def _quantize(x, dtype, ld_pad=0):
-    rows, K = x.shape
-    if ld_pad:
-        big = np.zeros((rows, K + ld_pad), F32)
-        big[:, :K] = x
-        xd = to_dev(big, dtype)[:, :K]
-    else:
-        xd = to_dev(x, dtype)
-    out = nv.quantize(xd)
+    out = nv.quantize(_dev(x, dtype, ld_pad))
     torch.cuda.synchronize()
     return out
 
@@ -100,12 +103,7 @@ def test_one_pass_zero_tensor():
 
 def _quantize_t(x, dtype, ld_pad=0, both=False):
     rows, cols = x.shape
-    if ld_pad:
-        big = np.zeros((rows, cols + ld_pad), F32)
-        big[:, :cols] = x
-        xd = to_dev(big, dtype)[:, :cols]
-    else:
-        xd = to_dev(x, dtype)
+    xd = _dev(x, dtype, ld_pad)
     ws = torch.empty(nv.nvfp4_quantize_workspace_bytes(rows, cols), dtype=torch.uint8, device="cuda")
     ct, st, g = nv.empty_quantized(cols, rows)
     if both:
@@ -149,3 +147,35 @@ def test_one_pass_transposed_local_path(monkeypatch):
     rowq, (ct, st), g = _quantize_t(x, "bf16", both=True)
     assert_every_byte(ct, st, g, np.ascontiguousarray(x.T), "x^T local path")
     assert_every_byte(rowq[0], rowq[1], g, x, "x local path")
+
+
+SIGNS = 0xB5C3
+# (dtype, rows, K, row padding, where the maximum is): the transform's one-pass form (taken from 4 blocks
+# per thread, 16.8M elements, up to the capacity) on nGPT's and GDN's activations, the FP32 capacity, strided
+# bf16 and FP32 rows; and a tensor below that size (two passes)
+RHT_CASES = [("bf16", 8192, 4096, 0, "last"), ("bf16", 4096, 5120, 0, "first"), ("f32", 2048, 8192, 0, "first"),
+             ("bf16", 4200, 4096, 64, "first"), ("f32", 2048, 8192, 4, "last"), ("bf16", 2048, 4112, 0, "last")]
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("dtype,rows,K,ld_pad,where", RHT_CASES)
+def test_one_pass_rht_every_byte(dtype, rows, K, ld_pad, where):
+    """The randomized Hadamard transform before the encoding: g from the maximum of the transformed tensor,
+    every code and scale byte against the oracle's encoding of its transformed blocks."""
+    say(f"one-pass quantizer with RHT: {dtype} {rows}x{K} ld pad {ld_pad}, maximum in the {where} share")
+    x = _as_dtype(_tensor(rows * 5 + K, rows, K, where), dtype)
+    c, s, g = nv.quantize_rht(_dev(x, dtype, ld_pad), SIGNS)
+    torch.cuda.synchronize()
+    assert_every_byte(c, s, g, rht.rht_blocks(x, SIGNS), f"rht {dtype} {rows}x{K}")
+
+
+@pytest.mark.timeout(300)
+def test_one_pass_rht_local_path(monkeypatch):
+    """A poll bound of zero with the transform: each workgroup reduces the transformed blocks of the whole
+    tensor itself."""
+    monkeypatch.setenv("NVFP4_AMAX_POLLS", "0")
+    say("one-pass quantizer with RHT, local path: bf16 4096x4112")
+    x = _as_dtype(_tensor(13, 4096, 4112, "first"), "bf16")
+    c, s, g = nv.quantize_rht(to_dev(x, "bf16"), SIGNS)
+    torch.cuda.synchronize()
+    assert_every_byte(c, s, g, rht.rht_blocks(x, SIGNS), "rht local path")
