@@ -800,6 +800,25 @@ static int resident_t_grid(int64_t rows, int64_t cols, int64_t ld, int in_dtype,
     return 0;
 }
 
+// Workgroups of the one-pass training-weight packer over the padded sizes
+// n_pad x k_pad, or 0 when it does not apply (x aligned for 16-byte loads).
+static int resident_pack_grid(int64_t n_pad, int64_t k_pad, int64_t rows, int64_t ld, int esize, int vec,
+                              const float* partials, int n_partials, int* nq) {
+    if (!vec || n_partials < kMaxAmaxPartials || reinterpret_cast<uintptr_t>(partials) % 16 != 0) return 0;
+    if (rows * ld * esize > INT32_MAX) return 0;
+    const int cus = cu_count();
+    const int64_t cap = cus < kResMaxGrid ? cus : kResMaxGrid;
+    const int64_t tcols = kTLanesC * (16 / esize), tiles_c = (k_pad + tcols - 1) / tcols;
+    for (int q = 1; q <= kResThreads / kQThreads; q *= 2) {   // the fewest quarters whose grid fits
+        const int64_t tiles = (n_pad + (int64_t)q * kTRows - 1) / ((int64_t)q * kTRows) * tiles_c;
+        if (tiles <= cap) {
+            *nq = q;
+            return (int)tiles;
+        }
+    }
+    return 0;
+}
+
 // Workgroups of the one-pass path for this tensor, or 0 when it does not apply.
 static int resident_grid(int64_t rows, int64_t K, int64_t ld, int in_dtype, const void* x, const float* partials,
                          int n_partials) {
@@ -930,6 +949,83 @@ __device__ __forceinline__ size_t scale_unit(int64_t row, int64_t kb, int64_t ks
     return (size_t)((row >> 4) * ks_per_row + (kb >> 3)) * 16 + (size_t)(row & 15);
 }
 
+// One lane's 16-row x kVec-column patch e (rows r0.., columns c0..; zero past
+// x, up to the padded sizes) into both packed blobs: its row-block parts (the
+// 16/kVec neighbouring lanes of a block combine their maxima) and its kVec
+// column blocks.
+template <typename T, int kVec>
+__device__ __forceinline__ void pack_train_patch(const T (&e)[16][kVec], int64_t r0, int64_t c0, int64_t rows,
+                                                 int64_t cols, float s_enc, const float* rtab, const PackedOut& o) {
+    uint8_t* const fc = o.fwd + o.f_codes;
+    uint8_t* const fs = o.fwd + o.f_scales;
+    uint8_t* const bc = o.bwd + o.b_codes;
+    uint8_t* const bs = o.bwd + o.b_scales;
+    // row blocks (the forward operand, k = cols columns; its padding rows up to n_pad are written too):
+    // 16/kVec neighbouring lanes share a block
+    const int64_t kb = c0 >> 4;
+    const int part = (int)((c0 >> (kVec == 8 ? 3 : 2)) & (16 / kVec - 1));   // which kVec-slice of the block
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        if (c0 >= cols) break;                  // (the lanes of a block agree: cols % 16 == 0)
+        float v[kVec];
+        float pm = 0.0f;
+#pragma unroll
+        for (int k = 0; k < kVec; ++k) {
+            v[k] = elem_f32(e[i][k]);
+            pm = fmaxf(pm, __builtin_fabsf(v[k]));
+        }
+        pm = fmaxf(pm, __shfl_xor(pm, 1, 64));
+        if constexpr (kVec == 4) pm = fmaxf(pm, __shfl_xor(pm, 2, 64));
+        uint32_t sc;
+        const uint32_t wd = encode_part<kVec>(v, pm, s_enc, rtab, sc);
+        const int64_t row = r0 + i;
+        uint8_t* dst = fc + code_unit(row, kb, o.ksf) * 16 + (kb & 1) * 8 + part * (kVec / 2);
+        if constexpr (kVec == 8)
+            *reinterpret_cast<uint32_t*>(dst) = wd;
+        else
+            *reinterpret_cast<uint16_t*>(dst) = (uint16_t)wd;
+        if (part == 0) fs[scale_unit(row, kb, o.ksf) * 8 + (kb & 7)] = (uint8_t)sc;
+    }
+    // column blocks (the backward operand, k = rows; its padding rows up to k_pad are written too):
+    // output row c0 + k, block r0 / 16 along n
+    const int64_t kbt = r0 >> 4;
+#pragma unroll
+    for (int k = 0; k < kVec; ++k) {
+        if (r0 >= rows) break;
+        float v[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = elem_f32(e[i][k]);
+        uint32_t lo, hi, sc;
+        encode_block(v, block_amax(v), s_enc, rtab, lo, hi, sc);
+        const int64_t c = c0 + k;
+        *reinterpret_cast<uint2*>(bc + code_unit(c, kbt, o.ksb) * 16 + (kbt & 1) * 8) = make_uint2(lo, hi);
+        bs[scale_unit(c, kbt, o.ksb) * 8 + (kbt & 7)] = (uint8_t)sc;
+    }
+}
+
+// Both blobs' column scales (g for real rows, 0 for padding) and headers, by
+// thread `tid` of `nthreads`.
+__device__ __forceinline__ void pack_train_headers(const PackedOut& o, int64_t rows, int64_t cols, float g,
+                                                   int64_t tid, int64_t nthreads) {
+    for (int64_t i = tid; i < o.n_pad + o.k_pad; i += nthreads) {
+        if (i < o.n_pad)
+            reinterpret_cast<float*>(o.fwd + o.f_cs)[i] = i < rows ? g : 0.0f;
+        else
+            reinterpret_cast<float*>(o.bwd + o.b_cs)[i - o.n_pad] = i - o.n_pad < cols ? g : 0.0f;
+    }
+    if (tid < 2) {
+        uint8_t* blob = tid == 0 ? o.fwd : o.bwd;
+        uint32_t* h32 = reinterpret_cast<uint32_t*>(blob);
+        int64_t* h64 = reinterpret_cast<int64_t*>(blob + 8);
+        h32[0] = NVFP4_WEIGHT_MAGIC;
+        h32[1] = NVFP4_WEIGHT_VERSION;
+        h64[0] = tid == 0 ? rows : cols;
+        h64[1] = tid == 0 ? cols : rows;
+        h64[2] = tid == 0 ? o.n_pad : o.k_pad;
+        h64[3] = 1;
+    }
+}
+
 template <typename T>
 __global__ __launch_bounds__(kQThreads) void pack_train_kernel(const T* __restrict__ x, int64_t rows, int64_t cols,
                                                                int64_t ld, float* __restrict__ g_io, int g_given,
@@ -958,25 +1054,7 @@ __global__ __launch_bounds__(kQThreads) void pack_train_kernel(const T* __restri
     fill_recip_table(rtab, s_enc, threadIdx.x, kQThreads);
     __syncthreads();
 
-    // column scales (g for real rows, 0 for padding) and the two headers
-    for (int64_t i = (int64_t)blockIdx.x * kQThreads + threadIdx.x; i < o.n_pad + o.k_pad;
-         i += (int64_t)gridDim.x * kQThreads) {
-        if (i < o.n_pad)
-            reinterpret_cast<float*>(o.fwd + o.f_cs)[i] = i < rows ? g : 0.0f;
-        else
-            reinterpret_cast<float*>(o.bwd + o.b_cs)[i - o.n_pad] = i - o.n_pad < cols ? g : 0.0f;
-    }
-    if (blockIdx.x == 0 && threadIdx.x < 2) {
-        uint8_t* blob = threadIdx.x == 0 ? o.fwd : o.bwd;
-        uint32_t* h32 = reinterpret_cast<uint32_t*>(blob);
-        int64_t* h64 = reinterpret_cast<int64_t*>(blob + 8);
-        h32[0] = NVFP4_WEIGHT_MAGIC;
-        h32[1] = NVFP4_WEIGHT_VERSION;
-        h64[0] = threadIdx.x == 0 ? rows : cols;
-        h64[1] = threadIdx.x == 0 ? cols : rows;
-        h64[2] = threadIdx.x == 0 ? o.n_pad : o.k_pad;
-        h64[3] = 1;
-    }
+    pack_train_headers(o, rows, cols, g, (int64_t)blockIdx.x * kQThreads + threadIdx.x, (int64_t)gridDim.x * kQThreads);
 
     constexpr int kVec = 16 / (int)sizeof(T);
     constexpr int kRG = 64 / kTLanesC;
@@ -984,10 +1062,6 @@ __global__ __launch_bounds__(kQThreads) void pack_train_kernel(const T* __restri
     const int64_t tiles_r = (o.n_pad + kTRows - 1) / kTRows, tiles_c = (o.k_pad + kTCols - 1) / kTCols;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int cl = lane % kTLanesC, rg = lane / kTLanesC;
-    uint8_t* const fc = o.fwd + o.f_codes;
-    uint8_t* const fs = o.fwd + o.f_scales;
-    uint8_t* const bc = o.bwd + o.b_codes;
-    uint8_t* const bs = o.bwd + o.b_scales;
     for (int64_t tile_id = blockIdx.x; tile_id < tiles_r * tiles_c; tile_id += gridDim.x) {
         const int64_t tr = tile_id % tiles_r, tc = tile_id / tiles_r;
         const int64_t r0 = tr * kTRows + (w * kRG + rg) * 16;
@@ -1005,48 +1079,70 @@ __global__ __launch_bounds__(kQThreads) void pack_train_kernel(const T* __restri
                 for (int k = 0; k < kVec; ++k)
                     e[i][k] = (r0 + i < rows && c0 + k < cols) ? src[i * ld + k] : T(0);
         }
-        // row blocks (the forward operand, k = cols columns; its padding rows up to n_pad are written too):
-        // 16/kVec neighbouring lanes share a block
-        const int64_t kb = c0 >> 4;
-        const int part = (int)((c0 >> (kVec == 8 ? 3 : 2)) & (16 / kVec - 1));   // which kVec-slice of the block
+        pack_train_patch<T, kVec>(e, r0, c0, rows, cols, s_enc, rtab, o);
+    }
+}
+
+// The one-pass form of the training-weight packer (g computed): each of the
+// first nq quarters of a 1024-thread workgroup holds one tile of patches of
+// pack_train_kernel in registers (quarters stacked along the rows, workgroups
+// numbered column-major, over the padded sizes), the workgroups exchange their
+// maxima as in quantize_resident_kernel, then every lane writes its patch into
+// both blobs from registers.  Patches lie wholly inside W or wholly in the
+// padding (n and k are multiples of 128); padding patches load zeros.
+template <typename T>
+__global__ __launch_bounds__(kResThreads) void pack_train_resident_kernel(const T* __restrict__ x, int64_t rows,
+                                                                          int64_t cols, int64_t ld,
+                                                                          float* __restrict__ g_out, AmaxRecord* rec,
+                                                                          int polls, PackedOut o, int nq) {
+    constexpr int kVec = 16 / (int)sizeof(T);
+    constexpr int kRG = 64 / kTLanesC;
+    constexpr int kTCols = kTLanesC * kVec;
+    __shared__ int s_fail;
+    __shared__ float rtab[128];
+    if (threadIdx.x == 0) s_fail = 0;   // (ordered before its uses by the barriers in block_max)
+    const int64_t tiles_r = (o.n_pad + (int64_t)nq * kTRows - 1) / ((int64_t)nq * kTRows);
+    const int64_t tr = blockIdx.x % tiles_r, tc = blockIdx.x / tiles_r;
+    const int q = threadIdx.x / kQThreads, t = threadIdx.x % kQThreads;
+    const int lane = t & 63, w = t >> 6;
+    const int cl = lane % kTLanesC, rg = lane / kTLanesC;
+    const int64_t r0 = (tr * nq + q) * kTRows + (w * kRG + rg) * 16;
+    const int64_t c0 = tc * kTCols + (int64_t)kVec * cl;
+    const bool live = q < nq && r0 < o.n_pad && c0 < o.k_pad;
+    const bool in_x = live && r0 < rows && c0 < cols;
+    const rsrc_t rx = make_rsrc(x, (uint64_t)rows * ld * sizeof(T));
+    const uint32_t off = in_x ? (uint32_t)((r0 * ld + c0) * (int64_t)sizeof(T)) : kOutOfBounds;
+    uint4 pu[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            if (c0 >= cols) break;                  // (the lanes of a block agree: cols % 16 == 0)
-            float v[kVec];
-            float pm = 0.0f;
+    for (int i = 0; i < 16; ++i) pu[i] = bload16(rx, in_x ? off + (uint32_t)(i * ld * (int64_t)sizeof(T)) : kOutOfBounds, 0);
+    uint32_t mb = 0;
 #pragma unroll
-            for (int k = 0; k < kVec; ++k) {
-                v[k] = elem_f32(e[i][k]);
-                pm = fmaxf(pm, __builtin_fabsf(v[k]));
+    for (int i = 0; i < 16; ++i) {
+        const uint32_t wd[4] = {pu[i].x, pu[i].y, pu[i].z, pu[i].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if constexpr (sizeof(T) == 2) {
+                mb = max(mb, (wd[j] & 0x7FFFu) << 16);
+                mb = max(mb, wd[j] & 0x7FFF0000u);
+            } else {
+                mb = max(mb, wd[j] & 0x7FFFFFFFu);
             }
-            pm = fmaxf(pm, __shfl_xor(pm, 1, 64));
-            if constexpr (kVec == 4) pm = fmaxf(pm, __shfl_xor(pm, 2, 64));
-            uint32_t sc;
-            const uint32_t wd = encode_part<kVec>(v, pm, s_enc, rtab, sc);
-            const int64_t row = r0 + i;
-            uint8_t* dst = fc + code_unit(row, kb, o.ksf) * 16 + (kb & 1) * 8 + part * (kVec / 2);
-            if constexpr (kVec == 8)
-                *reinterpret_cast<uint32_t*>(dst) = wd;
-            else
-                *reinterpret_cast<uint16_t*>(dst) = (uint16_t)wd;
-            if (part == 0) fs[scale_unit(row, kb, o.ksf) * 8 + (kb & 7)] = (uint8_t)sc;
-        }
-        // column blocks (the backward operand, k = rows; its padding rows up to k_pad are written too):
-        // output row c0 + k, block r0 / 16 along n
-        const int64_t kbt = r0 >> 4;
-#pragma unroll
-        for (int k = 0; k < kVec; ++k) {
-            if (r0 >= rows) break;
-            float v[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) v[i] = elem_f32(e[i][k]);
-            uint32_t lo, hi, sc;
-            encode_block(v, block_amax(v), s_enc, rtab, lo, hi, sc);
-            const int64_t c = c0 + k;
-            *reinterpret_cast<uint2*>(bc + code_unit(c, kbt, o.ksb) * 16 + (kbt & 1) * 8) = make_uint2(lo, hi);
-            bs[scale_unit(c, kbt, o.ksb) * 8 + (kbt & 7)] = (uint8_t)sc;
         }
     }
+    const float m = block_max<kResThreads>(__uint_as_float(mb));
+    const float amax = exchange_amax<T>(m, rec, polls, x, rows, cols, ld, &s_fail);
+    const float g = global_scale_from_amax(amax);
+    if (blockIdx.x == 0 && threadIdx.x == 0) g_out[0] = g;
+    const float s_enc = 1.0f / g;
+    fill_recip_table(rtab, s_enc, threadIdx.x, kResThreads);
+    pack_train_headers(o, rows, cols, g, (int64_t)blockIdx.x * kResThreads + threadIdx.x,
+                       (int64_t)gridDim.x * kResThreads);
+    __syncthreads();
+    // (the patch stays packed until here)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(pu[i].x), "+v"(pu[i].y), "+v"(pu[i].z), "+v"(pu[i].w));
+    if (live)
+        pack_train_patch<T, kVec>(*reinterpret_cast<const T(*)[16][kVec]>(pu), r0, c0, rows, cols, s_enc, rtab, o);
 }
 
 hipError_t launch_pack_train(const void* x, int in_dtype, int64_t rows, int64_t cols, int64_t ld_x, float* g,
@@ -1068,6 +1164,18 @@ hipError_t launch_pack_train(const void* x, int in_dtype, int64_t rows, int64_t 
     const int64_t tcols = kTLanesC * (16 / esize);
     const int64_t tiles = ((o.n_pad + kTRows - 1) / kTRows) * ((o.k_pad + tcols - 1) / tcols);
     const int grid = (int)(tiles < (1 << 24) ? tiles : (1 << 24));
+    int nq = 0;
+    const int rg = given ? 0 : resident_pack_grid(o.n_pad, o.k_pad, rows, ld_x, esize, vec, partials, n_partials, &nq);
+    if (rg > 0) {
+        AmaxRecord* rec = reinterpret_cast<AmaxRecord*>(partials);
+        if (in_dtype == NVFP4_IN_BF16)
+            hipLaunchKernelGGL(pack_train_resident_kernel<uint16_t>, dim3(rg), dim3(kResThreads), 0, stream,
+                               static_cast<const uint16_t*>(x), rows, cols, ld_x, g, rec, resident_polls(), o, nq);
+        else
+            hipLaunchKernelGGL(pack_train_resident_kernel<float>, dim3(rg), dim3(kResThreads), 0, stream,
+                               static_cast<const float*>(x), rows, cols, ld_x, g, rec, resident_polls(), o, nq);
+        return hipGetLastError();
+    }
     if (in_dtype == NVFP4_IN_BF16) {
         const uint16_t* xp = static_cast<const uint16_t*>(x);
         if (!given)

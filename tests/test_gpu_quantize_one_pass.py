@@ -5,7 +5,8 @@ bit for bit, every byte: bf16 and FP32, dense and strided rows, the tensor maxim
 the last workgroup's share, sizes at both ends of the range, and the local path a workgroup takes
 when the exchange does not complete (forced with a poll bound of zero: every workgroup then reduces
 max|x| over the whole tensor itself); the same for the transposed encoder (and the encoding both
-ways) and for the encoding behind the randomized Hadamard transform.
+ways), for the encoding behind the randomized Hadamard transform and for the training-weight packer
+(both packed operands of a weight).
 
 Pages: "Why Gated DeltaNet Survives 4-Bit Quantization", section "Why the 'Fragile' Recurrence is
 Actually Robust" (16-element blocks with E4M3 scales and one FP32 tensor scale)."""
@@ -179,3 +180,49 @@ def test_one_pass_rht_local_path(monkeypatch):
     c, s, g = nv.quantize_rht(to_dev(x, "bf16"), SIGNS)
     torch.cuda.synchronize()
     assert_every_byte(c, s, g, rht.rht_blocks(x, SIGNS), "rht local path")
+
+
+# (dtype, n, k, row padding): nGPT's W [4096 x 4096] (two quarters per workgroup), the bf16 and FP32
+# capacities (four quarters), strided rows, and n = 1152 (padding rows up to 1280 in the forward blob)
+PACK_CASES = [("bf16", 4096, 4096, 0), ("bf16", 8192, 4096, 0), ("f32", 2048, 8192, 0), ("bf16", 4096, 2560, 64),
+              ("f32", 1152, 8192, 0)]
+
+
+def _check_packed(fwd, bwd, g, w, what):
+    """Both blobs unpacked against the oracle's encodings of w and w^T, every byte, and every real row's
+    column scale equal to g; the padding rows, column scales and headers against the separate calls."""
+    for pw, x, side in ((fwd, w, "forward"), (bwd, np.ascontiguousarray(w.T), "backward")):
+        c, s, cs = pw.unpack()
+        torch.cuda.synchronize()
+        assert_every_byte(c, s, g, x, f"{what} {side}")
+        assert torch.equal(cs, g.expand_as(cs)), f"{what} {side}: column scales differ from g"
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("dtype,n,k,ld_pad", PACK_CASES)
+def test_one_pass_pack_weights_train(dtype, n, k, ld_pad):
+    """A training weight's two packed operands from registers: every code and scale against the oracle,
+    every blob byte (padding included) against quantize + pack and quantize_t + pack."""
+    from test_gpu_quantize_t import _blob_regions
+    say(f"one-pass training-weight packer: {dtype} {n}x{k} ld pad {ld_pad}")
+    w = _as_dtype(_tensor(n + 11 * k, n, k, "last"), dtype)
+    wd = _dev(w, dtype, ld_pad)
+    fwd, bwd, g = nv.pack_weights_train(wd)
+    torch.cuda.synchronize()
+    _check_packed(fwd, bwd, g, w, f"{dtype} {n}x{k}")
+    ref_fwd = nv.PackedWeight([nv.quantize(wd)], k)
+    ref_bwd = nv.PackedWeight([nv.quantize_t(wd)], n)
+    torch.cuda.synchronize()
+    for got, want, side in ((fwd, ref_fwd, "forward"), (bwd, ref_bwd, "backward")):
+        for part, (a, b) in zip(["header", "codes", "scales", "colscale"], zip(_blob_regions(got), _blob_regions(want))):
+            assert np.array_equal(a, b), f"{side} {part} differs from the separate calls"
+
+
+@pytest.mark.timeout(300)
+def test_one_pass_pack_weights_train_local_path(monkeypatch):
+    monkeypatch.setenv("NVFP4_AMAX_POLLS", "0")
+    say("one-pass training-weight packer, local path: bf16 4096x4096")
+    w = _as_dtype(_tensor(91, 4096, 4096, "first"), "bf16")
+    fwd, bwd, g = nv.pack_weights_train(to_dev(w, "bf16"))
+    torch.cuda.synchronize()
+    _check_packed(fwd, bwd, g, w, "local path")
