@@ -190,3 +190,49 @@ def test_workspace_shared_across_token_counts():
         torch.cuda.synchronize()
         assert torch.equal(c, c2) and torch.equal(s, s2) and torch.equal(g, g2), f"call {i} M={M}"
         assert torch.equal(y, y2), f"call {i} M={M}"
+
+
+def test_graph_replays_with_changing_inputs():
+    """The one-launch decode layer captured in a HIP graph and replayed on activations of very different
+    magnitude copied into the captured input between replays: each replay equals the eager call on that
+    input (codes, scales, g and Y), so no replay reads records an earlier launch published."""
+    wl = workloads.make_decode()
+    pw = nv.PackedWeight([nv.quantize(to_dev(wl.w[0], "bf16"))], wl.K)
+    xs = [to_dev(workloads.random_matrix(2300 + i, wl.M, wl.K, sc, dtype="bf16"), "bf16")
+          for i, sc in enumerate((1.0, 1e-3, 40.0))]
+    wsp = nv.linear_workspace(wl.M, torch.bfloat16, pw)
+    xd = torch.empty_like(xs[0])
+
+    def outs():
+        return (*nv.empty_quantized(wl.M, wl.K), torch.empty((wl.M, wl.N), dtype=torch.float32, device=DEV))
+
+    def step(o, s=None):
+        nv.nvfp4_linear(xd, o[0], o[1], o[2], pw.desc, o[3], wsp, stream=s)
+
+    say("linear graph replays on changing inputs: eager outputs")
+    want = []
+    for x in xs:
+        xd.copy_(x)
+        o = outs()
+        step(o)
+        torch.cuda.synchronize()
+        want.append(o)
+    got = outs()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        step(got, s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        step(got, s)
+    for rep in range(6):
+        i = (rep * 2) % 3
+        xd.copy_(xs[i])
+        for t in got:
+            t.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b, what in zip(got, want[i], ("codes", "scales", "g", "y")):
+            assert torch.equal(a, b), f"replay {rep} (input {i}): {what} differs from the eager call"
+        step(outs())                        # an eager call between replays shares the workspace

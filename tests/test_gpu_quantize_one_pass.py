@@ -226,3 +226,68 @@ def test_one_pass_pack_weights_train_local_path(monkeypatch):
     fwd, bwd, g = nv.pack_weights_train(to_dev(w, "bf16"))
     torch.cuda.synchronize()
     _check_packed(fwd, bwd, g, w, "local path")
+
+
+def test_one_pass_graph_replays_with_changing_inputs():
+    """The one-pass kernels captured in one HIP graph (row, transposed, both ways, RHT, the training-weight
+    packer), replayed on three tensors of very different magnitude copied into the captured input between
+    replays: every replay equals the eager calls on that tensor, so no replay takes a maximum that an
+    earlier one published (the launch tags differ between replays)."""
+    rows, cols = 4096, 4096
+    xs = [_as_dtype((_tensor(300 + i, rows, cols, "first" if i % 2 else "last") * F32(sc)).astype(F32), "bf16")
+          for i, sc in enumerate((1.0, 1e-3, 50.0))]
+    xd = torch.empty((rows, cols), dtype=torch.bfloat16, device="cuda")
+    ws = [torch.empty(nv.nvfp4_quantize_workspace_bytes(rows, cols), dtype=torch.uint8, device="cuda")
+          for _ in range(5)]
+    blob_f = torch.zeros((nv.nvfp4_packed_weight_bytes([rows], cols),), dtype=torch.uint8, device="cuda")
+    blob_b = torch.zeros((nv.nvfp4_packed_weight_bytes([cols], rows),), dtype=torch.uint8, device="cuda")
+
+    def buffers():
+        return {"q": nv.empty_quantized(rows, cols), "t": nv.empty_quantized(cols, rows),
+                "b": nv.empty_quantized(rows, cols) + nv.empty_quantized(cols, rows)[:2],
+                "r": nv.empty_quantized(rows, cols),      # (blobs zeroed: the alignment gaps are never written)
+                "p": (torch.zeros_like(blob_f), torch.zeros_like(blob_b),
+                      torch.empty((1,), dtype=torch.float32, device="cuda"))}
+
+    def run(o, s=None):
+        nv.nvfp4_quantize(xd, *o["q"], nv.NVFP4_G_COMPUTE, ws[0], stream=s)
+        nv.nvfp4_quantize_t(xd, *o["t"], nv.NVFP4_G_COMPUTE, ws[1], stream=s)
+        c, sc, g, ct, st = o["b"]
+        nv.nvfp4_quantize_both(xd, c, sc, ct, st, g, nv.NVFP4_G_COMPUTE, ws[2], stream=s)
+        nv.nvfp4_quantize_rht(xd, SIGNS, *o["r"], nv.NVFP4_G_COMPUTE, ws[3], stream=s)
+        bf, bb, gp = o["p"]
+        nv.nvfp4_pack_weights_train(xd, gp, bf, bb, nv.NVFP4_G_COMPUTE, ws[4], stream=s)
+
+    def flat(o):
+        return [t for v in o.values() for t in v]
+
+    say("one-pass kernels: eager outputs of three tensors")
+    want = []
+    for x in xs:
+        xd.copy_(torch.from_numpy(x).to(torch.bfloat16))
+        o = buffers()
+        run(o)
+        torch.cuda.synchronize()
+        want.append(o)
+    assert len({float(o["q"][2].cpu()[0]) for o in want}) == 3      # three different g
+    got = buffers()
+    strm = torch.cuda.Stream()
+    with torch.cuda.stream(strm):
+        run(got, strm)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=strm):
+        run(got, strm)
+    for rep in range(6):
+        i = (rep * 2) % 3
+        say(f"one-pass kernels: replay {rep} on tensor {i}")
+        xd.copy_(torch.from_numpy(xs[i]).to(torch.bfloat16))
+        for t in flat(got):
+            t.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name in got:
+            for a, b in zip(got[name], want[i][name]):
+                assert torch.equal(a, b), f"replay {rep} (tensor {i}): {name} differs from the eager call"
+        run(buffers())                      # eager calls between replays share the workspaces
