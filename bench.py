@@ -85,15 +85,21 @@ def measured_traffic(workload):
 
 
 def copy_probe(mib):
-    """A copy of known size: the HBM byte counters of its kernel scale those of the product kernels."""
+    """A copy of known size: the HBM byte counters of its kernel scale those of the product kernels, and
+    its rate (reads plus writes) is the ceiling of a pass that reads and writes HBM, as the encoder does."""
     import torch
     n = mib << 20
     src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
     dst = torch.empty_like(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
     for _ in range(20):
         dst.copy_(src)
+    e1.record()
     torch.cuda.synchronize()
-    print(json.dumps({"copy_probe_bytes": n, "launches": 20}), flush=True)
+    t = e0.elapsed_time(e1) * 1e-3 / 20
+    print(json.dumps({"copy_probe_bytes": n, "launches": 20, "us_per_copy": t * 1e6,
+                      "read_plus_write_gbs": 2 * n / t / 1e9}), flush=True)
 
 
 def log(msg):
