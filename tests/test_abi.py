@@ -265,6 +265,19 @@ def test_gemm_validation():
     assert nv.lib.nvfp4_unpack_weights(None, FAKE, FAKE, FAKE, None) == nv.NVFP4_ERR_INVALID_ARG
 
 
+def test_operand_size_limit():
+    """The products address codes with 32-bit byte offsets: activation codes of exactly 2 GiB pass the
+    checks, one row more is refused before any launch; a weight whose padded codes pass 2 GiB has no
+    packed size."""
+    d = make_desc(K=640)                      # 320 code bytes per row
+    m_max = (1 << 31) // 320
+    assert g_(M=m_max + 1, d=d) == nv.NVFP4_ERR_UNSUPPORTED
+    if _no_gpu():
+        assert g_(M=m_max, d=d) == nv.NVFP4_ERR_NO_DEVICE
+    assert nv.nvfp4_packed_weight_bytes([1 << 18], 16384) > 0       # 262144 x 16384: exactly 2 GiB of codes
+    assert nv.nvfp4_packed_weight_bytes([(1 << 18) + 1], 16384) == 0
+
+
 def test_gemm_valid_stops_at_device_check_without_gpu():
     if not _no_gpu():
         pytest.skip("a GPU is visible; this host-only check would launch on fake pointers")
