@@ -135,3 +135,34 @@ def test_hardware_e2m1_whole_range():
         assert np.array_equal(nib, ref.e2m1_encode(q.reshape(x.shape))), f"{what}: codes differ from e2m1_encode"
         assert np.array_equal(host(c), want.codes), what
     assert exps >= set(range(-148, 129)), "q covers every FP32 binade"
+
+
+@pytest.mark.timeout(300)
+def test_largest_activation_operand():
+    """Activation codes of exactly 2 GiB, the most the products address with their 32-bit byte offsets
+    (262144 x 16384 bf16, 8 GiB), through the layer call. X is zero except its last 300 rows (two
+    256-row tiles, the last operand offsets within a few MB of 2^31), so the tensor's amax is theirs:
+    g, those rows' codes and scales and their output rows against the oracle; every other code, scale
+    and output exactly zero."""
+    K, N, tail = 16384, 256, 300
+    M = (1 << 31) // (K // 2)
+    rng = np.random.default_rng(1 << 31)
+    xt = torch.from_numpy(rng.standard_normal((tail, K)).astype(F32)).to(torch.bfloat16).float().numpy()
+    w = torch.from_numpy((0.01 * rng.standard_normal((N, K))).astype(F32)).to(torch.bfloat16).float().numpy()
+    say(f"largest activation operand: M={M} K={K} N={N}, X {M * K * 2 >> 30} GiB bf16, codes {M * K // 2 >> 30} GiB")
+    x = torch.zeros((M, K), dtype=torch.bfloat16, device=DEV)
+    x[M - tail:] = to_dev(xt, "bf16")
+    pw = nv.PackedWeight([nv.quantize(to_dev(w, "bf16"))], K)
+    y, xc, xs, gx = nv.linear(x, pw, nv.linear_workspace(M, x.dtype, pw))
+    torch.cuda.synchronize()
+    del x
+    g_x = ref.global_scale(F32(np.max(np.abs(xt))))
+    xq = ref.quantize(xt, "given", g_x)
+    assert F32(host(gx)[0]).tobytes() == F32(g_x).tobytes()
+    assert np.array_equal(host(xs[M - tail:]), xq.scales)
+    assert np.array_equal(host(xc[M - tail:]), xq.codes)
+    assert int(torch.count_nonzero(xc[:M - tail])) == 0 and int(torch.count_nonzero(xs[:M - tail])) == 0
+    assert int(torch.count_nonzero(y[:M - tail])) == 0
+    y_ref, a_ref = ref.gemm(xq, [ref.quantize(w)])
+    ok, worst = ref.gemm_within_tolerance(host(y[M - tail:]), y_ref, a_ref)
+    assert ok, f"largest activation operand: worst |dy|/sum|terms| = {worst:.3e}"
