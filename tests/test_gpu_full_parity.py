@@ -166,3 +166,27 @@ def test_largest_activation_operand():
     y_ref, a_ref = ref.gemm(xq, [ref.quantize(w)])
     ok, worst = ref.gemm_within_tolerance(host(y[M - tail:]), y_ref, a_ref)
     assert ok, f"largest activation operand: worst |dy|/sum|terms| = {worst:.3e}"
+
+
+@pytest.mark.timeout(300)
+def test_largest_weight_operand():
+    """A packed weight of exactly 2 GiB of codes (262144 x 16384 bf16, 8 GiB, its last column tiles'
+    byte offsets within a few MB of 2^31), zero but for its last 300 rows, against 300 activation rows
+    through the layer call: those 300 output columns against the oracle, every other column zero."""
+    K, tail, M = 16384, 300, 300
+    N = (1 << 31) // (K // 2)
+    rng = np.random.default_rng((1 << 31) + 1)
+    wt = torch.from_numpy((0.01 * rng.standard_normal((tail, K))).astype(F32)).to(torch.bfloat16).float().numpy()
+    x = torch.from_numpy(rng.standard_normal((M, K)).astype(F32)).to(torch.bfloat16).float().numpy()
+    say(f"largest weight operand: M={M} K={K} N={N}, W {N * K * 2 >> 30} GiB bf16, codes {N * K // 2 >> 30} GiB")
+    w = torch.zeros((N, K), dtype=torch.bfloat16, device=DEV)
+    w[N - tail:] = to_dev(wt, "bf16")
+    pw = nv.PackedWeight([nv.quantize(w)], K)
+    del w
+    y, _, _, _ = nv.linear(to_dev(x, "bf16"), pw, nv.linear_workspace(M, torch.bfloat16, pw))
+    torch.cuda.synchronize()
+    assert int(torch.count_nonzero(y[:, :N - tail])) == 0
+    wq = ref.quantize(wt, "given", ref.global_scale(F32(np.max(np.abs(wt)))))
+    y_ref, a_ref = ref.gemm(ref.quantize(x), [wq])
+    ok, worst = ref.gemm_within_tolerance(host(y[:, N - tail:]), y_ref, a_ref)
+    assert ok, f"largest weight operand: worst |dy|/sum|terms| = {worst:.3e}"
