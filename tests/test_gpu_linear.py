@@ -51,7 +51,11 @@ def test_decode_workload():
                                    # 8 x 3, 39 over 8 x 5; one wavefront per k-step below 8
                                    (5, 2944, 200), (16, 4992, 5120), (2, 384, 33),
                                    # K above the one-workgroup-per-row-block limit: quantize + tiled product
-                                   (9, 9216, 256)])
+                                   (9, 9216, 256),
+                                   # degenerate layers: one output column, one token, one k-step; past 16
+                                   # tokens the tiled product with a single (ragged) column tile
+                                   (1, 128, 1), (16, 128, 1), (1, 128, 17), (17, 128, 1), (300, 256, 1),
+                                   (33, 128, 5)])
 def test_shapes(M, K, N):
     x = workloads.random_matrix(700 + M, M, K, dtype="bf16")
     w = workloads.random_matrix(800 + M, N, K, 0.05, dtype="bf16")
