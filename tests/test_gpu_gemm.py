@@ -68,6 +68,18 @@ def test_tiled_ragged_fused(M):
     check_dense(x, "bf16", ws, "bf16", f"tiled fused M={M}")
 
 
+@pytest.mark.parametrize("M", [5, 40])
+def test_most_modules(M):
+    """The most sub-modules one packed weight holds (16), several of a single row, each with its own
+    global scale (weight scales spread over five decades), on the few-token and the tiled product:
+    every module boundary, including ones inside a 16-row block and inside a column tile."""
+    rows = [1, 2, 3, 1, 16, 17, 1, 5, 31, 33, 1, 64, 1, 7, 2, 1]
+    x = workloads.random_matrix(1600 + M, M, 512, dtype="bf16")
+    ws = [workloads.random_matrix(1700 + i, r, 512, 10.0 ** (-4 + (i % 5)), dtype="bf16")
+          for i, r in enumerate(rows)]
+    check_dense(x, "bf16", ws, "bf16", f"16 modules M={M}")
+
+
 @pytest.mark.parametrize("M,K", [(40, 128), (260, 128), (260, 256), (260, 384), (40, 896)])
 def test_tiled_short_and_odd_k(M, K):
     """k-step counts of 1, 2, 3 and 7: the tile kernels' load ring runs past the last k-step."""
